@@ -1,0 +1,165 @@
+/*
+ * ev.h — one-pass verification of a drafted token tree on AMD MI355X (gfx950).
+ *
+ * What the library computes (sources, all web pages on EAGLE speculative decoding):
+ *   [TR] "Tech Radar: SGLang EAGLE-2 speculative decoding" (learn.tanhdev.com),
+ *        sec. 2: sequence diagram (draft a tree of at most 64 nodes plus its mask, run
+ *        ONE target forward over the whole tree, keep the accepted branch's KV, drop the
+ *        rest) and the dynamic tree-attention mask equation M.
+ *   [EX] "EAGLE — Draft head attached to an internal layer, 3x speedup" (troisinh.com),
+ *        "Core idea" (verify all branches at once for the longest accepted prefix) and
+ *        "Why it works" (rejection sampling keeps the target's output distribution).
+ *   [SN] "EAGLE — guessing the next step in feature space" (estelledc.github.io),
+ *        case 1 (k accepted drafts advance k + 1 tokens) and case 3 (lossless argument).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is DEVICE memory owned by the caller unless marked (host).
+ *   - Calls enqueue work on `stream` and return without synchronising.  No call
+ *     allocates memory or keeps state between calls; workspace comes from the caller,
+ *     sized by the matching *_workspace() query.
+ *   - Argument errors visible on the host (NULL pointers, sizes out of range, workspace
+ *     too small, bad scalars) return a non-zero ev_status before anything is launched.
+ *   - Errors that depend on device data (a bad parent[] array, a prefix that does not
+ *     fit the cache, a block id or token id out of range) are reported through the
+ *     optional device word *dev_status (may be NULL): the first error code stored there
+ *     wins (the caller zeroes it beforehand and reads it after synchronising).  Outputs of
+ *     an offending sequence are then unspecified, but no out-of-bounds access is made.
+ *   - Tree encoding: parent[B][T] int32, node 0 is the root (the last committed token,
+ *     parent -1) and 0 <= parent[i] < i for i >= 1; 1 <= T <= 64.
+ *   - Draft tokens: tokens[B][T] int32; tokens[b][i] is the token drafted at node i.
+ *   - KV slots: the tree's own keys/values occupy logical slots L_b .. L_b+T-1 in node
+ *     order, right after the committed prefix of length L_b = prefix_len[b].
+ */
+#ifndef EV_H
+#define EV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ev_status;
+
+enum {
+  EV_OK = 0,
+  EV_ERR_NULL = 1,        /* a required pointer is NULL */
+  EV_ERR_SHAPE = 2,       /* a size is out of range (T, heads, head_dim, V, layout) */
+  EV_ERR_DTYPE = 3,       /* unsupported element type */
+  EV_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the *_workspace() query */
+  EV_ERR_ARG = 5,         /* invalid scalar (temperature, softmax scale) */
+  EV_ERR_LAUNCH = 6,      /* a kernel launch failed */
+  /* device-side codes, stored into *dev_status */
+  EV_DERR_PARENT = 101,   /* parent[] is not a topological tree rooted at node 0 */
+  EV_DERR_BOUNDS = 102,   /* prefix + tree does not fit the cache, or a block id is out of range */
+  EV_DERR_TOKEN = 103,    /* a draft token id is outside [0, V) */
+  EV_DERR_PATH = 104      /* path / accept_len given to compaction is not a valid root path */
+};
+
+typedef enum { EV_F32 = 0, EV_BF16 = 1 } ev_dtype;
+
+/* (host) KV-cache descriptor shared by attention and compaction.
+ *   contiguous (paged = 0): k, v are [B][n_kv_heads][cap][head_dim]
+ *   paged      (paged = 1): k, v are [n_blocks][n_kv_heads][block_size][head_dim];
+ *              logical slot s of sequence b lives in block block_table[b][s / block_size]
+ *              (block_table is device int32 [B][max_blocks_per_seq]) at offset
+ *              s % block_size.
+ *   Compaction touches n_layers layers found at k + l * layer_stride (elements), same for v;
+ *   attention reads layer 0 only. */
+typedef struct {
+  int32_t dtype;              /* ev_dtype of K and V (and of Q / O for attention) */
+  int32_t n_kv_heads;
+  int32_t head_dim;           /* 64 or 128 */
+  int32_t paged;              /* 0 contiguous, 1 paged */
+  void *k;
+  void *v;
+  int32_t n_layers;           /* >= 1 */
+  int64_t layer_stride;       /* elements between consecutive layers */
+  int64_t cap;                /* contiguous: slots per sequence */
+  const int32_t *block_table; /* paged only */
+  int32_t block_size;         /* paged: slots per block, a power of two in [1, 256] */
+  int32_t max_blocks_per_seq; /* paged: columns of block_table */
+  int32_t n_blocks;           /* paged: blocks in the pool */
+} ev_kv_desc;
+
+/* ev_tree_mask_build — ancestor mask of each tree ([TR] sec. 2, mask equation M).
+ *   anc_mask[B][T] uint64: bit j of anc_mask[b][i] is set iff node j is node i or one of
+ *   its ancestors.  depth[B][T] int32 (may be NULL): edges from the root.
+ *   A parent[] that is not topological sets EV_DERR_PARENT. */
+ev_status ev_tree_mask_build(const int32_t *parent, int32_t B, int32_t T,
+                             uint64_t *anc_mask, int32_t *depth,
+                             int32_t *dev_status, hipStream_t stream);
+
+/* Bytes of workspace ev_tree_attention needs for these shapes (0 when none). */
+size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, int32_t Hq);
+
+/* ev_tree_attention — tree-masked attention of the T node queries of each sequence
+ * ([TR] sec. 2: every node attends to the whole committed prefix and, among the tree
+ * slots, exactly to those with M[i][j] = 1; [EX] "Core idea": all branches in one pass).
+ *   q    [B][T][Hq][head_dim], dtype kv->dtype;  query head h reads KV head h / (Hq / Hkv)
+ *   kv   layer 0 of the cache (slots L_b .. L_b+T-1 already hold the tree's own K/V)
+ *   prefix_len [B] int32, anc_mask [B][T] from ev_tree_mask_build
+ *   sm_scale   score scale (pass 1/sqrt(head_dim) for the usual attention)
+ *   out  [B][T][Hq][head_dim], dtype kv->dtype;  lse [B][T][Hq] float, natural log of the
+ *        softmax normaliser of the scaled scores.
+ *   bf16 is computed with bf16 matrix-core products and float32 softmax/accumulation;
+ *   f32 in float32 throughout.  EV_DERR_BOUNDS when L_b + T exceeds the cache. */
+ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
+                            const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
+                            float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes,
+                            int32_t *dev_status, hipStream_t stream);
+
+/* Bytes of workspace the acceptance calls need. */
+size_t ev_accept_workspace(int32_t B, int32_t T, int32_t V);
+
+/* ev_accept_greedy — greedy longest-matching-path acceptance ([EX] "Core idea";
+ * [SN] case 1).  From the root, the target's token at node a is the lowest-index argmax of
+ * the float32 row logits[b][a][:]; the walk moves to the lowest-index child drafted with
+ * that token and stops at the first node with no such child.
+ *   logits [B][T][V] float: row i is the target's next-token logits after node i.
+ *   accept_len[B]: k, the number of accepted drafts.
+ *   path[B][T]: accepted node indices (path[b][0] = 0), -1 after k + 1 entries.
+ *   out_tokens[B][T]: the k + 1 emitted tokens (k drafts and the target's own next
+ *   token at the last accepted node), -1 afterwards. */
+ev_status ev_accept_greedy(const float *logits, const int32_t *tokens, const int32_t *parent,
+                           int32_t B, int32_t T, int32_t V,
+                           int32_t *accept_len, int32_t *path, int32_t *out_tokens,
+                           void *ws, size_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/* ev_accept_rejection — distribution-preserving rejection sampling walked down the tree
+ * ([EX] "Why it works"; [SN] case 3) for deterministic (point-mass) drafts.
+ *   p_a = softmax(logits[b][a] / temperature), evaluated in float64:
+ *     s_y = double(logit_y) * (1.0 / double(temperature)), p(y) = exp(s_y - max s) / sum.
+ *   At node a the children c are tried in ascending index; a child whose token was
+ *   already rejected at a is skipped; child c is accepted iff uniforms[b][c] * Z < p_a(x)
+ *   with Z the residual mass (1 minus the mass of tokens rejected so far at a).  When
+ *   no child is accepted the emitted token is drawn from the residual distribution by
+ *   inverse CDF in ascending token id with t = uniforms[b][0] * Z.
+ *   uniforms [B][T] double in [0, 1).  Outputs as for ev_accept_greedy.
+ *   EV_ERR_ARG unless temperature is finite and > 0. */
+ev_status ev_accept_rejection(const float *logits, const int32_t *tokens, const int32_t *parent,
+                              int32_t B, int32_t T, int32_t V, float temperature,
+                              const double *uniforms,
+                              int32_t *accept_len, int32_t *path, int32_t *out_tokens,
+                              void *ws, size_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/* ev_kv_compact — keep the accepted branch's KV ([TR] sec. 2 sequence diagram).
+ * For m = 1..k (k = accept_len[b], path from an acceptance call), logical slot
+ * L_b + path[b][m] is copied to slot L_b + m, for K and V, every KV head and all
+ * kv->n_layers layers, in place; every source is read before any slot is written.
+ * new_len[B] = L_b + k + 1.  Slots at or beyond L_b + k + 1 are left untouched.
+ * EV_DERR_PATH when path is not strictly increasing within [0, T) from node 0. */
+ev_status ev_kv_compact(const ev_kv_desc *kv, const int32_t *prefix_len, const int32_t *path,
+                        const int32_t *accept_len, int32_t B, int32_t T,
+                        int32_t *new_len, int32_t *dev_status, hipStream_t stream);
+
+/* (host) Static description of a status code. */
+const char *ev_status_string(ev_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EV_H */

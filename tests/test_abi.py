@@ -1,0 +1,92 @@
+"""The C-ABI library loads, exports every entry point its header declares, and rejects
+host-visible argument errors before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_verification_ev_amd as ev
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ev.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ev_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ev.LIB_PATH):
+        pytest.fail("libev.so is not built (run __graft_entry__.build())")
+    return ev.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(ev.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in ev.STATUS_NAMES:
+        assert ev.ev_status_string(code) not in ("", "unknown status")
+    assert ev.ev_status_string(12345) == "unknown status"
+
+
+def _kv(**kw):
+    d = ev.EvKvDesc()
+    d.dtype, d.n_kv_heads, d.head_dim, d.paged = ev.EV_BF16, 8, 128, 0
+    d.k = d.v = 0x1000
+    d.n_layers, d.layer_stride, d.cap = 1, 0, 4176
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_workspace_queries(lib):
+    d = _kv()
+    ws = lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 64, 64)
+    assert ws % 256 == 0
+    assert lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 65, 64) == 0
+    assert lib.ev_tree_attention_workspace(ctypes.byref(_kv(head_dim=96)), 1, 64, 64) == 0
+    assert lib.ev_accept_workspace(1, 64, 128256) == 64 * 126 * 16
+    assert lib.ev_accept_workspace(0, 64, 10) == 0
+
+
+def test_host_errors_return_before_launch(lib):
+    P = 0x1000
+    d = _kv()
+    assert lib.ev_tree_mask_build(P, 1, 0, P, P, None, None) == 2
+    assert lib.ev_tree_mask_build(P, 1, 65, P, P, None, None) == 2
+    assert lib.ev_tree_mask_build(None, 1, 8, P, P, None, None) == 1
+    assert lib.ev_tree_mask_build(None, 0, 8, None, None, None, None) == 0   # empty batch
+    att = lambda desc, T=64, Hq=64, scale=0.088, ws=None, nbytes=0, q=P: lib.ev_tree_attention(
+        q, ctypes.byref(desc), P, P, 1, T, Hq, scale, P, P, ws, nbytes, None, None)
+    assert att(d, Hq=60) == 2                       # Hq not a multiple of Hkv
+    assert att(_kv(head_dim=96)) == 2
+    assert att(_kv(dtype=7)) == 3
+    assert att(d, scale=0.0) == 5
+    assert att(d, scale=float("nan")) == 5
+    assert att(d, q=None) == 1
+    assert att(d) == 4                              # split workspace missing
+    assert att(_kv(paged=1, block_table=None)) == 1
+    assert att(_kv(paged=1, block_table=P, block_size=12, max_blocks_per_seq=4, n_blocks=9)) == 2
+    assert lib.ev_accept_greedy(P, P, P, 1, 8, 0, P, P, P, P, 10, None, None) == 2
+    assert lib.ev_accept_greedy(P, P, P, 1, 8, 100, P, P, P, P, 10, None, None) == 4
+    assert lib.ev_accept_rejection(P, P, P, 1, 8, 100, 0.0, P, P, P, P, P, 10**6, None, None) == 5
+    assert lib.ev_accept_rejection(P, P, P, 1, 8, 100, float("inf"), P, P, P, P, P, 10**6, None, None) == 5
+    assert lib.ev_accept_rejection(P, P, P, 1, 8, 100, 0.7, None, P, P, P, P, 10**6, None, None) == 1
+    assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=0)), P, P, P, 1, 8, P, None, None) == 2
+    assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=2, layer_stride=0)), P, P, P, 1, 8, P, None, None) == 2
+    assert lib.ev_kv_compact(ctypes.byref(d), None, P, P, 1, 8, P, None, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ev.ev_tree_mask_build(torch.zeros((1, 4), dtype=torch.int32))

@@ -1,0 +1,351 @@
+"""GPU parity: the HIP library against the float64 oracle on identical seeded inputs.
+
+Bars: attention O within 1e-2 max-abs and LSE within 1e-3 (bf16 inputs, float32
+softmax); float32 attention within 1e-5 / 1e-5; masks, acceptance (lengths, paths,
+tokens) and compaction bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_attention_verification_ev_amd as ev
+from synth import CONFIGS, generate, round_to_bf16, scaled
+from synth.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+C1, C2, C3, C4, C5 = CONFIGS
+O_TOL_BF16, LSE_TOL_BF16 = 1e-2, 1e-3
+O_TOL_F32, LSE_TOL_F32 = 1e-5, 1e-5
+# A bf16 output cannot be closer to the exact value than half its ulp (2^-8 relative) and
+# the bf16 probabilities of the value product add at most as much again, so elements with
+# |O| > 1.28 (only reachable with a handful of visible keys, e.g. an empty prefix) are held
+# to 2^-7 |O| instead of 1e-2.
+BF16_REL = 2.0 ** -7
+
+
+def o_error(O, Oo, sel, dtype):
+    """Largest error in units of the allowed tolerance (<= 1 passes) and the max-abs error."""
+    mask = np.broadcast_to(sel[..., None], O.shape)
+    err = np.abs(O - Oo)[mask]
+    if dtype == "bf16":
+        tol = np.maximum(O_TOL_BF16, BF16_REL * np.abs(Oo[mask]))
+    else:
+        tol = O_TOL_F32
+    return float((err / tol).max()), float(err.max())
+
+
+def scale_of(cfg):
+    return float(np.float32(1.0 / math.sqrt(cfg.d)))
+
+
+def gpu_attention(inp, dev):
+    kv = ev.KvCache(dev.k, dev.v, dev.block_table)
+    anc, depth = ev.ev_tree_mask_build(dev.parent, check=True)
+    out, lse = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), check=True)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), anc, depth
+
+
+def oracle_attention(inp, seqs=None, heads=None):
+    anc, _ = oracle.tree_mask_batch(inp.parent)
+    return oracle.tree_attention_batch(inp.q, inp.k, inp.v, inp.prefix_len, anc, inp.layout,
+                                       inp.block_table, inp.cfg.block_size, scale_of(inp.cfg),
+                                       seqs=seqs, heads=heads)
+
+
+def check_attention(inp, seqs=None, heads=None):
+    dev = to_device(inp)
+    O, LSE, _, _ = gpu_attention(inp, dev)
+    Oo, Lo = oracle_attention(inp, seqs, heads)
+    sel = np.isfinite(Lo)
+    assert sel.any()
+    o_ratio, o_err = o_error(O, Oo, sel, inp.cfg.dtype)
+    l_err = np.abs(LSE - Lo)[sel].max()
+    tol_l = LSE_TOL_BF16 if inp.cfg.dtype == "bf16" else LSE_TOL_F32
+    assert np.isfinite(O).all() and np.isfinite(LSE).all()
+    assert o_ratio <= 1.0 and l_err <= tol_l, (o_err, l_err)
+    if inp.cfg.L and min(inp.cfg.prefix_range()) >= 128:
+        assert o_err <= (O_TOL_BF16 if inp.cfg.dtype == "bf16" else O_TOL_F32)
+    return o_err, l_err
+
+
+# ---------------------------------------------------------------- mask
+@pytest.mark.parametrize("seed", range(4))
+def test_mask_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    B, T = 7, [1, 2, 17, 64][seed]
+    parent = np.array([[-1] + [int(rng.integers(i)) for i in range(1, T)] for _ in range(B)], np.int32)
+    anc, depth = ev.ev_tree_mask_build(torch.from_numpy(parent).cuda(), check=True)
+    ao, do = oracle.tree_mask_batch(parent)
+    assert np.array_equal(anc.cpu().numpy().view(np.uint64), ao)
+    assert np.array_equal(depth.cpu().numpy(), do)
+
+
+def test_mask_rejects_bad_parent():
+    parent = torch.tensor([[-1, 0, 3, 1]], dtype=torch.int32, device="cuda")
+    with pytest.raises(ev.EvError) as e:
+        ev.ev_tree_mask_build(parent, check=True)
+    assert e.value.code == 101
+
+
+# ---------------------------------------------------------------- attention
+ATTN_SMALL = [
+    ("C1", C1),
+    ("C2_L300", scaled(C2, L=300, V=64)),
+    ("C3_L300", scaled(C3, L=300, V=64)),
+    ("C3_L0", scaled(C3, L=0, V=64)),
+    ("C3_L64_aligned", scaled(C3, L=64, V=64)),
+    ("C4_small", scaled(C4, B=4, L=(40, 400), V=64)),
+    ("C5_small", scaled(C5, B=2, L=700, V=64)),
+    ("chain64_mha", scaled(C2, T=64, tree="chain", L=130, V=64, Hq=4, Hkv=4)),
+    ("star64_gqa", scaled(C3, tree="star", L=77, V=64)),
+    ("root_only", scaled(C3, T=1, tree="grow", L=200, V=64)),
+    ("bf16_d64", scaled(C3, d=64, L=333, V=64)),
+    ("f32_d128", scaled(C1, d=128, L=190, Hq=8, Hkv=2, V=64)),
+    ("gqa4_T26", scaled(C2, Hq=32, Hkv=8, L=515, V=64)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", ATTN_SMALL, ids=[n for n, _ in ATTN_SMALL])
+def test_attention_small(name, cfg):
+    check_attention(generate(cfg, with_logits=False))
+
+
+@pytest.mark.parametrize("cfg", [C2, C3], ids=["C2_full", "C3_full"])
+def test_attention_full_contiguous(cfg):
+    check_attention(generate(cfg, with_logits=False))
+
+
+def test_attention_full_batched_paged():
+    check_attention(generate(C4, with_logits=False))
+
+
+def test_attention_full_long_context_sampled_heads():
+    inp = generate(C5, with_logits=False)
+    check_attention(inp, heads=[0, 9, 18, 27, 36, 45, 54, 63])
+
+
+def test_paged_equals_contiguous_on_the_same_data():
+    cfg = scaled(C4, B=3, L=(100, 900), V=64)
+    a = generate(cfg, layout="contiguous", with_logits=False)
+    b = generate(cfg, layout="paged", with_logits=False)
+    Oa, La, _, _ = gpu_attention(a, to_device(a))
+    Ob, Lb, _, _ = gpu_attention(b, to_device(b))
+    assert np.abs(Oa - Ob).max() <= 2e-3 and np.abs(La - Lb).max() <= 1e-5
+
+
+def test_attention_is_deterministic():
+    inp = generate(scaled(C3, L=1000, V=64), with_logits=False)
+    dev = to_device(inp)
+    O1, L1, _, _ = gpu_attention(inp, dev)
+    for _ in range(5):
+        O2, L2, _, _ = gpu_attention(inp, dev)
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_attention_reports_prefix_beyond_cache():
+    inp = generate(scaled(C3, L=100, V=64), with_logits=False)
+    dev = to_device(inp)
+    dev.prefix_len.fill_(inp.cap)                      # L + T > cap
+    kv = ev.KvCache(dev.k, dev.v)
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    with pytest.raises(ev.EvError) as e:
+        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, check=True)
+    assert e.value.code == 102
+
+
+def test_attention_reports_bad_block_id():
+    inp = generate(scaled(C4, B=2, L=(50, 90), V=64), with_logits=False)
+    dev = to_device(inp)
+    dev.block_table[1, 0] = inp.k.shape[0] + 5
+    kv = ev.KvCache(dev.k, dev.v, dev.block_table)
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    with pytest.raises(ev.EvError) as e:
+        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, check=True)
+    assert e.value.code == 102
+
+
+# ---------------------------------------------------------------- acceptance
+def run_greedy(inp, dev):
+    out = ev.ev_accept_greedy(dev.logits, dev.tokens, dev.parent, check=True)
+    return [t.cpu().numpy() for t in out]
+
+
+def run_rejection(inp, dev):
+    out = ev.ev_accept_rejection(dev.logits, dev.tokens, dev.parent, dev.tau, dev.uniforms, check=True)
+    return [t.cpu().numpy() for t in out]
+
+
+ACC_CASES = [
+    ("C1", C1), ("C2", C2),
+    ("C3_V5000", scaled(C3, V=5000, L=8)),
+    ("C4_V3001", scaled(C4, V=3001, L=(8, 16))),
+    ("C5_V128256_B2", scaled(C5, B=2, L=8)),
+    ("V1", scaled(C3, V=1, T=1, L=8)),
+    ("V7_chain", scaled(C3, V=70, T=64, tree="chain", L=8)),
+]
+
+
+@pytest.mark.parametrize("mode", ["planted", "raw"])
+@pytest.mark.parametrize("name,cfg", ACC_CASES, ids=[n for n, _ in ACC_CASES])
+def test_greedy_bit_exact(name, cfg, mode):
+    inp = generate(cfg, tokens=mode, with_kv=False)
+    g = run_greedy(inp, to_device(inp))
+    o = oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
+    for a, b in zip(g, o):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("mode", ["planted", "raw"])
+@pytest.mark.parametrize("name,cfg", ACC_CASES, ids=[n for n, _ in ACC_CASES])
+def test_rejection_bit_exact(name, cfg, mode):
+    inp = generate(cfg, tokens=mode, with_kv=False)
+    r = run_rejection(inp, to_device(inp))
+    o = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
+    assert min(min(m) for m in o[3]) > 1e-12            # no decision is a rounding tie
+    for a, b in zip(r, o[:3]):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", [C3, C4], ids=["C3_full", "C4_full"])
+def test_rejection_full_size(cfg):
+    inp = generate(cfg, with_kv=False)
+    r = run_rejection(inp, to_device(inp))
+    o = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
+    assert min(min(m) for m in o[3]) > 1e-12
+    for a, b in zip(r, o[:3]):
+        assert np.array_equal(a, b)
+
+
+def test_rejection_many_seeds_bonus_paths():
+    """Many sequences whose walks end in residual draws with rejected siblings."""
+    cfg = scaled(C3, B=64, V=2000, L=8)
+    inp = generate(cfg, tokens="raw", with_kv=False)
+    r = run_rejection(inp, to_device(inp))
+    o = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
+    for a, b in zip(r, o[:3]):
+        assert np.array_equal(a, b)
+
+
+def test_accept_reports_bad_token():
+    inp = generate(scaled(C3, V=500, L=8), with_kv=False)
+    dev = to_device(inp)
+    dev.tokens[0, 5] = 500
+    with pytest.raises(ev.EvError) as e:
+        ev.ev_accept_greedy(dev.logits, dev.tokens, dev.parent, check=True)
+    assert e.value.code == 103
+
+
+# ---------------------------------------------------------------- compaction
+def compaction_case(cfg, layout, n_layers, seed=0):
+    inp = generate(cfg, layout=layout, with_logits=False)
+    rng = np.random.default_rng(seed)
+    B, T = cfg.B, cfg.T
+    paths = np.full((B, T), -1, np.int32)
+    acc = np.zeros(B, np.int32)
+    for b in range(B):
+        # a random root path of the drawn tree
+        leaf = int(rng.integers(T))
+        p = []
+        u = leaf
+        while u != -1:
+            p.append(u)
+            u = int(inp.parent[b, u])
+        p = p[::-1]
+        paths[b, :len(p)] = p
+        acc[b] = len(p) - 1
+    k = np.stack([inp.k + 1000.0 * layer for layer in range(n_layers)])
+    v = np.stack([inp.v - 1000.0 * layer for layer in range(n_layers)])
+    if cfg.dtype == "bf16":
+        k, v = round_to_bf16(k), round_to_bf16(v)
+    return inp, k, v, paths, acc
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("n_layers", [1, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_compaction_bit_exact(layout, n_layers, dtype):
+    cfg = scaled(C4, B=5, L=(10, 200), V=64, dtype=dtype)
+    inp, k, v, paths, acc = compaction_case(cfg, layout, n_layers)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kd = torch.from_numpy(k).cuda().to(dt)
+    vd = torch.from_numpy(v).cuda().to(dt)
+    bt = None if layout == "contiguous" else torch.from_numpy(inp.block_table).cuda()
+    kv = ev.KvCache(kd, vd, bt, layered=True)
+    new_len = ev.ev_kv_compact(kv, torch.from_numpy(inp.prefix_len).cuda(), torch.from_numpy(paths).cuda(),
+                               torch.from_numpy(acc).cuda(), check=True)
+    ko, vo, nlo = oracle.kv_compact(k, v, inp.prefix_len, paths, acc, layout, inp.block_table,
+                                    cfg.block_size, layered=True)
+    assert np.array_equal(new_len.cpu().numpy(), nlo)
+    assert np.array_equal(kd.float().cpu().numpy(), ko, equal_nan=True)
+    assert np.array_equal(vd.float().cpu().numpy(), vo, equal_nan=True)
+
+
+def test_compaction_maximal_overlap():
+    cfg = scaled(C3, L=50, V=64, T=64, tree="chain")
+    inp = generate(cfg, with_logits=False)
+    paths = np.full((1, 64), -1, np.int32)
+    paths[0, :63] = [0] + list(range(2, 64))               # a_m = m + 1
+    acc = np.array([62], np.int32)
+    kd = torch.from_numpy(inp.k).cuda().to(torch.bfloat16)
+    vd = torch.from_numpy(inp.v).cuda().to(torch.bfloat16)
+    ev.ev_kv_compact(ev.KvCache(kd, vd), torch.from_numpy(inp.prefix_len).cuda(),
+                     torch.from_numpy(paths).cuda(), torch.from_numpy(acc).cuda(), check=True)
+    ko, vo, _ = oracle.kv_compact(inp.k, inp.v, inp.prefix_len, paths, acc, "contiguous")
+    assert np.array_equal(kd.float().cpu().numpy(), ko, equal_nan=True)
+    assert np.array_equal(vd.float().cpu().numpy(), vo, equal_nan=True)
+
+
+def test_compaction_reports_bad_path():
+    cfg = scaled(C3, L=50, V=64)
+    inp = generate(cfg, with_logits=False)
+    dev = to_device(inp)
+    paths = torch.tensor([[0, 5, 3] + [-1] * 61], dtype=torch.int32, device="cuda")
+    before = dev.k.clone()
+    with pytest.raises(ev.EvError) as e:
+        ev.ev_kv_compact(ev.KvCache(dev.k, dev.v), dev.prefix_len, paths,
+                         torch.tensor([2], dtype=torch.int32, device="cuda"), check=True)
+    assert e.value.code == 104
+    assert torch.equal(before.view(torch.int16), dev.k.view(torch.int16))
+
+
+# ---------------------------------------------------------------- whole pass
+@pytest.mark.parametrize("cfg", CONFIGS, ids=[f"C{c.index}" for c in CONFIGS])
+def test_full_verification_pass(cfg):
+    """mask -> attention -> acceptance -> compaction on the workload at full size,
+    attention compared on a sample of sequences/heads, the rest exhaustively."""
+    inp = generate(cfg)
+    dev = to_device(inp)
+    O, LSE, anc, _ = gpu_attention(inp, dev)
+    seqs = list(range(min(cfg.B, 2)))
+    heads = sorted({0, cfg.Hq // 2, cfg.Hq - 1})
+    Oo, Lo = oracle_attention(inp, seqs=seqs, heads=heads)
+    sel = np.isfinite(Lo)
+    tol_o, tol_l = (O_TOL_BF16, LSE_TOL_BF16) if cfg.dtype == "bf16" else (O_TOL_F32, LSE_TOL_F32)
+    assert np.abs(LSE - Lo)[sel].max() <= tol_l
+    assert np.abs(O - Oo)[np.broadcast_to(sel[..., None], O.shape)].max() <= tol_o
+    kmax = 0
+    kv = ev.KvCache(dev.k, dev.v, dev.block_table)
+    for mode in cfg.accept:
+        if mode == "greedy":
+            got = run_greedy(inp, dev)
+            exp = oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
+        else:
+            got = run_rejection(inp, dev)
+            exp = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)[:3]
+        for a, b in zip(got, exp):
+            assert np.array_equal(a, b), mode
+        kmax = max(kmax, int(exp[0].max()))
+    if cfg.B > 1:
+        assert kmax >= 2                                    # planted trees walk deep
+    acc, path = torch.from_numpy(exp[0]).cuda(), torch.from_numpy(exp[1]).cuda()
+    new_len = ev.ev_kv_compact(kv, dev.prefix_len, path, acc, check=True)
+    ko, vo, nlo = oracle.kv_compact(inp.k, inp.v, inp.prefix_len, exp[1], exp[0], inp.layout,
+                                    inp.block_table, cfg.block_size)
+    assert np.array_equal(new_len.cpu().numpy(), nlo)
+    assert np.array_equal(dev.k.float().cpu().numpy(), ko, equal_nan=True)
+    assert np.array_equal(dev.v.float().cpu().numpy(), vo, equal_nan=True)

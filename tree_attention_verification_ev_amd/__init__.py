@@ -1,0 +1,296 @@
+"""Python binding of libev.so: one-pass verification of a drafted token tree on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in include/ev.h.  Every function has the
+name of the C entry point it calls and takes torch tensors that already live on the GPU;
+torch provides device memory and the current HIP stream, nothing else.  All arithmetic
+happens in the HIP kernels of libev.so; there is no host fallback: if the library is not
+built or cannot be loaded, every call raises.
+
+Outputs and workspace may be passed in (preallocated) or are allocated here with
+torch.empty.  With check=True a call synchronises and raises EvError when the device
+status word reports a data error; the default leaves the call asynchronous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libev.so")
+
+EV_OK = 0
+EV_F32, EV_BF16 = 0, 1
+STATUS_NAMES = {
+    0: "EV_OK", 1: "EV_ERR_NULL", 2: "EV_ERR_SHAPE", 3: "EV_ERR_DTYPE", 4: "EV_ERR_WORKSPACE",
+    5: "EV_ERR_ARG", 6: "EV_ERR_LAUNCH", 101: "EV_DERR_PARENT", 102: "EV_DERR_BOUNDS",
+    103: "EV_DERR_TOKEN", 104: "EV_DERR_PATH",
+}
+EXPORTED = (
+    "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
+    "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection", "ev_kv_compact",
+    "ev_status_string",
+)
+
+
+class EvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS_NAMES.get(code, code)} ({_status_text(code)})")
+
+
+class EvKvDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("paged", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("n_layers", ctypes.c_int32), ("layer_stride", ctypes.c_int64), ("cap", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libev.so (raises EvError-free OSError/RuntimeError when absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m tree_attention_verification_ev_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        kv = ctypes.POINTER(EvKvDesc)
+        sigs = {
+            "ev_tree_mask_build": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
+            "ev_tree_attention_workspace": (_SZ, [kv, _I32, _I32, _I32]),
+            "ev_tree_attention": (_I32, [_P, kv, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ,
+                                         _P, _P]),
+            "ev_accept_workspace": (_SZ, [_I32, _I32, _I32]),
+            "ev_accept_greedy": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
+            "ev_accept_rejection": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _P,
+                                           _SZ, _P, _P]),
+            "ev_kv_compact": (_I32, [kv, _P, _P, _P, _I32, _I32, _P, _P, _P]),
+            "ev_status_string": (ctypes.c_char_p, [_I32]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _status_text(code: int) -> str:
+    try:
+        return lib().ev_status_string(code).decode()
+    except Exception:  # library missing while formatting an error
+        return "?"
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _finish(code: int, where: str, status: Optional[torch.Tensor], check: bool):
+    if code != EV_OK:
+        raise EvError(code, where)
+    if check and status is not None:
+        torch.cuda.current_stream(status.device).synchronize()
+        dev_code = int(status.item())
+        if dev_code != EV_OK:
+            raise EvError(dev_code, where)
+
+
+def _status_word(device, status):
+    return torch.zeros(1, dtype=torch.int32, device=device) if status is None else status
+
+
+class KvCache:
+    """A KV cache layout plus the ctypes descriptor handed to the library.
+
+    contiguous: k, v [B][Hkv][cap][d] (or [n_layers][B][Hkv][cap][d] with layered=True)
+    paged:      k, v [n_blocks][Hkv][block_size][d] (or with a leading layer axis) and
+                block_table int32 [B][max_blocks_per_seq]
+    """
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                 layered: bool = False):
+        _dev(k, "k")
+        _dev(v, "v")
+        if k.shape != v.shape or k.dtype != v.dtype:
+            raise ValueError("k and v must have the same shape and dtype")
+        if k.dtype == torch.float32:
+            dtype = EV_F32
+        elif k.dtype == torch.bfloat16:
+            dtype = EV_BF16
+        else:
+            raise ValueError(f"unsupported KV dtype {k.dtype}")
+        layer_shape = k.shape[1:] if layered else k.shape
+        n_layers = k.shape[0] if layered else 1
+        layer_stride = k.stride(0) if layered else 0
+        self.k, self.v, self.block_table, self.layered = k, v, block_table, layered
+        self.paged = block_table is not None
+        d = layer_shape[-1]
+        hkv = layer_shape[1]
+        desc = EvKvDesc()
+        desc.dtype, desc.n_kv_heads, desc.head_dim, desc.paged = dtype, hkv, d, int(self.paged)
+        desc.k, desc.v = k.data_ptr(), v.data_ptr()
+        desc.n_layers, desc.layer_stride = n_layers, layer_stride
+        if self.paged:
+            _dev(block_table, "block_table", torch.int32)
+            desc.cap = 0
+            desc.block_table = block_table.data_ptr()
+            desc.block_size = layer_shape[2]
+            desc.max_blocks_per_seq = block_table.shape[1]
+            desc.n_blocks = layer_shape[0]
+        else:
+            desc.cap = layer_shape[2]
+            desc.block_table = None
+            desc.block_size = desc.max_blocks_per_seq = desc.n_blocks = 0
+        self.desc = desc
+        self.dtype = k.dtype
+        self.n_kv_heads = hkv
+        self.head_dim = d
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def ev_tree_mask_build(parent: torch.Tensor, anc_mask: Optional[torch.Tensor] = None,
+                       depth: Optional[torch.Tensor] = None, dev_status: Optional[torch.Tensor] = None,
+                       check: bool = False):
+    """Ancestor bitmasks (int64 view of uint64) and depths of parent[B][T]."""
+    _dev(parent, "parent", torch.int32)
+    B, T = parent.shape
+    dev = parent.device
+    anc_mask = torch.empty((B, T), dtype=torch.int64, device=dev) if anc_mask is None else anc_mask
+    depth = torch.empty((B, T), dtype=torch.int32, device=dev) if depth is None else depth
+    status = _status_word(dev, dev_status)
+    code = lib().ev_tree_mask_build(_ptr(parent), B, T, _ptr(anc_mask), _ptr(depth), _ptr(status),
+                                    _stream(dev))
+    _finish(code, "ev_tree_mask_build", status, check)
+    return anc_mask, depth
+
+
+def ev_tree_attention_workspace(kv: KvCache, B: int, T: int, Hq: int) -> int:
+    return int(lib().ev_tree_attention_workspace(kv.ref(), B, T, Hq))
+
+
+def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, anc_mask: torch.Tensor,
+                      sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                      dev_status: Optional[torch.Tensor] = None, check: bool = False):
+    """Tree-masked attention; returns (out [B][T][Hq][d], lse [B][T][Hq] float32)."""
+    _dev(q, "q", kv.dtype)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(anc_mask, "anc_mask", torch.int64)
+    B, T, Hq, d = q.shape
+    dev = q.device
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    need = ev_tree_attention_workspace(kv, B, T, Hq)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = _status_word(dev, dev_status)
+    code = lib().ev_tree_attention(_ptr(q), kv.ref(), _ptr(prefix_len), _ptr(anc_mask), B, T, Hq,
+                                   float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                   _ptr(status), _stream(dev))
+    _finish(code, "ev_tree_attention", status, check)
+    return out, lse
+
+
+def ev_accept_workspace(B: int, T: int, V: int) -> int:
+    return int(lib().ev_accept_workspace(B, T, V))
+
+
+def _accept_outputs(B, T, dev, accept_len, path, out_tokens):
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    path = torch.empty((B, T), dtype=torch.int32, device=dev) if path is None else path
+    out_tokens = torch.empty((B, T), dtype=torch.int32, device=dev) if out_tokens is None else out_tokens
+    return accept_len, path, out_tokens
+
+
+def ev_accept_greedy(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                     accept_len=None, path=None, out_tokens=None, ws=None, dev_status=None,
+                     check: bool = False):
+    """Greedy acceptance; returns (accept_len [B], path [B][T], out_tokens [B][T])."""
+    _dev(logits, "logits", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    B, T, V = logits.shape
+    dev = logits.device
+    accept_len, path, out_tokens = _accept_outputs(B, T, dev, accept_len, path, out_tokens)
+    if ws is None:
+        ws = torch.empty(max(1, ev_accept_workspace(B, T, V)), dtype=torch.uint8, device=dev)
+    status = _status_word(dev, dev_status)
+    code = lib().ev_accept_greedy(_ptr(logits), _ptr(tokens), _ptr(parent), B, T, V, _ptr(accept_len),
+                                  _ptr(path), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _ptr(status), _stream(dev))
+    _finish(code, "ev_accept_greedy", status, check)
+    return accept_len, path, out_tokens
+
+
+def ev_accept_rejection(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                        temperature: float, uniforms: torch.Tensor, accept_len=None, path=None,
+                        out_tokens=None, ws=None, dev_status=None, check: bool = False):
+    """Rejection-sampling acceptance; returns (accept_len, path, out_tokens)."""
+    _dev(logits, "logits", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    _dev(uniforms, "uniforms", torch.float64)
+    B, T, V = logits.shape
+    dev = logits.device
+    accept_len, path, out_tokens = _accept_outputs(B, T, dev, accept_len, path, out_tokens)
+    if ws is None:
+        ws = torch.empty(max(1, ev_accept_workspace(B, T, V)), dtype=torch.uint8, device=dev)
+    status = _status_word(dev, dev_status)
+    code = lib().ev_accept_rejection(_ptr(logits), _ptr(tokens), _ptr(parent), B, T, V,
+                                     float(temperature), _ptr(uniforms), _ptr(accept_len), _ptr(path),
+                                     _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _ptr(status), _stream(dev))
+    _finish(code, "ev_accept_rejection", status, check)
+    return accept_len, path, out_tokens
+
+
+def ev_kv_compact(kv: KvCache, prefix_len: torch.Tensor, path: torch.Tensor, accept_len: torch.Tensor,
+                  new_len: Optional[torch.Tensor] = None, dev_status=None, check: bool = False):
+    """Move the accepted path's KV next to the prefix in place; returns new_len [B]."""
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(path, "path", torch.int32)
+    _dev(accept_len, "accept_len", torch.int32)
+    B, T = path.shape
+    dev = path.device
+    new_len = torch.empty(B, dtype=torch.int32, device=dev) if new_len is None else new_len
+    status = _status_word(dev, dev_status)
+    code = lib().ev_kv_compact(kv.ref(), _ptr(prefix_len), _ptr(path), _ptr(accept_len), B, T,
+                               _ptr(new_len), _ptr(status), _stream(dev))
+    _finish(code, "ev_kv_compact", status, check)
+    return new_len
+
+
+def ev_status_string(code: int) -> str:
+    return lib().ev_status_string(code).decode()
+
+
+__all__ = ["KvCache", "EvError", "EvKvDesc", "lib", "LIB_PATH", *EXPORTED]
