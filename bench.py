@@ -1,0 +1,306 @@
+"""Benchmark: verified tree-nodes/s for one verification pass of a drafted token tree.
+
+One step = the whole hot path on one batch: ancestor-mask build, tree attention over
+the KV prefix + ancestors, acceptance (rejection sampling for the Llama-3-70B-shaped
+layer), and KV compaction of the accepted path.  Inputs are seeded synthetic arrays
+already resident in HBM; several buffer sets rotate so that the timed footprint is at
+least 512 MB (twice the 256 MB Infinity Cache) and no step reads a cache-warm copy.
+Each set's step is captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed,
+so the timed loop measures the GPU rather than Python marshalling.
+
+Printed: one JSON line with the metric, per-kernel timings, the attention kernel's
+roofline fraction (HIP events around that kernel's launches on its own stream) and the
+CPU oracle's throughput on the same workload as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import tree_attention_verification_ev_amd as ev  # noqa: E402
+from synth import config_by_name, generate  # noqa: E402
+from synth.device import to_device  # noqa: E402
+
+METRIC = "verified tree-nodes/s + KV HBM GB/s (% roofline), GQA 64/8 d128 L=4096 T=64"
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+FOOTPRINT_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attention_llama3_70b_layer_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "tree_attention_verification_ev_amd", "csrc", "tree_attention.hip")
+
+
+def algorithmic_work(inp):
+    """Bytes and flops of one attention launch by the definitions of the method."""
+    cfg = inp.cfg
+    e = 2 if cfg.dtype == "bf16" else 4
+    anc_depth = []
+    for p in inp.parent:
+        depth = np.zeros(cfg.T, np.int64)
+        for i in range(1, cfg.T):
+            depth[i] = depth[p[i]] + 1
+        anc_depth.append(int((depth + 1).sum()))
+    L = inp.prefix_len.astype(np.int64)
+    kv_bytes = int(sum(2 * cfg.Hkv * (L[b] + cfg.T) * cfg.d * e for b in range(cfg.B)))
+    qo_bytes = 2 * cfg.B * cfg.T * cfg.Hq * cfg.d * e + 4 * cfg.B * cfg.T * cfg.Hq
+    table = 0
+    if inp.layout == "paged":
+        table = int(sum(4 * math.ceil((L[b] + cfg.T) / cfg.block_size) for b in range(cfg.B)))
+    flops = int(sum(4 * cfg.Hq * cfg.d * (cfg.T * L[b] + anc_depth[b]) for b in range(cfg.B)))
+    return {"bytes": kv_bytes + qo_bytes + table, "kv_bytes": kv_bytes, "flops": flops,
+            "logit_bytes": 4 * cfg.B * cfg.T * cfg.V}
+
+
+class BufferSet:
+    """Device inputs, preallocated outputs and the per-call graphs of one batch copy."""
+
+    def __init__(self, inp, dev, ws_attn, ws_acc):
+        cfg = inp.cfg
+        self.cfg, self.d = cfg, dev
+        self.kv = ev.KvCache(dev.k, dev.v, dev.block_table)
+        B, T = cfg.B, cfg.T
+        z = lambda *s, dt=torch.int32: torch.zeros(s, dtype=dt, device="cuda")
+        self.anc, self.depth = z(B, T, dt=torch.int64), z(B, T)
+        self.out = torch.empty_like(dev.q)
+        self.lse = z(B, T, cfg.Hq, dt=torch.float32)
+        self.acc, self.path, self.tok, self.new_len = z(B), z(B, T), z(B, T), z(B)
+        self.status = z(1)
+        self.ws_attn, self.ws_acc = ws_attn, ws_acc
+        self.scale = float(np.float32(1.0 / math.sqrt(cfg.d)))
+        self.mode = "rejection" if "rejection" in cfg.accept else "greedy"
+
+    def mask(self):
+        ev.ev_tree_mask_build(self.d.parent, self.anc, self.depth, self.status)
+
+    def attention(self):
+        ev.ev_tree_attention(self.d.q, self.kv, self.d.prefix_len, self.anc, self.scale, self.out,
+                             self.lse, self.ws_attn, self.status)
+
+    def accept(self):
+        if self.mode == "rejection":
+            ev.ev_accept_rejection(self.d.logits, self.d.tokens, self.d.parent, self.d.tau,
+                                   self.d.uniforms, self.acc, self.path, self.tok, self.ws_acc,
+                                   self.status)
+        else:
+            ev.ev_accept_greedy(self.d.logits, self.d.tokens, self.d.parent, self.acc, self.path,
+                                self.tok, self.ws_acc, self.status)
+
+    def compact(self):
+        ev.ev_kv_compact(self.kv, self.d.prefix_len, self.path, self.acc, self.new_len, self.status)
+
+    def step(self):
+        self.mask()
+        self.attention()
+        self.accept()
+        self.compact()
+
+
+def capture(fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def prime_gpu(ms: float = 20.0):
+    """Queue a few ms of unrelated GPU work so that the host enqueues ahead of the device."""
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(4):
+        a = a @ a
+        a = a / (a.abs().amax() + 1)
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t0) / 4
+    for _ in range(max(1, int(ms / 1e3 / max(per, 1e-6)))):
+        a = a @ a
+    return a
+
+
+def kernel_times(sets, graphs, reps):
+    """Average device time of each call, from HIP events on the launch stream."""
+    out = {}
+    for name in ("mask", "attention", "accept", "compact"):
+        keep = prime_gpu()
+        pairs = []
+        for r in range(reps):
+            s = r % len(sets)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graphs[s][name].replay()
+            e1.record()
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        del keep
+        ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        out[name] = {"mean_us": statistics.fmean(ts), "median_us": statistics.median(ts),
+                     "p10_us": float(np.percentile(ts, 10)), "p90_us": float(np.percentile(ts, 90))}
+    return out
+
+
+def traffic_entry():
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(ATTN_SRC, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+        if t.get("source_sha256") != h:
+            return None
+        return t["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, budget_s: float):
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    cfg = inp.cfg
+    scale = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        anc, _ = oracle.tree_mask_batch(inp.parent)
+        oracle.tree_attention_batch(inp.q, inp.k, inp.v, inp.prefix_len, anc, inp.layout,
+                                    inp.block_table, cfg.block_size, scale)
+        if "rejection" in cfg.accept:
+            r = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
+        else:
+            r = oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
+        oracle.kv_compact(inp.k, inp.v, inp.prefix_len, r[1], r[0], inp.layout, inp.block_table,
+                          cfg.block_size)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": cfg.B * cfg.T * steps / el, "unit": "tree-nodes/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full verification step(s) of the {cfg.name} workload (B={cfg.B}, "
+                      f"T={cfg.T}): float64 mask + explicit-mask attention + "
+                      f"{'rejection' if 'rejection' in cfg.accept else 'greedy'} walk + compaction, "
+                      f"{el:.1f} s on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="llama3_70b_layer")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-GPU share of a sharded verification is the single-GPU workload).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ev.lib()
+    cfg = config_by_name(args.config)
+    inp = generate(cfg)
+    dev0 = to_device(inp)
+    per_set = sum(t.numel() * t.element_size() for t in (dev0.q, dev0.k, dev0.v, dev0.logits))
+    n_sets = max(1, math.ceil(FOOTPRINT_BYTES / per_set))
+    kv_tmp = ev.KvCache(dev0.k, dev0.v, dev0.block_table)
+    ws_attn = torch.empty(max(1, ev.ev_tree_attention_workspace(kv_tmp, cfg.B, cfg.T, cfg.Hq)),
+                          dtype=torch.uint8, device="cuda")
+    ws_acc = torch.empty(max(1, ev.ev_accept_workspace(cfg.B, cfg.T, cfg.V)), dtype=torch.uint8,
+                         device="cuda")
+    sets = [BufferSet(inp, dev0 if i == 0 else to_device(inp), ws_attn, ws_acc) for i in range(n_sets)]
+
+    # eager reference of the acceptance result, then capture
+    sets[0].step()
+    torch.cuda.synchronize()
+    if int(sets[0].status.item()) != 0:
+        raise ev.EvError(int(sets[0].status.item()), "bench eager step")
+    ref = (sets[0].acc.clone(), sets[0].path.clone(), sets[0].tok.clone())
+    graphs = []
+    for s in sets:
+        graphs.append({"step": capture(s.step), "mask": capture(s.mask),
+                       "attention": capture(s.attention), "accept": capture(s.accept),
+                       "compact": capture(s.compact)})
+    for _ in range(3):                                    # replays agree with the eager run
+        graphs[0]["step"].replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (sets[0].acc, sets[0].path, sets[0].tok)):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay disagrees with the eager step")
+
+    for w in range(args.warmup):
+        graphs[w % n_sets]["step"].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        graphs[s % n_sets]["step"].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if any(int(s.status.item()) != 0 for s in sets):
+        raise RuntimeError("device status reported an error during the timed steps")
+
+    if args.calibrate:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    kt = kernel_times(sets, graphs, max(50, min(args.steps, 400)))
+    work = algorithmic_work(inp)
+    t_attn = kt["attention"]["mean_us"] * 1e-6
+    ms_per_step = elapsed * 1e3 / args.steps
+    nodes = cfg.B * cfg.T
+    if cfg.dtype == "bf16":
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+        achieved = work["flops"] / t_attn / 1e12
+    else:
+        bound, peak, unit = "alu", PEAK_F32_TFLOPS, "TFLOP/s"
+        achieved = work["flops"] / t_attn / 1e12
+    kv_gbps = work["bytes"] / t_attn / 1e9
+    result = {
+        "metric": METRIC,
+        "value": nodes / (ms_per_step * 1e-3),
+        "unit": "tree-nodes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.workload, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+                   "L": cfg.L, "T": cfg.T, "V": cfg.V, "kv_layout": inp.layout,
+                   "acceptance": sets[0].mode, "tau": cfg.tau, "buffer_sets": n_sets},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic_entry(),
+                     "kernel": "ev_tree_attention", "algorithmic_flops": work["flops"],
+                     "algorithmic_bytes": work["bytes"]},
+        "kv_hbm_gbps": kv_gbps,
+        "kv_hbm_frac": kv_gbps / PEAK_HBM_GBPS,
+        "attention_nodes_per_s": nodes / t_attn,
+        "kernels_us": {k: round(v["mean_us"], 3) for k, v in kt.items()},
+        "kernels_us_p10_p90": {k: [round(v["p10_us"], 3), round(v["p90_us"], 3)] for k, v in kt.items()},
+        "accept_len": int(ref[0].float().mean().item()),
+        "tokens_per_step": float(ref[0].float().mean().item()) + 1.0,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

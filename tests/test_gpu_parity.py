@@ -349,3 +349,48 @@ def test_full_verification_pass(cfg):
     assert np.array_equal(new_len.cpu().numpy(), nlo)
     assert np.array_equal(dev.k.float().cpu().numpy(), ko, equal_nan=True)
     assert np.array_equal(dev.v.float().cpu().numpy(), vo, equal_nan=True)
+
+
+# ---------------------------------------------------------------- graph capture
+def test_graph_replays_match_eager():
+    """The verification calls captured in a HIP graph give the eager results on every replay,
+    with unrelated eager work and synchronisations between replays."""
+    cfg = scaled(C3, L=700, V=6000)
+    inp = generate(cfg)
+    dev = to_device(inp)
+    kv = ev.KvCache(dev.k, dev.v)
+    B, T = cfg.B, cfg.T
+    anc = torch.zeros((B, T), dtype=torch.int64, device="cuda")
+    depth = torch.zeros((B, T), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(dev.q)
+    lse = torch.zeros((B, T, cfg.Hq), dtype=torch.float32, device="cuda")
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    path = torch.zeros((B, T), dtype=torch.int32, device="cuda")
+    tok = torch.zeros((B, T), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws_a = torch.empty(max(1, ev.ev_tree_attention_workspace(kv, B, T, cfg.Hq)), dtype=torch.uint8,
+                       device="cuda")
+    ws_r = torch.empty(ev.ev_accept_workspace(B, T, cfg.V), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ev.ev_tree_mask_build(dev.parent, anc, depth, status)
+        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(cfg), out, lse, ws_a, status)
+        ev.ev_accept_rejection(dev.logits, dev.tokens, dev.parent, dev.tau, dev.uniforms, acc, path,
+                               tok, ws_r, status)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (anc, out, lse, acc, path, tok)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        for t in (anc, out, lse, acc, path, tok):
+            t.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()      # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (anc, out, lse, acc, path, tok)):
+            assert torch.equal(a, b)
+        assert int(status.item()) == 0 and torch.isfinite(junk)

@@ -8,24 +8,31 @@
 // gfx950 design (bf16):
 //   * Work unit = (sequence, KV head, block of query rows, range of key tiles).  The rows
 //     of a unit are the T*G (node, q-head-in-group) pairs that share one KV head, so a
-//     grouped-query layer reuses each K/V byte G*T times.
-//   * A workgroup of NW wavefronts stages 64-key tiles of K (row-major) and V (transposed)
-//     in LDS; each wavefront owns QT tiles of 32 query rows.
-//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//     the accumulator column is the query, so every lane holds 16 keys of ONE query and
-//     the softmax statistics, the rescale of the output and the final normalisation are
-//     lane-local (only the row max crosses the two wave halves).
-//   * K rows are fed to the matrix core in a permuted order (bits 2 and 3 of the row
-//     index swapped) so that the score accumulator, converted to bf16, is directly the
-//     B operand of O^T += V^T P^T for 16 consecutive keys — no shuffle of P.
-//   * The output accumulator is O^T (head_dim x 32 queries), again lane-local per query.
-//   * The online softmax runs in float32 in base 2 (scale folded into one FMA before
-//     exp2); only tiles that reach past the prefix apply the ancestor bitmask.
-//   * Long prefixes are split across workgroups; each split writes a partial (O, LSE)
-//     in float32 and a merge kernel combines them.
+//     grouped-query layer reuses each K/V byte G*T times inside one workgroup.
+//   * Workgroups of NW wavefronts stage 64-key tiles of K (row-major) and V (transposed)
+//     in LDS; with NW >= 2 the LDS is double-buffered and the next tile's global loads
+//     are in flight (in registers) while the current tile is computed.  Each wavefront
+//     owns QT tiles of 32 query rows.
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the
+//     accumulator column is the query, so each lane holds 16 keys of ONE query and the
+//     softmax statistics, the output rescale and the final normalisation are lane-local
+//     (only the tile max crosses the two wave halves).
+//   * K rows enter the matrix core with bits 2 and 3 of the row index swapped, so that the
+//     score accumulator, converted to bf16, is directly the B operand of O^T += V^T P^T
+//     for 16 consecutive keys — no data movement for P.
+//   * Online softmax in float32, base 2, scale folded into one FMA before v_exp_f32.  The
+//     reference max is only raised when a tile's max exceeds it by more than 8 (a factor
+//     256 in probability), so the O rescale runs on a handful of tiles, not on every one.
+//   * Only tiles reaching past the prefix apply the ancestor bitmask.
+//   * 1-D grid with an XCD-aware order: the row blocks of one (sequence, head, split) are
+//     dispatched to the same XCD and so share its L2 for the K/V tiles.
+//   * Long prefixes are split across workgroups; each split writes its normalised partial
+//     O in fp16 (pre-divided by max(1, |O|max) of the row, the divisor kept in float32) and
+//     its LSE; a merge kernel combines the splits.
 // float32 path: a plain VALU kernel (one wavefront per (sequence, head, node)).
 #include "ev_internal.h"
 
+#include <algorithm>
 #include <math.h>
 
 namespace ev {
@@ -33,6 +40,8 @@ namespace ev {
 constexpr int kKT = 64;                 // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the reference max is raised
+constexpr int kXcds = 8;
 
 struct AttnArgs {
   const void *q;
@@ -43,12 +52,15 @@ struct AttnArgs {
   const uint64_t *anc;
   int B, T, Hq, G;
   float scale_log2;        // sm_scale * log2(e)
+  int row_blocks;
   int tiles_per_split;
   int n_splits;
+  int n_work;              // B * Hkv * row_blocks * n_splits
   void *out;               // final O (n_splits == 1)
   float *lse;              // final LSE (n_splits == 1)
-  float *part_o;           // [n_splits][B][T][Hq][D] (n_splits > 1)
+  _Float16 *part_o;        // [n_splits][B][T][Hq][D], scaled by 1 / part_scale
   float *part_lse;         // [n_splits][B][T][Hq]
+  float *part_scale;       // [n_splits][B][T][Hq]
   int32_t *dev_status;
 };
 
@@ -61,25 +73,291 @@ __device__ inline bool visible(int slot, int L, uint64_t anc) {
 // MFMA row index -> key within a 32-key subtile: swap bits 2 and 3.
 __device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-template <int D, int QT, int NW>
+// S^T = K Q^T of one 64-key tile as two 32-key subtiles; kfrag(st, ks) returns the K
+// fragment (A operand) of subtile st, head-dim step ks for this lane.
+template <int QT, int KS, typename KFrag>
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[QT][2], const bf16x8 (&qf)[QT][KS],
+                                            KFrag kfrag) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+#pragma unroll
+    for (int t = 0; t < QT; ++t) s[t][st] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kf = kfrag(st, ks);
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+        s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][ks], s[t][st], 0, 0, 0);
+    }
+  }
+}
+
+// Online softmax (base 2, float32) of one tile's scores, lane-local per query.  Register r
+// of subtile st holds key st*32 + 16*(r>>3) + 8*hh + 4*((r>>2)&1) + (r&3) (the K rows were
+// fed with bits 2 and 3 swapped), so each 8-register group is 8 consecutive keys: the bf16
+// probabilities are directly the B operand of O^T += V^T P^T.
+template <int QT, int DT>
+__device__ __forceinline__ void tile_softmax(f32x16 (&s)[QT][2], bf16x8 (&pf)[QT][2][2],
+                                             f32x16 (&o)[QT][DT], float (&mref)[QT],
+                                             float (&l)[QT], const uint64_t (&anc_q)[QT],
+                                             int key0, int L, int hh, float scale_log2) {
+  const bool need_mask = key0 + kKT > L;
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    float sv[32];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[st * 16 + r] = s[t][st][r];
+    if (need_mask) {
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        const int st = x >> 4, r = x & 15;
+        const int key = st * 32 + (r >> 3) * 16 + hh * 8 + ((r >> 2) & 1) * 4 + (r & 3);
+        if (!visible(key0 + key, L, anc_q[t])) sv[x] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) mx = fmaxf(mx, sv[x]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    // Raise the reference max only when this tile could overflow the headroom.
+    if (__any(mx > mref[t] + kRescaleSlack)) {
+      const float mnew = fmaxf(mref[t], mx);
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[t] - mnew);
+      l[t] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+      mref[t] = mnew;
+    }
+    const float nb = mref[t] == -INFINITY ? 0.f : -mref[t];
+    float sum = 0.f;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      sv[x] = __builtin_amdgcn_exp2f(fmaf(sv[x], scale_log2, nb));
+      sum += sv[x];
+    }
+    l[t] += sum;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const float *v8 = sv + st * 16 + kk * 8;
+        pf[t][st][kk] = bf16x8{(__bf16)v8[0], (__bf16)v8[1], (__bf16)v8[2], (__bf16)v8[3],
+                               (__bf16)v8[4], (__bf16)v8[5], (__bf16)v8[6], (__bf16)v8[7]};
+      }
+  }
+}
+
+// O^T += V^T P^T over one tile; vfrag(st, kk, dt) returns the V^T fragment (A operand): head
+// dims dt*32 + qn, keys st*32 + kk*16 + 8*hh + 0..7.
+template <int QT, int DT, typename VFrag>
+__device__ __forceinline__ void tile_pv(f32x16 (&o)[QT][DT], const bf16x8 (&pf)[QT][2][2],
+                                        VFrag vfrag) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 vf = vfrag(st, kk, dt);
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+          o[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][st][kk], o[t][dt], 0, 0, 0);
+      }
+}
+
+// Normalise this lane's query rows and write them: the final O (bf16) and LSE when the
+// sequence is not split, else an fp16 partial O pre-divided by max(1, |O|max of the row)
+// (the divisor kept in float32 so the partial cannot overflow) plus the partial LSE.
+template <int D, int QT>
+__device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[QT][D / 32],
+                                           const float (&mref)[QT], const float (&l)[QT],
+                                           int row0, int b, int g, int split, int qn, int hh) {
+  constexpr int DT = D / 32;
+  const int rows = a.T * a.G;
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int r = row0 + t * 32 + qn;
+    const float ltot = l[t] + __shfl_xor(l[t], 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float lse = ltot > 0.f ? (mref[t] + __log2f(ltot)) * kLn2 : -INFINITY;
+    const bool ok = r < rows;
+    const int node = ok ? r / a.G : 0;
+    const int head = g * a.G + (ok ? r % a.G : 0);
+    const int64_t orow = ((int64_t)b * a.T + node) * a.Hq + head;
+    if (a.n_splits == 1) {
+      if (!ok) continue;
+      __bf16 *dst = (__bf16 *)a.out + orow * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16 &ov = o[t][dt];
+          *(bf16x4 *)(dst + dt * 32 + 8 * j + 4 * hh) =
+              bf16x4{(__bf16)(ov[4 * j] * inv), (__bf16)(ov[4 * j + 1] * inv),
+                     (__bf16)(ov[4 * j + 2] * inv), (__bf16)(ov[4 * j + 3] * inv)};
+        }
+      if (hh == 0) a.lse[orow] = lse;
+    } else {
+      float amax = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[t][dt][i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+      const float scale = fmaxf(1.f, amax);
+      const float k = inv / scale;
+      if (!ok) continue;
+      const int64_t prow = (int64_t)split * a.B * a.T * a.Hq + orow;
+      _Float16 *dst = a.part_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16 &ov = o[t][dt];
+          *(f16x4 *)(dst + dt * 32 + 8 * j + 4 * hh) =
+              f16x4{(_Float16)(ov[4 * j] * k), (_Float16)(ov[4 * j + 1] * k),
+                    (_Float16)(ov[4 * j + 2] * k), (_Float16)(ov[4 * j + 3] * k)};
+        }
+      if (hh == 0) {
+        a.part_lse[prow] = lse;
+        a.part_scale[prow] = scale;
+      }
+    }
+  }
+}
+
+// Block ids of one split's paged tiles, cached in LDS by the workgroup.
+constexpr int kTableCache = 1024;
+
+// Global -> register staging of one 64-key tile; registers -> LDS after the compute.
+// Thread `tid` always owns the same (key, 8-dim chunk) positions of a tile, so a full
+// contiguous tile is one uniform base pointer plus fixed per-thread offsets; a paged tile
+// reads its block ids from the LDS cache.  Only the last tile of a sequence is partial.
+// V is transposed on its way to LDS in items of KPI keys x 8 dims (one item per thread
+// for 256- and 512-thread workgroups).
+template <int D, int NT, bool PAGED>
+struct TileStage {
+  static constexpr int DC = D / 8;                     // 16-byte chunks per key row
+  static constexpr int KCHUNKS = kKT * DC;             // K chunks per tile
+  static constexpr int KPI = NT >= 512 ? 2 : 4;        // keys per V item
+  static constexpr int VITEMS = (kKT / KPI) * DC;      // V items per tile
+  static constexpr int KPT = (KCHUNKS + NT - 1) / NT;
+  static constexpr int VPT = (VITEMS + NT - 1) / NT;
+  static constexpr int KSTEP = NT / DC;                // key stride between a thread's K chunks
+  static constexpr int KP = D + 8;                     // LDS pitch of the K tile (elements)
+  static constexpr int VP = kKT + 8;                   // LDS pitch of the V^T tile (elements)
+  static_assert(NT % DC == 0 && NT % (kKT / KPI) == 0, "thread count must tile the stage");
+  u32x4 kr[KPT];
+  u32x4 vr[VPT][KPI];
+
+  // Element offset of logical slot `slot` (PAGED: -1 for a bad block id).
+  __device__ static inline int64_t slot_off(const KvAddr &kv, int64_t seq_base, const int *stbl,
+                                            int blk0, int g, int slot) {
+    if (!PAGED) return seq_base + (int64_t)slot * D;
+    const int blk = stbl[(slot >> kv.block_shift) - blk0];
+    if (blk < 0) return -1;
+    return ((((int64_t)blk * kv.hkv + g) << kv.block_shift) | (slot & ((1 << kv.block_shift) - 1))) * D;
+  }
+
+  __device__ inline void load(const AttnArgs &a, const __bf16 *K, const __bf16 *V, int64_t seq_base,
+                              const int *stbl, int blk0, int g, int key0, int nkeys) {
+    const int tid = threadIdx.x;
+    const bool full = key0 + kKT <= nkeys;
+    const int dc = tid % DC;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int key = tid / DC + i * KSTEP;
+      u32x4 val = {};
+      if (key < kKT && (full || key0 + key < nkeys)) {
+        const int64_t off = slot_off(a.kv, seq_base, stbl, blk0, g, key0 + key);
+        if (off >= 0) val = *(const u32x4 *)(K + off + dc * 8);
+      }
+      kr[i] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      const int kq = c % (kKT / KPI), vdc = c / (kKT / KPI);
+#pragma unroll
+      for (int r = 0; r < KPI; ++r) {
+        u32x4 val = {};
+        const int key = KPI * kq + r;
+        if (c < VITEMS && (full || key0 + key < nkeys)) {
+          const int64_t off = slot_off(a.kv, seq_base, stbl, blk0, g, key0 + key);
+          if (off >= 0) val = *(const u32x4 *)(V + off + vdc * 8);
+        }
+        vr[i][r] = val;
+      }
+    }
+  }
+
+  __device__ inline void store(__bf16 *sK, __bf16 *sV) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int key = tid / DC + i * KSTEP;
+      if (key < kKT) *(u32x4 *)(sK + key * KP + (tid % DC) * 8) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      if (c >= VITEMS) continue;
+      const int kq = c % (kKT / KPI), vdc = c / (kKT / KPI);
+      // dim e of the item's keys: the low (even e) or high (odd e) half of word e / 2
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        if (KPI == 4) {
+          const u32x4 &r0 = vr[i][0], &r1 = vr[i][1], &r2 = vr[i][KPI - 2], &r3 = vr[i][KPI - 1];
+          u32x2 lo = {__builtin_amdgcn_perm(r1[wd], r0[wd], 0x05040100u),
+                      __builtin_amdgcn_perm(r3[wd], r2[wd], 0x05040100u)};
+          u32x2 hi = {__builtin_amdgcn_perm(r1[wd], r0[wd], 0x07060302u),
+                      __builtin_amdgcn_perm(r3[wd], r2[wd], 0x07060302u)};
+          *(u32x2 *)(sV + (vdc * 8 + 2 * wd) * VP + KPI * kq) = lo;
+          *(u32x2 *)(sV + (vdc * 8 + 2 * wd + 1) * VP + KPI * kq) = hi;
+        } else {
+          const u32x4 &r0 = vr[i][0], &r1 = vr[i][1];
+          *(uint32_t *)(sV + (vdc * 8 + 2 * wd) * VP + KPI * kq) =
+              __builtin_amdgcn_perm(r1[wd], r0[wd], 0x05040100u);
+          *(uint32_t *)(sV + (vdc * 8 + 2 * wd + 1) * VP + KPI * kq) =
+              __builtin_amdgcn_perm(r1[wd], r0[wd], 0x07060302u);
+        }
+      }
+    }
+  }
+};
+
+template <int D, int QT, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  using Stage = TileStage<D, NT, PAGED>;
   constexpr int KS = D / 16;            // k-steps of the score product
   constexpr int DT = D / 32;            // 32-row tiles of O^T
-  constexpr int KP = D + 8;             // LDS pitch of the K tile (elements)
-  constexpr int VP = kKT + 8;           // LDS pitch of the V^T tile (elements)
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[kKT * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[D * VP];
+  constexpr int KP = Stage::KP;
+  constexpr int VP = Stage::VP;
+  constexpr int KBUF = kKT * KP;        // elements per K buffer
+  constexpr int VBUF = D * VP;          // elements per V^T buffer
+  __shared__ __attribute__((aligned(16))) __bf16 sK[KBUF];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[VBUF];
+  __shared__ int stbl[PAGED ? kTableCache : 1];
+
+  // XCD-aware work order: consecutive work items (the row blocks of one split) land on the
+  // same XCD, whose L2 then serves their shared K/V tiles.
+  const int per_xcd = gridDim.x / kXcds;
+  const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (w >= a.n_work) return;
+  const int rb = w % a.row_blocks;
+  const int split = (w / a.row_blocks) % a.n_splits;
+  const int bg = w / (a.row_blocks * a.n_splits);
+  const int b = bg / a.kv.hkv;
+  const int g = bg % a.kv.hkv;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int qn = lane & 31;             // query column of this lane
   const int hh = lane >> 5;             // wave half
 
-  const int split = blockIdx.x;
-  const int rb = blockIdx.y;
-  const int b = blockIdx.z / a.kv.hkv;
-  const int g = blockIdx.z % a.kv.hkv;
   const int L = a.prefix_len[b];
   const int nkeys = L + a.T;
   if (L < 0 || !a.kv.fits(nkeys)) {
@@ -96,6 +374,25 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
   const __bf16 *Q = (const __bf16 *)a.q;
   const __bf16 *K = (const __bf16 *)a.k;
   const __bf16 *V = (const __bf16 *)a.v;
+  const int64_t seq_base = PAGED ? 0 : (int64_t)(b * a.kv.hkv + g) * a.kv.cap * D;
+
+  int blk0 = 0;
+  if (PAGED) {
+    blk0 = (t_begin * kKT) >> a.kv.block_shift;
+    const int nblk = ((min(t_end * kKT, nkeys) - 1) >> a.kv.block_shift) - blk0 + 1;
+    bool bad = false;
+    for (int i = threadIdx.x; i < nblk; i += NT) {
+      const int blk = a.kv.table[(int64_t)b * a.kv.max_blocks + blk0 + i];
+      const bool ok = blk >= 0 && blk < a.kv.n_blocks;
+      bad |= !ok;
+      stbl[i] = ok ? blk : -1;
+    }
+    if (__any(bad) && lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    __syncthreads();
+  }
+
+  Stage s0;
+  s0.load(a, K, V, seq_base, stbl, blk0, g, t_begin * kKT, nkeys);
 
   // Q^T fragments (B operand): lane holds query row qn, 8 head-dim elements per k-step.
   bf16x8 qf[QT][KS];
@@ -116,173 +413,251 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
   }
 
   f32x16 o[QT][DT];
-  float m[QT], l[QT];
+  float mref[QT], l[QT];                // reference max (log2 units) and lane-partial sum
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    m[t] = -INFINITY;
+    mref[t] = -INFINITY;
     l[t] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x16{};
   }
 
+  auto kfrag = [&](int st, int ks) {
+    return *(const bf16x8 *)(sK + (st * 32 + swap23(qn)) * KP + 8 * hh + 16 * ks);
+  };
+  auto vfrag = [&](int st, int kk, int dt) {
+    return *(const bf16x8 *)(sV + (dt * 32 + qn) * VP + st * 32 + kk * 16 + 8 * hh);
+  };
+  s0.store(sK, sV);
+  __syncthreads();
   for (int tile = t_begin; tile < t_end; ++tile) {
-    const int key0 = tile * kKT;
-    __syncthreads();
-    // ---- stage K tile (row-major) ----
-    for (int c = threadIdx.x; c < kKT * (D / 8); c += NT) {
-      int key = c / (D / 8), dc = c % (D / 8);
-      int slot = key0 + key;
-      bf16x8 val = {};
-      if (slot < nkeys) {
-        int64_t off = a.kv.slot_offset(b, g, slot);
-        if (off >= 0) val = *(const bf16x8 *)(K + off + dc * 8);
-        else report(a.dev_status, EV_DERR_BOUNDS);
-      }
-      *(bf16x8 *)(sK + key * KP + dc * 8) = val;
-    }
-    // ---- stage V tile transposed: 4 keys x 8 dims per item ----
-    for (int c = threadIdx.x; c < (kKT / 4) * (D / 8); c += NT) {
-      int kq = c % (kKT / 4), dc = c / (kKT / 4);
-      bf16x8 rows4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int slot = key0 + 4 * kq + r;
-        bf16x8 val = {};
-        if (slot < nkeys) {
-          int64_t off = a.kv.slot_offset(b, g, slot);
-          if (off >= 0) val = *(const bf16x8 *)(V + off + dc * 8);
-        }
-        rows4[r] = val;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 col = {rows4[0][e], rows4[1][e], rows4[2][e], rows4[3][e]};
-        *(bf16x4 *)(sV + (dc * 8 + e) * VP + 4 * kq) = col;
-      }
-    }
-    __syncthreads();
-
-    const bool need_mask = key0 + kKT > L;
-    // ---- S^T = K Q^T for two 32-key subtiles ----
-    f32x16 s[QT][2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int t = 0; t < QT; ++t) s[t][st] = f32x16{};
-      const __bf16 *krow = sK + (st * 32 + swap23(qn)) * KP + 8 * hh;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 kf = *(const bf16x8 *)(krow + 16 * ks);
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-          s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][ks], s[t][st], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax (base 2), lane-local per query ----
+    f32x16 sc[QT][2];
     bf16x8 pf[QT][2][2];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      if (need_mask) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int j = r >> 2, i = r & 3;
-            int key = st * 32 + (j >> 1) * 16 + hh * 8 + (j & 1) * 4 + i;
-            if (!visible(key0 + key, L, anc_q[t])) s[t][st][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][st][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[t], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f((m[t] - m_use) * a.scale_log2);
-      const float nb = -m_use * a.scale_log2;
-      float sum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = exp2f(fmaf(s[t][st][r], a.scale_log2, nb));
-          s[t][st][r] = p;
-          sum += p;
-        }
-      l[t] = l[t] * alpha + sum;
-      m[t] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[t][st][kk][e] = (__bf16)s[t][st][kk * 8 + e];
-    }
-
-    // ---- O^T += V^T P^T, 16 keys per step ----
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          bf16x8 vf = *(const bf16x8 *)(sV + (dt * 32 + qn) * VP + st * 32 + kk * 16 + 8 * hh);
-#pragma unroll
-          for (int t = 0; t < QT; ++t)
-            o[t][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][st][kk], o[t][dt], 0, 0, 0);
-        }
-      }
-  }
-
-  // ---- epilogue: normalise and write (final or partial) ----
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    int r = row0 + t * 32 + qn;
-    float ltot = l[t] + __shfl_xor(l[t], 32);
-    if (r >= rows) continue;
-    int node = r / a.G;
-    int head = g * a.G + r % a.G;
-    int64_t orow = ((int64_t)b * a.T + node) * a.Hq + head;
-    float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    float lse = ltot > 0.f ? (m[t] * a.scale_log2 + log2f(ltot)) * kLn2 : -INFINITY;
-    if (a.n_splits == 1) {
-      __bf16 *dst = (__bf16 *)a.out + orow * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[t][dt][4 * j + i] * inv);
-          *(bf16x4 *)(dst + dt * 32 + 8 * j + 4 * hh) = w;
-        }
-      if (hh == 0) a.lse[orow] = lse;
-    } else {
-      int64_t prow = (int64_t)split * a.B * a.T * a.Hq + orow;
-      float *dst = a.part_o + prow * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = o[t][dt][4 * j + i] * inv;
-          *(f32x4 *)(dst + dt * 32 + 8 * j + 4 * hh) = w;
-        }
-      if (hh == 0) a.part_lse[prow] = lse;
+    tile_scores(sc, qf, kfrag);
+    tile_softmax(sc, pf, o, mref, l, anc_q, tile * kKT, L, hh, a.scale_log2);
+    tile_pv(o, pf, vfrag);
+    if (tile + 1 < t_end) {
+      s0.load(a, K, V, seq_base, stbl, blk0, g, (tile + 1) * kKT, nkeys);
+      __syncthreads();
+      s0.store(sK, sV);
+      __syncthreads();
     }
   }
+
+  write_rows<D, QT>(a, o, mref, l, row0, b, g, split, qn, hh);
+}
+
+// ---------------------------------------------------------------------------------------
+// Direct-to-LDS pipeline (head_dim 128, 2-8 wavefronts of 32 query rows).
+//
+// K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no staging registers): lane
+// l of a wave-instruction fills LDS chunk base + l, so the LDS layout is chosen on the global
+// side.  Both matrices are stored row-major by key with the 16-byte chunks of each row
+// XOR-swizzled (K: chunk ^ (key & 15); V: chunk ^ 2*(key & 7)), which makes the K fragment
+// reads and the transposing V reads (ds_read_b64_tr_b16: within 16 lanes, lane 4a+c receives
+// element c of the 4-element rows addressed by lanes a, a+4, a+8, a+12) bank-conflict-free.
+// Four LDS stages hold tiles j (P V), j+1 (Q K^T, overlapping the softmax of j) and j+2, j+3
+// (in flight).  Completion is tracked with explicit vmcnt waits, one barrier per tile.
+constexpr int kStages = 4;
+
+__device__ __forceinline__ void dma16(const __bf16 *g, __bf16 *l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int NW, bool PAGED>
+__global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int QT = 1;
+  constexpr int KS = D / 16, DT = D / 32, DCH = D / 8;
+  constexpr int MAT = kKT * D;                   // bf16 elements of one K or V tile
+  constexpr int IPW = kKT * DCH / 64 / NW;       // DMA instructions per wave per matrix
+  constexpr int PER = 2 * IPW;                   // per wave per tile
+  static_assert(IPW >= 1 && 2 * PER <= 63, "vmcnt range");
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT];
+  __shared__ int stbl[PAGED ? kTableCache : 1];
+
+  const int per_xcd = gridDim.x / kXcds;
+  const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (w >= a.n_work) return;
+  const int rb = w % a.row_blocks;
+  const int split = (w / a.row_blocks) % a.n_splits;
+  const int bg = w / (a.row_blocks * a.n_splits);
+  const int b = bg / a.kv.hkv;
+  const int g = bg % a.kv.hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int qn = lane & 31;
+  const int hh = lane >> 5;
+
+  const int L = a.prefix_len[b];
+  const int nkeys = L + a.T;
+  if (L < 0 || !a.kv.fits(nkeys)) {
+    if (threadIdx.x == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    return;
+  }
+  const int ntiles = (nkeys + kKT - 1) / kKT;
+  const int t_begin = split * a.tiles_per_split;
+  const int t_end = min(t_begin + a.tiles_per_split, ntiles);
+  if (t_begin >= t_end) return;
+
+  const int rows = a.T * a.G;
+  const int row0 = (rb * NW + wave) * 32;
+  const __bf16 *Q = (const __bf16 *)a.q;
+  const __bf16 *K = (const __bf16 *)a.k;
+  const __bf16 *V = (const __bf16 *)a.v;
+  const int64_t seq_base = PAGED ? 0 : (int64_t)(b * a.kv.hkv + g) * a.kv.cap * D;
+
+  int blk0 = 0;
+  if (PAGED) {
+    blk0 = (t_begin * kKT) >> a.kv.block_shift;
+    const int nblk = ((min(t_end * kKT, nkeys) - 1) >> a.kv.block_shift) - blk0 + 1;
+    bool bad = false;
+    for (int i = threadIdx.x; i < nblk; i += NT) {
+      const int blk = a.kv.table[(int64_t)b * a.kv.max_blocks + blk0 + i];
+      const bool ok = blk >= 0 && blk < a.kv.n_blocks;
+      bad |= !ok;
+      stbl[i] = ok ? blk : -1;
+    }
+    if (__any(bad) && lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    __syncthreads();
+  }
+
+  // Q^T fragments first, so the DMA traffic that follows is the only vmem in the loop.
+  bf16x8 qf[QT][KS];
+  uint64_t anc_q[QT];
+  {
+    const int r = row0 + qn;
+    const bool ok = r < rows;
+    const int node = ok ? r / a.G : 0;
+    const int head = g * a.G + (ok ? r % a.G : 0);
+    const __bf16 *src = Q + (((int64_t)b * a.T + node) * a.Hq + head) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 z = {};
+      qf[0][ks] = ok ? *(const bf16x8 *)(src + 16 * ks) : z;
+    }
+    anc_q[0] = ok ? a.anc[(int64_t)b * a.T + node] : 0ull;
+  }
+
+  // Element offset of a slot's row; slots past the sequence read the tile's first slot
+  // (finite data that the mask removes) and bad block ids read row 0 (already reported).
+  auto row_off = [&](int slot) -> int64_t {
+    if (!PAGED) return seq_base + (int64_t)slot * D;
+    const int blk = stbl[(slot >> a.kv.block_shift) - blk0];
+    if (blk < 0) return 0;
+    return ((((int64_t)blk * a.kv.hkv + g) << a.kv.block_shift) |
+            (slot & ((1 << a.kv.block_shift) - 1))) * D;
+  };
+  auto stage = [&](int tile) { return lds + ((tile - t_begin) % kStages) * 2 * MAT; };
+  auto issue = [&](int tile) {
+    const int key0 = tile * kKT;
+    __bf16 *kd = stage(tile);
+    __bf16 *vd = kd + MAT;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int blk = wave * IPW + i;            // 1 KB block of the tile (4 key rows)
+      const int q = blk * 64 + lane;
+      const int key = q / DCH, pc = q % DCH;
+      int slot = key0 + key;
+      if (slot >= nkeys) slot = key0;
+      const int64_t off = row_off(slot);
+      dma16(K + off + ((pc ^ (key & 15)) << 3), kd + blk * 512);
+      dma16(V + off + ((pc ^ ((key & 7) << 1)) << 3), vd + blk * 512);
+    }
+  };
+  // Wait until `tile` has landed, given how many newer tiles this wave has issued.
+  auto landed = [&](int newer) {
+    if (newer >= 2) wait_vm<2 * PER>();
+    else if (newer == 1) wait_vm<PER>();
+    else wait_vm<0>();
+  };
+
+  // Lane-constant LDS offsets (elements) of the fragments.
+  const int krow = swap23(qn);                   // key row within a subtile
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = krow * D + ((((2 * ks) | hh) ^ (krow & 15)) << 3);
+  const int r16 = lane & 15, grp = lane >> 4;
+  int voff[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) {
+      const int rr = (r16 >> 2) + 4 * hr;        // key within the 8-key group
+      const int d = dt * 32 + 16 * (grp & 1) + 4 * (r16 & 3);
+      voff[dt][hr] = (8 * hh + rr) * D + ((((d >> 3) ^ (rr << 1))) << 3) + (d & 7);
+    }
+
+  f32x16 o[QT][DT];
+  float mref[QT] = {-INFINITY}, l[QT] = {0.f};
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[0][dt] = f32x16{};
+
+  auto scores_of = [&](f32x16 (&s)[QT][2], int tile) {
+    const __bf16 *kb = stage(tile);
+    tile_scores(s, qf, [&](int st, int ks) {
+      return *(const bf16x8 *)(kb + st * 32 * D + koff[ks]);
+    });
+  };
+  auto softmax_pv = [&](f32x16 (&s)[QT][2], int tile) {
+    bf16x8 pf[QT][2][2];
+    tile_softmax(s, pf, o, mref, l, anc_q, tile * kKT, L, hh, a.scale_log2);
+    const __bf16 *vb = stage(tile) + MAT;
+    tile_pv(o, pf, [&](int st, int kk, int dt) {
+      const __bf16 *base = vb + (st * 32 + kk * 16) * D;
+      typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + voff[dt][0]));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + voff[dt][1]));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    });
+  };
+
+  // prologue: three tiles in flight, scores of the first
+  issue(t_begin);
+  if (t_begin + 1 < t_end) issue(t_begin + 1);
+  if (t_begin + 2 < t_end) issue(t_begin + 2);
+  landed(min(t_end - 1, t_begin + 2) - t_begin);
+  wg_barrier();
+  f32x16 sa[QT][2], sb[QT][2];
+  scores_of(sa, t_begin);
+  for (int j = t_begin; j < t_end; j += 2) {
+    if (j + 1 < t_end) {
+      landed(min(t_end - 1, j + 2) - (j + 1));
+      wg_barrier();                              // tile j+1 visible; stage of j-1 free
+      if (j + 3 < t_end) issue(j + 3);
+      scores_of(sb, j + 1);
+    }
+    softmax_pv(sa, j);
+    if (j + 1 >= t_end) break;
+    if (j + 2 < t_end) {
+      landed(min(t_end - 1, j + 3) - (j + 2));
+      wg_barrier();
+      if (j + 4 < t_end) issue(j + 4);
+      scores_of(sa, j + 2);
+    }
+    softmax_pv(sb, j + 1);
+  }
+  write_rows<D, QT>(a, o, mref, l, row0, b, g, split, qn, hh);
 }
 
 // Combine split partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
-// One row (sequence, node, head) per 32 lanes, 4 head-dim elements per lane.
-template <int D, typename OutT>
+// 32 lanes per row (sequence, node, head), D/32 head-dim elements per lane; the partials
+// are read in batches of 8 splits (all loads of a batch in flight together) and combined
+// with a running maximum.
+template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int E = D / 32;
+  constexpr int BATCH = 8;
+  typedef _Float16 hE __attribute__((ext_vector_type(E)));
   const int64_t nrows = (int64_t)a.B * a.T * a.Hq;
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int c = threadIdx.x & 31;
@@ -292,24 +667,41 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (L < 0 || !a.kv.fits(L + a.T)) return;
   const int ntiles = (L + a.T + kKT - 1) / kKT;
   const int nvalid = min(a.n_splits, (ntiles + a.tiles_per_split - 1) / a.tiles_per_split);
-  const int64_t stride = nrows;
-  float mx = -INFINITY;
-  for (int s = 0; s < nvalid; ++s) mx = fmaxf(mx, a.part_lse[s * stride + row]);
-  float acc[D / 32] = {};
-  float wsum = 0.f;
-  for (int s = 0; s < nvalid; ++s) {
-    float ls = a.part_lse[s * stride + row];
-    float w = ls == -INFINITY ? 0.f : exp2f((ls - mx) * kLog2e);
-    wsum += w;
-    if (w == 0.f) continue;
-    const float *src = a.part_o + (s * stride + row) * D;
+  float mx = -INFINITY, wsum = 0.f;
+  float acc[E] = {};
+  for (int s0 = 0; s0 < nvalid; s0 += BATCH) {
+    float ls[BATCH], sc[BATCH];
+    hE x[BATCH];
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k) acc[k] += w * src[c + 32 * k];
+    for (int u = 0; u < BATCH; ++u) {
+      const int s = s0 + u;
+      const bool ok = s < nvalid;
+      ls[u] = ok ? a.part_lse[s * nrows + row] : -INFINITY;
+      sc[u] = ok ? a.part_scale[s * nrows + row] : 0.f;
+      x[u] = ok ? *(const hE *)(a.part_o + (s * nrows + row) * D + c * E) : hE{};
+    }
+    float bm = mx;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) bm = fmaxf(bm, ls[u]);
+    if (bm == -INFINITY) continue;
+    const float r = mx == -INFINITY ? 0.f : exp2f((mx - bm) * kLog2e);
+    wsum *= r;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= r;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const float w = ls[u] == -INFINITY ? 0.f : exp2f((ls[u] - bm) * kLog2e);
+      wsum += w;
+      const float ws = w * sc[u];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += ws * (float)x[u][e];
+    }
+    mx = bm;
   }
-  float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  OutT *dst = (OutT *)a.out + row * D;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  __bf16 *dst = (__bf16 *)a.out + row * D + c * E;
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) dst[c + 32 * k] = (OutT)(acc[k] * inv);
+  for (int e = 0; e < E; ++e) dst[e] = (__bf16)(acc[e] * inv);
   if (c == 0) a.lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
@@ -376,19 +768,21 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
   }
   float inv = l > 0.f ? 1.f / l : 0.f;
   float lse = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-  if (a.n_splits == 1) {
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) ((float *)a.out)[orow * D + lane + 64 * k] = o[k] * inv;
-    if (lane == 0) a.lse[orow] = lse;
-  }
+  for (int k = 0; k < D / 64; ++k) ((float *)a.out)[orow * D + lane + 64 * k] = o[k] * inv;
+  if (lane == 0) a.lse[orow] = lse;
 }
 
 // ---------------------------------------------------------------------------------------
 // Launch policy.
+constexpr int kMaxSplits = 32;
+constexpr int kCUs = 256;
+
 struct Plan {
   int qt, nw;            // query tiles per wave, waves per workgroup
   int row_blocks;
   int tiles_per_split, n_splits;
+  int n_work, grid;
 };
 
 static int max_slots(const KvAddr &kv) {
@@ -396,58 +790,90 @@ static int max_slots(const KvAddr &kv) {
   return kv.max_blocks << kv.block_shift;
 }
 
+// Splits are sized so that one round of workgroups fills the chip (GQA: one 8-wave
+// workgroup per CU; MHA: four 1-wave workgroups per CU), at most kMaxSplits of them, and
+// a paged split's block ids must fit the LDS cache.
 static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq) {
   Plan p{};
   if (dtype == EV_F32) {
-    p.qt = p.nw = p.row_blocks = 1;
+    p.qt = p.nw = p.row_blocks = p.n_splits = 1;
     p.tiles_per_split = 1 << 30;
-    p.n_splits = 1;
     return p;
   }
   const int G = Hq / kv.hkv;
   const int rows = T * G;
-  p.qt = rows >= 256 ? 2 : 1;
+#ifndef EV_ATTN_WIDE_WAVES
+#define EV_ATTN_WIDE_WAVES 0
+#endif
+  // Many rows per KV head: 8 waves of 32 rows (two waves per SIMD, no accumulator
+  // spill to AGPRs); EV_ATTN_WIDE_WAVES selects 4 waves of 64 rows instead.
+  p.qt = (EV_ATTN_WIDE_WAVES && rows >= 256) ? 2 : 1;
   const int wave_rows = 32 * p.qt;
   const int waves_needed = (rows + wave_rows - 1) / wave_rows;
-  p.nw = waves_needed >= 4 ? 4 : waves_needed;
+  p.nw = waves_needed >= 8 && p.qt == 1 ? 8
+       : waves_needed >= 4 ? 4 : (waves_needed >= 2 ? 2 : 1);
   p.row_blocks = (waves_needed + p.nw - 1) / p.nw;
   const int max_tiles = (max_slots(kv) + kKT - 1) / kKT;
   const int units = B * kv.hkv * p.row_blocks;
-  // Aim for about two workgroups per compute unit, at least 4 tiles per split.
-  const int target_wgs = 512;
-  int splits = (target_wgs + units - 1) / units;
+  const int slots = p.nw >= 4 ? kCUs : (p.nw == 2 ? 2 * kCUs : 4 * kCUs);
+  int splits = std::max(1, slots / units);
+  splits = std::min(splits, std::min(kMaxSplits, max_tiles));
   int tps = (max_tiles + splits - 1) / splits;
-  if (tps < 4) tps = 4;
+  if (kv.paged) {
+    // a split's block ids must fit the LDS cache
+    const int blocks_per_tile = std::max(1, kKT >> kv.block_shift);
+    tps = std::min(tps, (kTableCache - 1) / blocks_per_tile);
+  }
   p.tiles_per_split = tps;
   p.n_splits = (max_tiles + tps - 1) / tps;
-  if (p.n_splits < 1) p.n_splits = 1;
+  p.n_work = units * p.n_splits;
+  p.grid = (p.n_work + kXcds - 1) / kXcds * kXcds;
   return p;
+}
+
+static size_t part_rows(const Plan &p, int B, int T, int Hq) {
+  return (size_t)p.n_splits * B * T * Hq;
 }
 
 static size_t workspace_bytes(const Plan &p, int B, int T, int Hq, int D) {
   if (p.n_splits <= 1) return 0;
-  size_t rows = (size_t)p.n_splits * B * T * Hq;
-  return align_up(rows * D * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+  size_t rows = part_rows(p, B, T, Hq);
+  return align_up(rows * D * sizeof(_Float16), 256) + 2 * align_up(rows * sizeof(float), 256);
+}
+
+template <int D, bool PAGED>
+static void launch_main(const Plan &p, const AttnArgs &a, hipStream_t stream) {
+  dim3 grid(p.grid);
+  if (D == 128 && p.qt == 1 && p.nw >= 2) {
+    if (p.nw == 8)
+      hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED>), grid, dim3(512), 0, stream, a);
+    else if (p.nw == 4)
+      hipLaunchKernelGGL((tree_attn_dma_kernel<4, PAGED>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED>), grid, dim3(128), 0, stream, a);
+  } else if (p.qt == 2) {
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 2, 4, PAGED>), grid, dim3(256), 0, stream, a);
+  } else if (p.nw == 8) {
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 8, PAGED>), grid, dim3(512), 0, stream, a);
+  } else if (p.nw == 4) {
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 4, PAGED>), grid, dim3(256), 0, stream, a);
+  } else if (p.nw == 2) {
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 2, PAGED>), grid, dim3(128), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 1, PAGED>), grid, dim3(64), 0, stream, a);
+  }
 }
 
 template <int D>
 static void launch_bf16(const Plan &p, const AttnArgs &a, hipStream_t stream) {
-  dim3 grid(p.n_splits, p.row_blocks, a.B * a.kv.hkv);
-  if (p.qt == 2) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 2, 4>), grid, dim3(256), 0, stream, a);
-  } else if (p.nw == 4) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 4>), grid, dim3(256), 0, stream, a);
-  } else if (p.nw == 2) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 2>), grid, dim3(128), 0, stream, a);
-  } else if (p.nw == 3) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 3>), grid, dim3(192), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 1>), grid, dim3(64), 0, stream, a);
-  }
+  if (a.kv.paged)
+    launch_main<D, true>(p, a, stream);
+  else
+    launch_main<D, false>(p, a, stream);
   if (p.n_splits > 1) {
     int64_t nrows = (int64_t)a.B * a.T * a.Hq;
-    hipLaunchKernelGGL((attn_merge_kernel<D, __bf16>), dim3((unsigned)((nrows + 7) / 8)),
-                       dim3(256), 0, stream, a);
+    dim3 mgrid((unsigned)((nrows + 7) / 8));
+    hipLaunchKernelGGL((attn_merge_kernel<D>), mgrid, dim3(256), 0, stream, a);
   }
 }
 
@@ -473,6 +899,7 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return EV_ERR_ARG;
   if (B == 0) return EV_OK;
   if (!q || !prefix_len || !anc_mask || !out || !lse) return EV_ERR_NULL;
+  if ((int64_t)B * kv->n_kv_heads > (1 << 24)) return EV_ERR_SHAPE;
   ev::Plan p = ev::make_plan(addr, kv->dtype, B, T, Hq);
   size_t need = ev::workspace_bytes(p, B, T, Hq, kv->head_dim);
   if (ws_bytes < need || (need && !ws)) return EV_ERR_WORKSPACE;
@@ -489,15 +916,20 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   a.Hq = Hq;
   a.G = Hq / kv->n_kv_heads;
   a.scale_log2 = sm_scale * ev::kLog2e;
+  a.row_blocks = p.row_blocks;
   a.tiles_per_split = p.tiles_per_split;
   a.n_splits = p.n_splits;
+  a.n_work = p.n_work;
   a.out = out;
   a.lse = lse;
   a.dev_status = dev_status;
   if (need) {
-    size_t rows = (size_t)p.n_splits * B * T * Hq;
-    a.part_o = (float *)ws;
-    a.part_lse = (float *)((char *)ws + ev::align_up(rows * kv->head_dim * sizeof(float), 256));
+    size_t rows = ev::part_rows(p, B, T, Hq);
+    char *base = (char *)ws;
+    size_t o_bytes = ev::align_up(rows * kv->head_dim * sizeof(_Float16), 256);
+    a.part_o = (_Float16 *)base;
+    a.part_lse = (float *)(base + o_bytes);
+    a.part_scale = (float *)(base + o_bytes + ev::align_up(rows * sizeof(float), 256));
   }
   if (kv->dtype == EV_F32) {
     dim3 grid(T, Hq, B);
