@@ -223,7 +223,7 @@ def main():
     kv_tmp = ev.KvCache(dev0.k, dev0.v, dev0.block_table)
     ws_attn = torch.empty(max(1, ev.ev_tree_attention_workspace(kv_tmp, cfg.B, cfg.T, cfg.Hq)),
                           dtype=torch.uint8, device="cuda")
-    ws_acc = torch.empty(max(1, ev.ev_accept_workspace(cfg.B, cfg.T, cfg.V)), dtype=torch.uint8,
+    ws_acc = torch.zeros(max(1, ev.ev_accept_workspace(cfg.B, cfg.T, cfg.V)), dtype=torch.uint8,
                          device="cuda")
     sets = [BufferSet(inp, dev0 if i == 0 else to_device(inp), ws_attn, ws_acc) for i in range(n_sets)]
 

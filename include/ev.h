@@ -111,7 +111,11 @@ ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const int32_t *
                             float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes,
                             int32_t *dev_status, hipStream_t stream);
 
-/* Bytes of workspace the acceptance calls need. */
+/* Bytes of workspace the acceptance calls need (B * T <= 65535, V <= 262144).
+ * The acceptance workspace holds arrival counters: zero-fill it (for example with
+ * hipMemset) before its first use.  Every call that launches leaves the counters at zero
+ * again, whatever B, T and V were, so one zeroed workspace of the largest size serves
+ * calls of every smaller shape.  Calls that overlap in time must not share a workspace. */
 size_t ev_accept_workspace(int32_t B, int32_t T, int32_t V);
 
 /* ev_accept_greedy — greedy longest-matching-path acceptance ([EX] "Core idea";

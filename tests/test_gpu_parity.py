@@ -231,6 +231,29 @@ def test_rejection_many_seeds_bonus_paths():
         assert np.array_equal(a, b)
 
 
+def test_accept_workspace_reuse_across_shapes():
+    """One zeroed workspace serves consecutive calls of different shapes, and every call
+    leaves the arrival counters at zero (the workspace contract of the acceptance calls)."""
+    big = scaled(C3, B=4, V=20000, L=8)
+    small = scaled(C3, B=2, V=3000, L=8)
+    ws = torch.zeros(ev.ev_accept_workspace(4, big.T, big.V), dtype=torch.uint8, device="cuda")
+    ws[ev.ev_accept_workspace(1, 1, 1):].fill_(0x5A)        # garbage beyond the counters
+    counters = 2 * 65536 * 4
+    for cfg, rej in ((big, True), (small, True), (big, False), (small, False), (big, True)):
+        inp = generate(cfg, tokens="raw", with_kv=False)
+        dev = to_device(inp)
+        if rej:
+            got = ev.ev_accept_rejection(dev.logits, dev.tokens, dev.parent, dev.tau, dev.uniforms,
+                                         ws=ws, check=True)
+            exp = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
+        else:
+            got = ev.ev_accept_greedy(dev.logits, dev.tokens, dev.parent, ws=ws, check=True)
+            exp = oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
+        for a, b in zip(got, exp[:3]):
+            assert np.array_equal(a.cpu().numpy(), b)
+        assert int(ws[:counters].count_nonzero()) == 0
+
+
 def test_accept_reports_bad_token():
     inp = generate(scaled(C3, V=500, L=8), with_kv=False)
     dev = to_device(inp)
@@ -370,7 +393,7 @@ def test_graph_replays_match_eager():
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws_a = torch.empty(max(1, ev.ev_tree_attention_workspace(kv, B, T, cfg.Hq)), dtype=torch.uint8,
                        device="cuda")
-    ws_r = torch.empty(ev.ev_accept_workspace(B, T, cfg.V), dtype=torch.uint8, device="cuda")
+    ws_r = torch.zeros(ev.ev_accept_workspace(B, T, cfg.V), dtype=torch.uint8, device="cuda")
 
     def step():
         ev.ev_tree_mask_build(dev.parent, anc, depth, status)

@@ -242,7 +242,7 @@ def ev_accept_greedy(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.T
     dev = logits.device
     accept_len, path, out_tokens = _accept_outputs(B, T, dev, accept_len, path, out_tokens)
     if ws is None:
-        ws = torch.empty(max(1, ev_accept_workspace(B, T, V)), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(1, ev_accept_workspace(B, T, V)), dtype=torch.uint8, device=dev)
     status = _status_word(dev, dev_status)
     code = lib().ev_accept_greedy(_ptr(logits), _ptr(tokens), _ptr(parent), B, T, V, _ptr(accept_len),
                                   _ptr(path), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
@@ -263,7 +263,7 @@ def ev_accept_rejection(logits: torch.Tensor, tokens: torch.Tensor, parent: torc
     dev = logits.device
     accept_len, path, out_tokens = _accept_outputs(B, T, dev, accept_len, path, out_tokens)
     if ws is None:
-        ws = torch.empty(max(1, ev_accept_workspace(B, T, V)), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(1, ev_accept_workspace(B, T, V)), dtype=torch.uint8, device=dev)
     status = _status_word(dev, dev_status)
     code = lib().ev_accept_rejection(_ptr(logits), _ptr(tokens), _ptr(parent), B, T, V,
                                      float(temperature), _ptr(uniforms), _ptr(accept_len), _ptr(path),

@@ -8,14 +8,21 @@
 // u * Z < p_a(x); a rejected token leaves the residual (Z -= p_a(x)); when every child
 // fails, the emitted token is an inverse-CDF draw from the residual.
 //
-// Two launches per call:
-//   1. stats: one wavefront per (row, 1024-logit chunk) streams the float32 logits once.
-//      greedy    -> (max, lowest argmax) per chunk
-//      rejection -> float64 (M_c = max s, S_c = sum exp(s - M_c)) per chunk, s = logit/tau
-//   2. walk: one wavefront per sequence; lane i holds node i (T <= 64).  Children of the
-//      current node come from a ballot over parent[]; per-node statistics are reduced
-//      from the chunk table; the bonus draw locates its chunk from the chunk masses and
-//      then scans only that chunk in float64.
+// The walk is sequential, but the outcome at a node depends only on that node's logit
+// row, its children's draft tokens and their uniforms — not on how the walk got there.  So
+// everything happens in ONE launch over (row = node, 1024-logit chunk) wavefronts:
+//   * each wavefront streams its chunk of float32 logits once and stores the chunk's
+//     statistics — greedy: (max, lowest argmax); rejection: float64 (M_c = max s,
+//     S_c = sum exp(s - M_c)), s = logit/tau;
+//   * the workgroup that completes a row's last chunk (a device-scope counter per row)
+//     reduces the row and settles that node's outcome: its argmax / accepted child,
+//     residual mass, rejected children and their probabilities;
+//   * the workgroup that completes a sequence's last row (a counter per sequence) follows
+//     accepted children from the root and draws the bonus token at the last node (greedy:
+//     its argmax; rejection: the residual inverse CDF, located through the chunk masses,
+//     then one 1024-logit chunk scanned in float64).
+// The counters live in the caller's workspace, which must be zero-filled before its first
+// use; every call leaves them at zero again.
 #include "ev_internal.h"
 
 #include <limits.h>
@@ -24,18 +31,46 @@
 namespace ev {
 
 constexpr int kChunk = 1024;       // logits per wavefront chunk (16 per lane)
-constexpr int kChunksPerWG = 4;
+constexpr int kChunksPerWG = 4;    // one chunk per wavefront
 
-struct GreedyStat {
+struct GreedyStat {                      // stored as one 64-bit word: value bits, index
   float val;
   int idx;
 };
+__device__ inline uint64_t pack(GreedyStat g) {
+  return (uint64_t)__float_as_uint(g.val) | ((uint64_t)(uint32_t)g.idx << 32);
+}
+__device__ inline GreedyStat unpack(uint64_t w) {
+  return GreedyStat{__uint_as_float((uint32_t)w), (int)(uint32_t)(w >> 32)};
+}
 struct RejStat {
   double M;
   double S;
 };
 
 __host__ __device__ inline int n_chunks_of(int V) { return (V + kChunk - 1) / kChunk; }
+
+// exp(x) for x <= 0 in float64 by the table-driven method of P. T. P. Tang (ACM TOMS 15(2),
+// 1989): x = (64 m + j) ln2/64 + r with |r| <= ln2/128, exp(x) = 2^m 2^(j/64) exp(r), the
+// last factor by its Taylor polynomial to r^6 (truncation below 3e-20).  tab[j] = 2^(j/64).
+__device__ inline double exp_nonpos(double x, const double *tab) {
+  constexpr double kInvLn2x64 = 92.33248261689366;            // 64 / ln 2
+  constexpr double kLn2d64Hi = 0.010830424696249145;          // ln2/64 rounded to double
+  constexpr double kLn2d64Lo = 3.623510646634843e-19;         // ln2/64 - kLn2d64Hi
+  if (!(x > -745.2)) return 0.0;
+  const double kf = rint(x * kInvLn2x64);
+  const int k = (int)kf;
+  double r = fma(-kf, kLn2d64Hi, x);
+  r = fma(-kf, kLn2d64Lo, r);
+  double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+  p = fma(r, p, 1.0 / 24.0);
+  p = fma(r, p, 1.0 / 6.0);
+  p = fma(r, p, 0.5);
+  p = fma(r, p, 1.0);
+  p *= r;                                                     // exp(r) - 1
+  const double t = tab[k & 63];
+  return ldexp(fma(t, p, t), k >> 6);
+}
 
 // Lane's 16 logits of chunk `base`: element (k*64 + lane)*4 + e, k < 4, e < 4 (coalesced).
 __device__ inline void load_chunk(const float *row, int V, int base, bool vec_ok, float v[16],
@@ -91,61 +126,91 @@ __device__ inline double wave_max(double x) {
   return x;
 }
 
-template <bool REJ>
-__global__ __launch_bounds__(256) void accept_stats_kernel(const float *__restrict__ logits, int V,
-                                                           int n_chunks, double inv_tau,
-                                                           void *__restrict__ stats) {
-  const int lane = threadIdx.x & 63;
-  const int chunk = blockIdx.x * kChunksPerWG + (threadIdx.x >> 6);
-  const int64_t row = blockIdx.y;
-  if (chunk >= n_chunks) return;
-  const float *src = logits + row * V;
-  const bool vec_ok = (V & 3) == 0;
-  float v[16];
-  int idx[16];
-  load_chunk(src, V, chunk * kChunk, vec_ok, v, idx);
-  float best = -INFINITY;
-  int bi = INT_MAX;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) better(best, bi, v[e], idx[e]);
-  wave_argmax(best, bi);
-  if (!REJ) {
-    if (lane == 0) ((GreedyStat *)stats)[row * n_chunks + chunk] = GreedyStat{best, bi};
-    return;
-  }
-  const double M = (double)best * inv_tau;
-  double s = 0.0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (idx[e] != INT_MAX) s += exp((double)v[e] * inv_tau - M);
-  s = wave_sum(s);
-  if (lane == 0) ((RejStat *)stats)[row * n_chunks + chunk] = RejStat{M, s};
+// 2^(j/64), j < 64, into LDS (one entry per thread of the first wavefront).
+__device__ inline void fill_exp_table(double *tab) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
 }
 
-struct WalkArgs {
+// Data handed from one workgroup to another within a launch (chunk statistics, node
+// outcomes) moves through agent-scope atomic stores and loads, which are coherent across
+// the XCDs' separate L2 caches without the whole-L2 write-back and invalidate that an
+// agent-scope fence costs.  A writer waits for its stores to complete before it bumps an
+// arrival counter; a reader loads only after its own increment has returned the final
+// count, so every store it reads has already reached the coherence point.
+template <class X>
+__device__ inline void publish(X *p, X v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class X>
+__device__ inline X observe(const X *p) {
+  return __hip_atomic_load(const_cast<X *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Returns true in the one workgroup whose arrival completes `expected` arrivals; that
+// workgroup also resets the counter for the next call.  Call with the whole workgroup.
+__device__ inline bool last_arrival(int32_t *cnt, int expected, int *s_flag) {
+  stores_complete();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == expected - 1;
+    if (last) publish(cnt, 0);
+    *s_flag = last;
+  }
+  __syncthreads();
+  asm volatile("" ::: "memory");
+  return *s_flag;
+}
+
+struct NodeOut {                         // one per (sequence, node), written by its row's
+  double Z;                              // last workgroup: residual mass left at the node
+  double M, S;                           // row statistics (rejection)
+  double prej;                           // p of this node's token at its parent, if rejected
+  uint64_t rej;                          // children whose tokens were rejected at this node
+  int32_t next;                          // accepted child, -1 if none
+  int32_t y;                             // greedy: the row's lowest argmax
+};
+
+struct AcceptArgs {
   const float *logits;
   const int32_t *tokens;
   const int32_t *parent;
-  int T, V, n_chunks;
+  int B, T, V, n_chunks;
   double inv_tau;
   const double *uniforms;
-  const void *stats;
+  void *stats;                           // [B*T][n_chunks] chunk statistics
+  int32_t *row_cnt;                      // [B*T]
+  int32_t *seq_cnt;                      // [B]
+  NodeOut *nodes;                        // [B*T]
   int32_t *accept_len;
   int32_t *path;
   int32_t *out_tokens;
   int32_t *dev_status;
 };
 
-// p_a(y) under the float64 contract.
-__device__ inline double prob(const float *row, int y, double inv_tau, double M, double S) {
-  return exp((double)row[y] * inv_tau - M) / S;
+// Row statistics (max s, sum exp(s - max)) of a node from its chunk statistics, held in
+// registers (lane holds chunks lane, lane + 64, ... up to kChunkRegs of them).
+constexpr int kChunkRegs = 4;            // V <= 256 Ki logits
+__device__ inline void row_stats_regs(const RejStat (&cs)[kChunkRegs], const double *tab,
+                                      double &M, double &S) {
+  M = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) M = fmax(M, cs[r].M);
+  M = wave_max(M);
+  S = 0.0;
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r)
+    if (cs[r].S > 0.0) S += cs[r].S * exp_nonpos(cs[r].M - M, tab);
+  S = wave_sum(S);
 }
 
-// Inverse-CDF draw from the residual of node row `row` (rejected tokens: lanes set in
-// `rej` hold them in `tok`, with their probabilities in `prej`).
-__device__ int residual_draw(const WalkArgs &a, const float *row, const RejStat *st, double M,
-                             double S, uint64_t rej, int tok, double prej, double t) {
-  const int lane = threadIdx.x;
+// Inverse-CDF draw from the residual of a node (rejected tokens: lanes set in `rej` hold
+// them in `tok` and their probabilities in `prej`).  One wavefront.
+__device__ int residual_draw(const AcceptArgs &a, const float *row, const RejStat *st, double M,
+                             double S, uint64_t rej, int tok, double prej, double t,
+                             const double *tab) {
+  const int lane = threadIdx.x & 63;
   const int nc = a.n_chunks;
   const int cpl = (nc + 63) / 64;      // contiguous chunks per lane
   // chunk masses with the rejected tokens removed
@@ -153,7 +218,7 @@ __device__ int residual_draw(const WalkArgs &a, const float *row, const RejStat 
   double tot = 0.0;
   for (int r = 0; r < cpl; ++r) {
     int c = lane * cpl + r;
-    mass[r] = c < nc ? st[c].S * exp(st[c].M - M) / S : 0.0;
+    mass[r] = c < nc ? observe(&st[c].S) * exp_nonpos(observe(&st[c].M) - M, tab) / S : 0.0;
   }
   for (uint64_t rr = rej; rr; rr &= rr - 1) {
     int src = __ffsll((unsigned long long)rr) - 1;
@@ -200,10 +265,11 @@ __device__ int residual_draw(const WalkArgs &a, const float *row, const RejStat 
     const int y0 = cstar * kChunk + lane * 16;
     double pv[16];
     double lsum = 0.0;
+    const double inv_S = 1.0 / S;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       int y = y0 + e;
-      pv[e] = y < a.V ? prob(row, y, a.inv_tau, M, S) : 0.0;
+      pv[e] = y < a.V ? exp_nonpos((double)row[y] * a.inv_tau - M, tab) * inv_S : 0.0;
     }
     for (uint64_t rr = rej; rr; rr &= rr - 1) {
       int src = __ffsll((unsigned long long)rr) - 1;
@@ -239,80 +305,154 @@ __device__ int residual_draw(const WalkArgs &a, const float *row, const RejStat 
   }
 }
 
-template <bool REJ>
-__global__ __launch_bounds__(64) void accept_walk_kernel(WalkArgs a) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int T = a.T;
-  const bool live = lane < T;
-  const int par = live ? a.parent[(int64_t)b * T + lane] : -2;
-  const int tok = live ? a.tokens[(int64_t)b * T + lane] : -1;
-  bool ok = !live || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
-  if (__any(!ok)) {
+// Workspace: the counters sit at fixed offsets at its start, sized for the largest
+// launch (B * T <= 65535 rows, B <= 65535 sequences), so that a workspace left at zero by
+// one call is still zero where a call of any other shape looks for its counters.
+constexpr int kMaxRows = 65535;
+constexpr size_t kCounterBytes = 2 * align_up((kMaxRows + 1) * sizeof(int32_t), 256);
+
+struct WsLayout {
+  size_t row_cnt, seq_cnt, stats, nodes, total;
+};
+
+inline WsLayout ws_layout(int B, int T, int V) {
+  WsLayout w;
+  const size_t rows = (size_t)B * T;
+  w.row_cnt = 0;
+  w.seq_cnt = kCounterBytes / 2;
+  w.stats = kCounterBytes;
+  w.nodes = w.stats + align_up(rows * n_chunks_of(V) * sizeof(RejStat), 256);
+  w.total = w.nodes + align_up(rows * sizeof(NodeOut), 256);
+  return w;
+}
+
+// Node data of sequence b, lane i = node i; false when parent[] or a token is invalid.
+__device__ inline bool load_tree(const AcceptArgs &a, int b, int &par, int &tok) {
+  const int lane = threadIdx.x & 63;
+  const bool live = lane < a.T;
+  par = live ? a.parent[(int64_t)b * a.T + lane] : -2;
+  tok = live ? a.tokens[(int64_t)b * a.T + lane] : -1;
+  const bool pok = !live || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+  if (__any(!pok)) {
     if (lane == 0) report(a.dev_status, EV_DERR_PARENT);
-    return;
+    return false;
   }
   if (__any(live && lane > 0 && (tok < 0 || tok >= a.V))) {
     if (lane == 0) report(a.dev_status, EV_DERR_TOKEN);
-    return;
+    return false;
   }
-  const int nc = a.n_chunks;
-  int node = 0;
-  int k = 0;
-  int my_path = lane == 0 ? 0 : -1;    // lane m holds path[m]
-  int my_out = -1;                      // lane m holds out_tokens[m]
-  for (;;) {
-    const int64_t row_id = (int64_t)b * T + node;
-    const float *row = a.logits + row_id * a.V;
-    const uint64_t kids = __ballot(live && par == node);
-    int emitted;
-    int next = -1;
+  return true;
+}
+
+// Outcome of node n of sequence b (one wavefront): greedy argmax and matching child, or
+// the rejection tests of its children in ascending index.
+template <bool REJ>
+__device__ void settle_node(const AcceptArgs &a, int b, int n, const double *tab) {
+  const int lane = threadIdx.x & 63;
+  const int T = a.T, nc = a.n_chunks;
+  const int64_t row_id = (int64_t)b * T + n;
+  int par, tok;
+  NodeOut out{1.0, NAN, NAN, 0.0, 0, -1, 0};
+  if (load_tree(a, b, par, tok)) {
+    const bool live = lane < T;
+    const uint64_t kids = __ballot(live && par == n);
     if (!REJ) {
-      const GreedyStat *st = (const GreedyStat *)a.stats + row_id * nc;
+      const uint64_t *st = (const uint64_t *)a.stats + row_id * nc;
       float v = -INFINITY;
       int i = INT_MAX;
-      for (int c = lane; c < nc; c += 64) better(v, i, st[c].val, st[c].idx);
+      for (int c = lane; c < nc; c += 64) {
+        const GreedyStat g = unpack(observe(&st[c]));
+        better(v, i, g.val, g.idx);
+      }
       wave_argmax(v, i);
-      emitted = i;
-      uint64_t match = kids & __ballot(live && tok == i);
-      if (match) next = __ffsll((unsigned long long)match) - 1;
+      const uint64_t match = kids & __ballot(live && tok == i);
+      out.y = i;
+      out.next = match ? __ffsll((unsigned long long)match) - 1 : -1;
     } else {
       const RejStat *st = (const RejStat *)a.stats + row_id * nc;
-      double M = -INFINITY;
-      for (int c = lane; c < nc; c += 64) M = fmax(M, st[c].M);
-      M = wave_max(M);
-      double S = 0.0;
-      for (int c = lane; c < nc; c += 64) S += st[c].S * exp(st[c].M - M);
-      S = wave_sum(S);
-      double Z = 1.0;
+      RejStat cs[kChunkRegs];
+#pragma unroll
+      for (int r = 0; r < kChunkRegs; ++r) {
+        const int c = lane + 64 * r;
+        cs[r] = c < nc ? RejStat{observe(&st[c].M), observe(&st[c].S)} : RejStat{-INFINITY, 0.0};
+      }
+      const float lg = ((kids >> lane) & 1) ? a.logits[row_id * a.V + tok] : 0.f;
+      const double ul = live ? a.uniforms[(int64_t)b * T + lane] : 0.0;
+      double M, S;
+      row_stats_regs(cs, tab, M, S);
+      double Z = 1.0, myp = 0.0;
       uint64_t rej = 0;
-      double prej = 0.0;                // lane c: p of its token if rejected here
-      const double *u = a.uniforms + (int64_t)b * T;
+      int next = -1;
       for (uint64_t kk = kids; kk; kk &= kk - 1) {
-        int c = __ffsll((unsigned long long)kk) - 1;
-        int x = __shfl(tok, c);
+        const int c = __ffsll((unsigned long long)kk) - 1;
+        const int x = __shfl(tok, c);
         if (__ballot(((rej >> lane) & 1) && tok == x)) continue;   // already rejected here
-        double p = prob(row, x, a.inv_tau, M, S);
-        if (u[c] * Z < p) {
+        const double p = exp_nonpos((double)__shfl(lg, c) * a.inv_tau - M, tab) / S;
+        if (__shfl(ul, c) * Z < p) {
           next = c;
           break;
         }
         rej |= 1ull << c;
-        if (lane == c) prej = p;
+        if (lane == c) myp = p;
         Z -= p;
       }
-      if (next >= 0) {
-        emitted = __shfl(tok, next);
-      } else {
-        emitted = residual_draw(a, row, st, M, S, rej, tok, prej, u[0] * Z);
-      }
+      out.Z = Z;
+      out.M = M;
+      out.S = S;
+      out.rej = rej;
+      out.next = next;
+      if ((rej >> lane) & 1) publish(&a.nodes[(int64_t)b * T + lane].prej, myp);
     }
-    if (lane == k) my_out = emitted;
-    if (next < 0) break;
-    ++k;
-    if (lane == k) my_path = next;
-    node = next;
+  } else {
+    out.next = -2;                       // invalid tree: the sequence's outputs are skipped
   }
+  if (lane == 0) {
+    NodeOut *dst = a.nodes + row_id;
+    publish(&dst->Z, out.Z);
+    publish(&dst->M, out.M);
+    publish(&dst->S, out.S);
+    publish(&dst->rej, out.rej);
+    publish(&dst->next, out.next);
+    publish(&dst->y, out.y);
+  }
+}
+
+// Follow accepted children from the root of sequence b and draw the bonus token (one
+// wavefront); writes accept_len, path and out_tokens.
+template <bool REJ>
+__device__ void finish_sequence(const AcceptArgs &a, int b, const double *tab) {
+  const int lane = threadIdx.x & 63;
+  const int T = a.T;
+  const bool live = lane < T;
+  const NodeOut *nodes = a.nodes + (int64_t)b * T;
+  const int next_l = live ? observe(&nodes[lane].next) : -1;
+  if (__any(next_l == -2)) return;      // invalid tree, already reported
+  const int tok = live ? a.tokens[(int64_t)b * T + lane] : -1;
+  int node = 0, k = 0;
+  int my_path = lane == 0 ? 0 : -1;      // lane m holds path[m]
+  int my_out = -1;                       // lane m holds out_tokens[m]
+  for (;;) {
+    const int nxt = __shfl(next_l, node);
+    if (nxt < 0) break;
+    const int drafted = __shfl(tok, nxt);
+    if (lane == k) my_out = drafted;
+    ++k;
+    if (lane == k) my_path = nxt;
+    node = nxt;
+  }
+  int bonus;
+  if (!REJ) {
+    bonus = observe(&nodes[node].y);
+  } else {
+    const int64_t row_id = (int64_t)b * T + node;
+    const uint64_t rej = observe(&nodes[node].rej);
+    const double prej = ((rej >> lane) & 1) ? observe(&nodes[lane].prej) : 0.0;
+    const double u0 = a.uniforms[(int64_t)b * T];
+    bonus = residual_draw(a, a.logits + row_id * a.V, (const RejStat *)a.stats + row_id * a.n_chunks,
+                          observe(&nodes[node].M), observe(&nodes[node].S), rej, tok, prej,
+                          u0 * observe(&nodes[node].Z), tab);
+  }
+  if (lane == k) my_out = bonus;
   if (live) {
     a.path[(int64_t)b * T + lane] = my_path;
     a.out_tokens[(int64_t)b * T + lane] = my_out;
@@ -320,22 +460,89 @@ __global__ __launch_bounds__(64) void accept_walk_kernel(WalkArgs a) {
   if (lane == 0) a.accept_len[b] = k;
 }
 
+template <bool REJ>
+__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+  __shared__ double tab[64];
+  __shared__ int s_last;
+  if (REJ) fill_exp_table(tab);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x * kChunksPerWG + wave;
+  const int64_t row = blockIdx.y;
+  const int nc = a.n_chunks;
+
+  // ---- this wavefront's chunk statistics ----
+  if (chunk < nc) {
+    float v[16];
+    int idx[16];
+    load_chunk(a.logits + row * a.V, a.V, chunk * kChunk, (a.V & 3) == 0, v, idx);
+    float best = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) better(best, bi, v[e], idx[e]);
+    wave_argmax(best, bi);
+    if (!REJ) {
+      if (lane == 0) publish((uint64_t *)a.stats + row * nc + chunk, pack(GreedyStat{best, bi}));
+    } else {
+      const double M = (double)best * a.inv_tau;
+      double sum = 0.0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (idx[e] != INT_MAX) sum += exp_nonpos((double)v[e] * a.inv_tau - M, tab);
+      sum = wave_sum(sum);
+      if (lane == 0) {
+        RejStat *dst = (RejStat *)a.stats + row * nc + chunk;
+        publish(&dst->M, M);
+        publish(&dst->S, sum);
+      }
+    }
+  }
+  if (!last_arrival(&a.row_cnt[row], gridDim.x, &s_last)) return;
+
+  // ---- last workgroup of this row: settle the node ----
+  const int b = (int)(row / a.T), n = (int)(row % a.T);
+  if (wave == 0) settle_node<REJ>(a, b, n, tab);
+  if (!last_arrival(&a.seq_cnt[b], a.T, &s_last)) return;
+
+  // ---- last row of this sequence: walk and bonus ----
+  if (wave == 0) finish_sequence<REJ>(a, b, tab);
+}
+
 static ev_status check_common(const float *logits, const int32_t *tokens, const int32_t *parent,
                               int32_t B, int32_t T, int32_t V, int32_t *accept_len,
                               int32_t *path, int32_t *out_tokens, void *ws, size_t ws_bytes) {
-  if (B < 0 || T < 1 || T > kMaxNodes || V < 1 || V > 64 * 4 * kChunk) return EV_ERR_SHAPE;
+  if (B < 0 || T < 1 || T > kMaxNodes || V < 1 || V > 64 * kChunkRegs * kChunk) return EV_ERR_SHAPE;
+  if ((int64_t)B * T > kMaxRows) return EV_ERR_SHAPE;
   if (B == 0) return EV_OK;
   if (!logits || !tokens || !parent || !accept_len || !path || !out_tokens) return EV_ERR_NULL;
-  size_t need = (size_t)B * T * n_chunks_of(V) * sizeof(RejStat);
-  if (ws_bytes < need || !ws) return EV_ERR_WORKSPACE;
+  if (ws_bytes < ws_layout(B, T, V).total || !ws) return EV_ERR_WORKSPACE;
   return EV_OK;
+}
+
+static ev_status launch_accept(bool rej, const float *logits, const int32_t *tokens,
+                               const int32_t *parent, int32_t B, int32_t T, int32_t V,
+                               double inv_tau, const double *uniforms, int32_t *accept_len,
+                               int32_t *path, int32_t *out_tokens, void *ws,
+                               int32_t *dev_status, hipStream_t stream) {
+  const WsLayout w = ws_layout(B, T, V);
+  char *base = (char *)ws;
+  AcceptArgs a{logits, tokens, parent, B, T, V, n_chunks_of(V), inv_tau, uniforms,
+               base + w.stats, (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
+               (NodeOut *)(base + w.nodes), accept_len, path, out_tokens, dev_status};
+  dim3 grid((a.n_chunks + kChunksPerWG - 1) / kChunksPerWG, B * T);
+  if (rej)
+    hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(accept_kernel<false>, grid, dim3(256), 0, stream, a);
+  return launch_status();
 }
 
 }  // namespace ev
 
 EV_API size_t ev_accept_workspace(int32_t B, int32_t T, int32_t V) {
   if (B < 1 || T < 1 || V < 1) return 0;
-  return (size_t)B * T * ev::n_chunks_of(V) * sizeof(ev::RejStat);
+  return ev::ws_layout(B, T, V).total;
 }
 
 EV_API ev_status ev_accept_greedy(const float *logits, const int32_t *tokens, const int32_t *parent,
@@ -345,14 +552,8 @@ EV_API ev_status ev_accept_greedy(const float *logits, const int32_t *tokens, co
   ev_status st = ev::check_common(logits, tokens, parent, B, T, V, accept_len, path, out_tokens,
                                   ws, ws_bytes);
   if (st != EV_OK || B == 0) return st;
-  const int nc = ev::n_chunks_of(V);
-  dim3 grid((nc + ev::kChunksPerWG - 1) / ev::kChunksPerWG, B * T);
-  hipLaunchKernelGGL(ev::accept_stats_kernel<false>, grid, dim3(256), 0, stream, logits, V, nc,
-                     0.0, ws);
-  ev::WalkArgs a{logits, tokens, parent, T, V, nc, 0.0, nullptr, ws,
-                 accept_len, path, out_tokens, dev_status};
-  hipLaunchKernelGGL(ev::accept_walk_kernel<false>, dim3(B), dim3(64), 0, stream, a);
-  return ev::launch_status();
+  return ev::launch_accept(false, logits, tokens, parent, B, T, V, 0.0, nullptr, accept_len, path,
+                           out_tokens, ws, dev_status, stream);
 }
 
 EV_API ev_status ev_accept_rejection(const float *logits, const int32_t *tokens,
@@ -366,13 +567,6 @@ EV_API ev_status ev_accept_rejection(const float *logits, const int32_t *tokens,
                                   ws, ws_bytes);
   if (st != EV_OK || B == 0) return st;
   if (!uniforms) return EV_ERR_NULL;
-  const int nc = ev::n_chunks_of(V);
-  const double inv_tau = 1.0 / (double)temperature;
-  dim3 grid((nc + ev::kChunksPerWG - 1) / ev::kChunksPerWG, B * T);
-  hipLaunchKernelGGL(ev::accept_stats_kernel<true>, grid, dim3(256), 0, stream, logits, V, nc,
-                     inv_tau, ws);
-  ev::WalkArgs a{logits, tokens, parent, T, V, nc, inv_tau, uniforms, ws,
-                 accept_len, path, out_tokens, dev_status};
-  hipLaunchKernelGGL(ev::accept_walk_kernel<true>, dim3(B), dim3(64), 0, stream, a);
-  return ev::launch_status();
+  return ev::launch_accept(true, logits, tokens, parent, B, T, V, 1.0 / (double)temperature,
+                           uniforms, accept_len, path, out_tokens, ws, dev_status, stream);
 }

@@ -88,6 +88,6 @@ inline ev_status launch_status() {
   return hipGetLastError() == hipSuccess ? EV_OK : EV_ERR_LAUNCH;
 }
 
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace ev

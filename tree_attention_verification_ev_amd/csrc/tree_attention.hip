@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <math.h>
+#include <type_traits>
 
 namespace ev {
 
@@ -92,36 +93,41 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[QT][2], const bf16x8 (&q
   }
 }
 
-// Online softmax (base 2, float32) of one tile's scores, lane-local per query.  Register r
-// of subtile st holds key st*32 + 16*(r>>3) + 8*hh + 4*((r>>2)&1) + (r&3) (the K rows were
-// fed with bits 2 and 3 swapped), so each 8-register group is 8 consecutive keys: the bf16
-// probabilities are directly the B operand of O^T += V^T P^T.
-template <int QT, int DT>
-__device__ __forceinline__ void tile_softmax(f32x16 (&s)[QT][2], bf16x8 (&pf)[QT][2][2],
-                                             f32x16 (&o)[QT][DT], float (&mref)[QT],
-                                             float (&l)[QT], const uint64_t (&anc_q)[QT],
-                                             int key0, int L, int hh, float scale_log2) {
-  const bool need_mask = key0 + kKT > L;
+// Ancestor mask of a tile reaching past the prefix, applied in place to the scores: a key
+// that is neither a prefix slot nor an ancestor-or-self tree slot of the lane's query gets
+// -inf.  Register r of subtile st holds key st*32 + 16*(r>>3) + 8*hh + 4*((r>>2)&1) + (r&3)
+// (the K rows were fed with bits 2 and 3 of the row index swapped).
+template <int QT>
+__device__ __forceinline__ void tile_mask(f32x16 (&s)[QT][2], const uint64_t (&anc_q)[QT],
+                                          int key0, int L, int hh) {
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    float sv[32];
+  for (int t = 0; t < QT; ++t)
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[st * 16 + r] = s[t][st][r];
-    if (need_mask) {
-#pragma unroll
-      for (int x = 0; x < 32; ++x) {
-        const int st = x >> 4, r = x & 15;
+      for (int r = 0; r < 16; ++r) {
         const int key = st * 32 + (r >> 3) * 16 + hh * 8 + ((r >> 2) & 1) * 4 + (r & 3);
-        if (!visible(key0 + key, L, anc_q[t])) sv[x] = -INFINITY;
+        if (!visible(key0 + key, L, anc_q[t])) s[t][st][r] = -INFINITY;
       }
-    }
+}
+
+// Online softmax (base 2, float32) of one tile's (masked) scores, lane-local per query,
+// in two parts so that independent matrix-core work can be scheduled between them:
+// tile_rescale takes the tile max and raises the reference max (rescaling O and the sum)
+// only when the tile could overflow 2^8 of headroom; tile_exp forms the probabilities,
+// their sum and the bf16 P fragments.  Each 8-register group of a subtile is 8 consecutive
+// keys, so the fragments are directly the B operand of O^T += V^T P^T.
+template <int QT, int DT>
+__device__ __forceinline__ void tile_rescale(const f32x16 (&s)[QT][2], f32x16 (&o)[QT][DT],
+                                             float (&mref)[QT], float (&l)[QT], float scale_log2) {
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < 32; ++x) mx = fmaxf(mx, sv[x]);
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][st][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-    // Raise the reference max only when this tile could overflow the headroom.
     if (__any(mx > mref[t] + kRescaleSlack)) {
       const float mnew = fmaxf(mref[t], mx);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[t] - mnew);
@@ -130,22 +136,31 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[QT][2], bf16x8 (&pf)[QT
       for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
       mref[t] = mnew;
     }
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ void tile_exp(const f32x16 (&s)[QT][2], bf16x8 (&pf)[QT][2][2],
+                                         const float (&mref)[QT], float (&l)[QT], float scale_log2) {
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
     const float nb = mref[t] == -INFINITY ? 0.f : -mref[t];
     float sum = 0.f;
 #pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      sv[x] = __builtin_amdgcn_exp2f(fmaf(sv[x], scale_log2, nb));
-      sum += sv[x];
+    for (int st = 0; st < 2; ++st) {
+      f32x16 p;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(s[t][st][r], scale_log2, nb));
+        sum += p[r];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pf[t][st][kk] = bf16x8{(__bf16)p[8 * kk + 0], (__bf16)p[8 * kk + 1], (__bf16)p[8 * kk + 2],
+                               (__bf16)p[8 * kk + 3], (__bf16)p[8 * kk + 4], (__bf16)p[8 * kk + 5],
+                               (__bf16)p[8 * kk + 6], (__bf16)p[8 * kk + 7]};
     }
     l[t] += sum;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const float *v8 = sv + st * 16 + kk * 8;
-        pf[t][st][kk] = bf16x8{(__bf16)v8[0], (__bf16)v8[1], (__bf16)v8[2], (__bf16)v8[3],
-                               (__bf16)v8[4], (__bf16)v8[5], (__bf16)v8[6], (__bf16)v8[7]};
-      }
   }
 }
 
@@ -434,7 +449,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
     f32x16 sc[QT][2];
     bf16x8 pf[QT][2][2];
     tile_scores(sc, qf, kfrag);
-    tile_softmax(sc, pf, o, mref, l, anc_q, tile * kKT, L, hh, a.scale_log2);
+    if (tile * kKT + kKT > L) tile_mask(sc, anc_q, tile * kKT, L, hh);
+    tile_rescale(sc, o, mref, l, a.scale_log2);
+    tile_exp(sc, pf, mref, l, a.scale_log2);
     tile_pv(o, pf, vfrag);
     if (tile + 1 < t_end) {
       s0.load(a, K, V, seq_base, stbl, blk0, g, (tile + 1) * kKT, nkeys);
@@ -548,8 +565,20 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     anc_q[0] = ok ? a.anc[(int64_t)b * a.T + node] : 0ull;
   }
 
-  // Element offset of a slot's row; slots past the sequence read the tile's first slot
-  // (finite data that the mask removes) and bad block ids read row 0 (already reported).
+  // Lane-constant parts of this wave's DMA: instruction i fills 1 KB block wave*IPW + i of
+  // a tile, i.e. key rows 4*(wave*IPW + i) .. +3; lane l takes row key_i, physical chunk
+  // l % 16, and so fetches logical chunk (l % 16) ^ swizzle(key_i).
+  int dkey[IPW], doffK[IPW], doffV[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int q = (wave * IPW + i) * 64 + lane;
+    const int key = q / DCH, pc = q % DCH;
+    dkey[i] = key;
+    doffK[i] = ((pc ^ swap23(key & 15)) << 3);
+    doffV[i] = ((pc ^ ((5 * (key & 3)) & 15)) << 3);
+  }
+  // Element offset of a slot's row (PAGED: from the LDS block-id cache; bad ids read row 0,
+  // already reported).
   auto row_off = [&](int slot) -> int64_t {
     if (!PAGED) return seq_base + (int64_t)slot * D;
     const int blk = stbl[(slot >> a.kv.block_shift) - blk0];
@@ -557,35 +586,32 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     return ((((int64_t)blk * a.kv.hkv + g) << a.kv.block_shift) |
             (slot & ((1 << a.kv.block_shift) - 1))) * D;
   };
-  auto stage = [&](int tile) { return lds + ((tile - t_begin) % kStages) * 2 * MAT; };
-  auto issue = [&](int tile) {
+  auto issue = [&](int tile, int stg) {
     const int key0 = tile * kKT;
-    __bf16 *kd = stage(tile);
-    __bf16 *vd = kd + MAT;
+    const bool full = key0 + kKT <= nkeys;
+    __bf16 *kd = lds + stg * 2 * MAT;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int blk = wave * IPW + i;            // 1 KB block of the tile (4 key rows)
-      const int q = blk * 64 + lane;
-      const int key = q / DCH, pc = q % DCH;
-      int slot = key0 + key;
-      if (slot >= nkeys) slot = key0;
+      int slot = key0 + dkey[i];
+      if (!full && slot >= nkeys) slot = key0;   // past the sequence: finite data, masked out
       const int64_t off = row_off(slot);
-      dma16(K + off + ((pc ^ (key & 15)) << 3), kd + blk * 512);
-      dma16(V + off + ((pc ^ ((key & 7) << 1)) << 3), vd + blk * 512);
+      const int blk = wave * IPW + i;
+      dma16(K + off + doffK[i], kd + blk * 512);
+      dma16(V + off + doffV[i], kd + MAT + blk * 512);
     }
   };
-  // Wait until `tile` has landed, given how many newer tiles this wave has issued.
+  // Wait until the tile `newer` tiles older than the newest issued one has landed.
   auto landed = [&](int newer) {
     if (newer >= 2) wait_vm<2 * PER>();
     else if (newer == 1) wait_vm<PER>();
     else wait_vm<0>();
   };
 
-  // Lane-constant LDS offsets (elements) of the fragments.
+  // Lane-constant LDS offsets (elements) of the fragments within a stage.
   const int krow = swap23(qn);                   // key row within a subtile
   int koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = krow * D + ((((2 * ks) | hh) ^ (krow & 15)) << 3);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = krow * D + ((((2 * ks) | hh) ^ (qn & 15)) << 3);
   const int r16 = lane & 15, grp = lane >> 4;
   int voff[DT][2];
 #pragma unroll
@@ -594,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     for (int hr = 0; hr < 2; ++hr) {
       const int rr = (r16 >> 2) + 4 * hr;        // key within the 8-key group
       const int d = dt * 32 + 16 * (grp & 1) + 4 * (r16 & 3);
-      voff[dt][hr] = (8 * hh + rr) * D + ((((d >> 3) ^ (rr << 1))) << 3) + (d & 7);
+      voff[dt][hr] = (8 * hh + rr) * D + (((d >> 3) ^ ((5 * (rr & 3)) & 15)) << 3) + (d & 7);
     }
 
   f32x16 o[QT][DT];
@@ -602,16 +628,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[0][dt] = f32x16{};
 
-  auto scores_of = [&](f32x16 (&s)[QT][2], int tile) {
-    const __bf16 *kb = stage(tile);
-    tile_scores(s, qf, [&](int st, int ks) {
+  // Stage index is a compile-time constant in every call below, so all LDS addresses are
+  // a lane-constant register plus an immediate offset.
+  auto scores_of = [&](f32x16 (&sc)[QT][2], auto stg) {
+    const __bf16 *kb = lds + decltype(stg)::value * 2 * MAT;
+    tile_scores(sc, qf, [&](int st, int ks) {
       return *(const bf16x8 *)(kb + st * 32 * D + koff[ks]);
     });
   };
-  auto softmax_pv = [&](f32x16 (&s)[QT][2], int tile) {
-    bf16x8 pf[QT][2][2];
-    tile_softmax(s, pf, o, mref, l, anc_q, tile * kKT, L, hh, a.scale_log2);
-    const __bf16 *vb = stage(tile) + MAT;
+  auto pv_of = [&](const bf16x8 (&pf)[QT][2][2], auto stg) {
+    const __bf16 *vb = lds + decltype(stg)::value * 2 * MAT + MAT;
     tile_pv(o, pf, [&](int st, int kk, int dt) {
       const __bf16 *base = vb + (st * 32 + kk * 16) * D;
       typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -620,31 +646,47 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
       return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     });
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+
+  // One pipeline step for tile j in stage STG: make tile j+1 visible, refill the stage of
+  // j-1 with tile j+3, and compute the scores of j+1 (into sn; the matrix cores run them
+  // while the wave continues) before the softmax and P V of j.  Returns false when j was
+  // the last tile.
+  auto step = [&](int j, f32x16 (&sc)[QT][2], f32x16 (&sn)[QT][2], auto stg) -> bool {
+    constexpr int STG = decltype(stg)::value;
+    using NEXT = std::integral_constant<int, (STG + 1) % kStages>;
+    using REFILL = std::integral_constant<int, (STG + 3) % kStages>;
+    const bool more = j + 1 < t_end;
+    if (more) {
+      landed(min(t_end - 1, j + 2) - (j + 1));
+      wg_barrier();                              // tile j+1 visible; stage of j-1 free
+      if (j + 3 < t_end) issue(j + 3, REFILL::value);
+      scores_of(sn, NEXT{});
+    }
+    if (j * kKT + kKT > L) tile_mask(sc, anc_q, j * kKT, L, hh);
+    tile_rescale(sc, o, mref, l, a.scale_log2);
+    bf16x8 pf[QT][2][2];
+    tile_exp(sc, pf, mref, l, a.scale_log2);
+    pv_of(pf, stg);
+    return more;
+  };
 
   // prologue: three tiles in flight, scores of the first
-  issue(t_begin);
-  if (t_begin + 1 < t_end) issue(t_begin + 1);
-  if (t_begin + 2 < t_end) issue(t_begin + 2);
+  issue(t_begin, 0);
+  if (t_begin + 1 < t_end) issue(t_begin + 1, 1);
+  if (t_begin + 2 < t_end) issue(t_begin + 2, 2);
   landed(min(t_end - 1, t_begin + 2) - t_begin);
   wg_barrier();
   f32x16 sa[QT][2], sb[QT][2];
-  scores_of(sa, t_begin);
-  for (int j = t_begin; j < t_end; j += 2) {
-    if (j + 1 < t_end) {
-      landed(min(t_end - 1, j + 2) - (j + 1));
-      wg_barrier();                              // tile j+1 visible; stage of j-1 free
-      if (j + 3 < t_end) issue(j + 3);
-      scores_of(sb, j + 1);
-    }
-    softmax_pv(sa, j);
-    if (j + 1 >= t_end) break;
-    if (j + 2 < t_end) {
-      landed(min(t_end - 1, j + 3) - (j + 2));
-      wg_barrier();
-      if (j + 4 < t_end) issue(j + 4);
-      scores_of(sa, j + 2);
-    }
-    softmax_pv(sb, j + 1);
+  scores_of(sa, S0{});
+  for (int j = t_begin;; j += 4) {
+    if (!step(j, sa, sb, S0{})) break;
+    if (!step(j + 1, sb, sa, S1{})) break;
+    if (!step(j + 2, sa, sb, S2{})) break;
+    if (!step(j + 3, sb, sa, S3{})) break;
   }
   write_rows<D, QT>(a, o, mref, l, row0, b, g, split, qn, hh);
 }
