@@ -129,25 +129,79 @@ def prime_gpu(ms: float = 20.0):
     return a
 
 
-def kernel_times(sets, graphs, reps):
-    """Average device time of each call, from HIP events on the launch stream."""
+def kernel_times(sets, reps):
+    """Average device time of one call of each part of the step, from HIP events on the
+    launch stream around a graph of back-to-back calls that cycles through the buffer
+    sets (so each call reads cache-cold inputs and graph-launch overhead is amortised)."""
     out = {}
+    n_calls = len(sets) * max(1, math.ceil(32 / len(sets)))
     for name in ("mask", "attention", "accept", "compact"):
+        calls = [getattr(sets[i % len(sets)], name) for i in range(n_calls)]
+        g = capture(lambda: [c() for c in calls])
+        g.replay()
+        torch.cuda.synchronize()
         keep = prime_gpu()
         pairs = []
-        for r in range(reps):
-            s = r % len(sets)
+        for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            graphs[s][name].replay()
+            g.replay()
             e1.record()
             pairs.append((e0, e1))
         torch.cuda.synchronize()
         del keep
-        ts = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        ts = [a.elapsed_time(b) * 1e3 / n_calls for a, b in pairs]
         out[name] = {"mean_us": statistics.fmean(ts), "median_us": statistics.median(ts),
-                     "p10_us": float(np.percentile(ts, 10)), "p90_us": float(np.percentile(ts, 90))}
+                     "p10_us": float(np.percentile(ts, 10)), "p90_us": float(np.percentile(ts, 90)),
+                     "calls_per_graph": n_calls}
     return out
+
+
+def _counter_values(csv_path, counter):
+    """Per-dispatch values of one counter in a rocprofv3 counter_collection.csv, by kernel."""
+    import csv
+    acc = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def write_traffic(fetch_csv, write_csv, command):
+    """HBM bytes per attention call (main + split merge kernels) from two rocprofv3 --pmc
+    runs of `bench.py --calibrate`, each counter scaled by what it reads for the 256 MiB
+    device copy of the same run."""
+    fetch, write = _counter_values(fetch_csv, "FETCH_SIZE"), _counter_values(write_csv, "WRITE_SIZE")
+    copy_kib = (256 << 20) / 1024
+
+    def pick(table, key):
+        hits = [(k, v) for k, v in table.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no kernel matching {key!r} in the counter file")
+        return max(hits, key=lambda kv: len(kv[1]))
+
+    # the calibration copy is the largest device copy of the run
+    cal_f = copy_kib / max(max(v) for k, v in fetch.items() if "copyBuffer" in k)
+    cal_w = copy_kib / max(max(v) for k, v in write.items() if "copyBuffer" in k)
+    kernels = {}
+    total = 0.0
+    for key in ("tree_attn_", "attn_merge_kernel"):
+        kf, vf = pick(fetch, key)
+        kw, vw = pick(write, key)
+        f_kib, nf, w_kib, nw = statistics.fmean(vf), len(vf), statistics.fmean(vw), len(vw)
+        b = f_kib * 1024 * cal_f + w_kib * 1024 * cal_w
+        kernels[kf] = {"fetch_kib": f_kib, "write_kib": w_kib, "dispatches": [nf, nw],
+                       "hbm_bytes": b}
+        total += b
+    with open(ATTN_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    rec = {"workload": "llama3_70b_layer", "hbm_bytes_per_launch": total,
+           "fetch_calibration": cal_f, "write_calibration": cal_w, "kernels": kernels,
+           "source_sha256": sha, "command": command}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def traffic_entry():
@@ -205,7 +259,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the attention traffic record from two rocprofv3 --pmc "
+                         "counter files (FETCH_SIZE, WRITE_SIZE) and exit (no GPU needed)")
+    ap.add_argument("--traffic-command", default="", help="command recorded with --traffic-from")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.traffic_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the per-GPU share of a sharded verification is the single-GPU workload).",
@@ -235,9 +296,7 @@ def main():
     ref = (sets[0].acc.clone(), sets[0].path.clone(), sets[0].tok.clone())
     graphs = []
     for s in sets:
-        graphs.append({"step": capture(s.step), "mask": capture(s.mask),
-                       "attention": capture(s.attention), "accept": capture(s.accept),
-                       "compact": capture(s.compact)})
+        graphs.append({"step": capture(s.step)})
     for _ in range(3):                                    # replays agree with the eager run
         graphs[0]["step"].replay()
         torch.cuda.synchronize()
@@ -262,7 +321,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    kt = kernel_times(sets, graphs, max(50, min(args.steps, 400)))
+    kt = kernel_times(sets, 10)
     work = algorithmic_work(inp)
     t_attn = kt["attention"]["mean_us"] * 1e-6
     ms_per_step = elapsed * 1e3 / args.steps
