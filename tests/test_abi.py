@@ -56,7 +56,7 @@ def test_workspace_queries(lib):
     assert lib.ev_tree_attention_workspace(ctypes.byref(_kv(head_dim=96)), 1, 64, 64) == 0
     counters = 2 * 65536 * 4                       # fixed row and sequence counter areas
     stats = 64 * 126 * 16                          # (max, sum) per 1024-logit chunk per row
-    assert lib.ev_accept_workspace(1, 64, 128256) == counters + stats + 64 * 48
+    assert lib.ev_accept_workspace(1, 64, 128256) == counters + stats + 64 * 8
     assert lib.ev_accept_workspace(1, 64, 128256) % 256 == 0
     assert lib.ev_accept_workspace(0, 64, 10) == 0
 

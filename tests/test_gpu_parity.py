@@ -139,12 +139,16 @@ def test_paged_equals_contiguous_on_the_same_data():
 
 
 def test_attention_is_deterministic():
+    """100 repeats are bitwise identical (no run-order or race dependence)."""
     inp = generate(scaled(C3, L=1000, V=64), with_logits=False)
     dev = to_device(inp)
-    O1, L1, _, _ = gpu_attention(inp, dev)
-    for _ in range(5):
-        O2, L2, _, _ = gpu_attention(inp, dev)
-        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    kv = ev.KvCache(dev.k, dev.v, dev.block_table)
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    O1, L1 = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), check=True)
+    O2, L2 = torch.empty_like(O1), torch.empty_like(L1)
+    for _ in range(100):
+        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), O2, L2)
+        assert torch.equal(O1, O2) and torch.equal(L1, L2)
 
 
 def test_attention_reports_prefix_beyond_cache():
@@ -229,6 +233,41 @@ def test_rejection_many_seeds_bonus_paths():
     o = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
     for a, b in zip(r, o[:3]):
         assert np.array_equal(a, b)
+
+
+def test_rejection_gpu_preserves_target_distribution_chi_square():
+    """The GPU sampler itself emits the target's distribution (explainer "Why it works";
+    study note case 3): 5e5 copies of a tiny tree with fresh uniforms.  The first emitted
+    token must follow p_root, and the second, given node 1 was accepted, p_node1."""
+    import scipy.special
+    import scipy.stats
+    V, tau = 8, 0.7
+    parent = np.array([-1, 0, 0, 0, 1, 1], np.int32)
+    rng = np.random.default_rng(2024)
+    logits = (2 * rng.standard_normal((6, V))).astype(np.float32)
+    top, t1 = int(np.argmax(logits[0])), int(np.argmax(logits[1]))
+    tokens = np.array([0, top, (top + 3) % V, (top + 5) % V, t1, (t1 + 2) % V], np.int32)
+    Bc, calls = 10000, 50
+    lg = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(logits, (Bc, 6, V)))).cuda()
+    tk = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(tokens, (Bc, 6)))).cuda()
+    pa = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(parent, (Bc, 6)))).cuda()
+    first, second, lens = np.zeros(V, np.int64), np.zeros(V, np.int64), np.zeros(3, np.int64)
+    urng = np.random.default_rng(2025)
+    for _ in range(calls):
+        u = torch.from_numpy(urng.random((Bc, 6))).cuda()
+        acc, path, out = (t.cpu().numpy() for t in
+                          ev.ev_accept_rejection(lg, tk, pa, tau, u, check=True))
+        first += np.bincount(out[:, 0], minlength=V)
+        sel = (acc >= 1) & (path[:, 1] == 1)
+        second += np.bincount(out[sel, 1], minlength=V)
+        lens += np.bincount(acc, minlength=3)[:3]
+    inv_tau = 1.0 / np.float64(np.float32(tau))
+    ref0 = scipy.special.softmax(logits[0].astype(np.float64) * inv_tau)
+    ref1 = scipy.special.softmax(logits[1].astype(np.float64) * inv_tau)
+    pv0 = scipy.stats.chisquare(first, first.sum() * ref0).pvalue
+    pv1 = scipy.stats.chisquare(second, second.sum() * ref1).pvalue
+    assert pv0 > 1e-3 and pv1 > 1e-3, (pv0, pv1, first, second)
+    assert lens[1] > 0 and lens[2] > 0
 
 
 def test_accept_workspace_reuse_across_shapes():

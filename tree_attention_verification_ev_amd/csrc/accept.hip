@@ -52,24 +52,33 @@ __host__ __device__ inline int n_chunks_of(int V) { return (V + kChunk - 1) / kC
 
 // exp(x) for x <= 0 in float64 by the table-driven method of P. T. P. Tang (ACM TOMS 15(2),
 // 1989): x = (64 m + j) ln2/64 + r with |r| <= ln2/128, exp(x) = 2^m 2^(j/64) exp(r), the
-// last factor by its Taylor polynomial to r^6 (truncation below 3e-20).  tab[j] = 2^(j/64).
+// last factor by its Taylor polynomial to r^5 (truncation below 4e-17).  tab[j] = 2^(j/64).
+// The nearest integer to 64 x / ln2 comes from adding and removing 1.5 * 2^52, whose low
+// word then holds it as a two's-complement integer.  Arguments below -745 (results below
+// the smallest subnormal) are clamped there, so they return at most 5e-324.
 __device__ inline double exp_nonpos(double x, const double *tab) {
   constexpr double kInvLn2x64 = 92.33248261689366;            // 64 / ln 2
   constexpr double kLn2d64Hi = 0.010830424696249145;          // ln2/64 rounded to double
   constexpr double kLn2d64Lo = 3.623510646634843e-19;         // ln2/64 - kLn2d64Hi
-  if (!(x > -745.2)) return 0.0;
-  const double kf = rint(x * kInvLn2x64);
-  const int k = (int)kf;
+  constexpr double kShifter = 6755399441055744.0;             // 1.5 * 2^52
+  x = fmax(x, -745.0);
+  const double t = fma(x, kInvLn2x64, kShifter);
+  const double kf = t - kShifter;
+  const int k = (int)(uint32_t)__double_as_longlong(t);
   double r = fma(-kf, kLn2d64Hi, x);
   r = fma(-kf, kLn2d64Lo, r);
-  double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
-  p = fma(r, p, 1.0 / 24.0);
+  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
   p = fma(r, p, 1.0 / 6.0);
   p = fma(r, p, 0.5);
   p = fma(r, p, 1.0);
   p *= r;                                                     // exp(r) - 1
-  const double t = tab[k & 63];
-  return ldexp(fma(t, p, t), k >> 6);
+  const double tj = tab[k & 63];
+  return ldexp(fma(tj, p, tj), k >> 6);
+}
+
+// s - M for a logit at inverse temperature inv_tau (one rounding).
+__device__ inline double shifted(float logit, double inv_tau, double M) {
+  return fma((double)logit, inv_tau, -M);
 }
 
 // Lane's 16 logits of chunk `base`: element (k*64 + lane)*4 + e, k < 4, e < 4 (coalesced).
@@ -97,12 +106,12 @@ __device__ inline void load_chunk(const float *row, int V, int base, bool vec_ok
   }
 }
 
-// (value, index) pairs: larger value wins, equal values keep the lower index.
+// (value, index) pairs: larger value wins, equal values keep the lower index (selects,
+// no branches).
 __device__ inline void better(float &v, int &i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
+  const bool take = (v2 > v) | ((v2 == v) & (i2 < i));
+  v = take ? v2 : v;
+  i = take ? i2 : i;
 }
 
 __device__ inline void wave_argmax(float &v, int &i) {
@@ -117,6 +126,12 @@ __device__ inline void wave_argmax(float &v, int &i) {
 __device__ inline double wave_sum(double x) {
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) x += __shfl_xor(x, w);
+  return x;
+}
+
+__device__ inline float wave_max_f(float x) {
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) x = fmaxf(x, __shfl_xor(x, w));
   return x;
 }
 
@@ -163,15 +178,6 @@ __device__ inline bool last_arrival(int32_t *cnt, int expected, int *s_flag) {
   return *s_flag;
 }
 
-struct NodeOut {                         // one per (sequence, node), written by its row's
-  double Z;                              // last workgroup: residual mass left at the node
-  double M, S;                           // row statistics (rejection)
-  double prej;                           // p of this node's token at its parent, if rejected
-  uint64_t rej;                          // children whose tokens were rejected at this node
-  int32_t next;                          // accepted child, -1 if none
-  int32_t y;                             // greedy: the row's lowest argmax
-};
-
 struct AcceptArgs {
   const float *logits;
   const int32_t *tokens;
@@ -180,18 +186,22 @@ struct AcceptArgs {
   double inv_tau;
   const double *uniforms;
   void *stats;                           // [B*T][n_chunks] chunk statistics
-  int32_t *row_cnt;                      // [B*T]
-  int32_t *seq_cnt;                      // [B]
-  NodeOut *nodes;                        // [B*T]
+  int32_t *row_cnt;                      // [B*T] arrivals per row
+  int32_t *seq_cnt;                      // [B] settled rows per sequence
+  uint64_t *node_out;                    // [B*T] (accepted child | bonus token << 32)
   int32_t *accept_len;
   int32_t *path;
   int32_t *out_tokens;
   int32_t *dev_status;
 };
 
-// Row statistics (max s, sum exp(s - max)) of a node from its chunk statistics, held in
-// registers (lane holds chunks lane, lane + 64, ... up to kChunkRegs of them).
-constexpr int kChunkRegs = 4;            // V <= 256 Ki logits
+__device__ inline uint64_t pack_node(int next, int bonus) {
+  return (uint64_t)(uint32_t)next | ((uint64_t)(uint32_t)bonus << 32);
+}
+
+// Row statistics (max s, sum exp(s - max)) from chunk statistics held in registers: lane
+// holds chunks lane, lane + 64, ... (kChunkRegs of them, so V <= 256 Ki logits).
+constexpr int kChunkRegs = 4;
 __device__ inline void row_stats_regs(const RejStat (&cs)[kChunkRegs], const double *tab,
                                       double &M, double &S) {
   M = -INFINITY;
@@ -205,85 +215,70 @@ __device__ inline void row_stats_regs(const RejStat (&cs)[kChunkRegs], const dou
   S = wave_sum(S);
 }
 
-// Inverse-CDF draw from the residual of a node (rejected tokens: lanes set in `rej` hold
-// them in `tok` and their probabilities in `prej`).  One wavefront.
-__device__ int residual_draw(const AcceptArgs &a, const float *row, const RejStat *st, double M,
-                             double S, uint64_t rej, int tok, double prej, double t,
-                             const double *tab) {
+// Inverse-CDF draw from the residual of a node, t = u0 * Z (one wavefront).  Rejected
+// tokens: lanes set in `rej` hold them in `tok` and their probabilities in `prej`.  The
+// chunk whose cumulative residual mass first exceeds t is found from the chunk statistics
+// (cs, strided as in row_stats_regs); that chunk is then scanned element by element.
+__device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
+                             const RejStat (&cs)[kChunkRegs], double M, double S,
+                             uint64_t rej, int tok, double prej, double t, const double *tab) {
   const int lane = threadIdx.x & 63;
-  const int nc = a.n_chunks;
-  const int cpl = (nc + 63) / 64;      // contiguous chunks per lane
-  // chunk masses with the rejected tokens removed
-  double mass[4];                       // cpl <= 4 for V <= 262144
-  double tot = 0.0;
-  for (int r = 0; r < cpl; ++r) {
-    int c = lane * cpl + r;
-    mass[r] = c < nc ? observe(&st[c].S) * exp_nonpos(observe(&st[c].M) - M, tab) / S : 0.0;
-  }
-  for (uint64_t rr = rej; rr; rr &= rr - 1) {
-    int src = __ffsll((unsigned long long)rr) - 1;
-    int x = __shfl(tok, src);
-    double px = __shfl(prej, src);
-    int c = x / kChunk;
-    for (int r = 0; r < cpl; ++r)
-      if (lane * cpl + r == c) mass[r] -= px;
-  }
-  for (int r = 0; r < cpl; ++r) tot += mass[r];
-  // exclusive scan of lane totals
-  double incl = tot;
+  const double inv_S = 1.0 / S;
+  double mass[kChunkRegs];
 #pragma unroll
-  for (int w = 1; w < 64; w <<= 1) {
-    double y = __shfl_up(incl, w);
-    if (lane >= w) incl += y;
+  for (int r = 0; r < kChunkRegs; ++r)
+    mass[r] = cs[r].S > 0.0 ? cs[r].S * exp_nonpos(cs[r].M - M, tab) * inv_S : 0.0;
+  for (uint64_t rr = rej; rr; rr &= rr - 1) {
+    const int src = __ffsll((unsigned long long)rr) - 1;
+    const int x = __shfl(tok, src);
+    const double px = __shfl(prej, src);
+#pragma unroll
+    for (int r = 0; r < kChunkRegs; ++r)
+      if (lane + 64 * r == x / kChunk) mass[r] -= px;
   }
-  double excl = incl - tot;
-  uint64_t hit = __ballot(incl > t);
   int cstar = -1;
-  double cbefore = 0.0;
-  if (hit) {
-    int hl = __ffsll((unsigned long long)hit) - 1;
-    if (lane == hl) {
-      double acc = excl;
-      for (int r = 0; r < cpl; ++r) {
-        if (acc + mass[r] > t || r == cpl - 1) {
-          cstar = lane * cpl + r;
-          cbefore = acc;
-          break;
-        }
-        acc += mass[r];
+  double cbefore = -INFINITY, base = 0.0;
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) {
+    if (cstar < 0 && 64 * r < nc) {
+      double incl = mass[r];
+#pragma unroll
+      for (int w = 1; w < 64; w <<= 1) {
+        const double y = __shfl_up(incl, w);
+        if (lane >= w) incl += y;
       }
-      if (cstar >= nc) cstar = nc - 1;
+      const uint64_t hit = __ballot(lane + 64 * r < nc && base + incl > t);
+      if (hit) {
+        const int hl = __ffsll((unsigned long long)hit) - 1;
+        cstar = hl + 64 * r;
+        cbefore = base + __shfl(incl - mass[r], hl);
+      }
+      base += __shfl(incl, 63);
     }
-    cstar = __shfl(cstar, hl);
-    cbefore = __shfl(cbefore, hl);
-  } else {
-    cstar = nc - 1;                      // rounding left t beyond the total: last chunk
-    cbefore = -INFINITY;
   }
-  // scan the chosen chunk element by element (lane owns 16 consecutive ids)
+  if (cstar < 0) cstar = nc - 1;          // rounding left t beyond the total: last chunk
   for (;;) {
-    const int y0 = cstar * kChunk + lane * 16;
+    const int y0 = cstar * kChunk + lane * 16;   // lane scans 16 consecutive ids
     double pv[16];
-    double lsum = 0.0;
-    const double inv_S = 1.0 / S;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      int y = y0 + e;
-      pv[e] = y < a.V ? exp_nonpos((double)row[y] * a.inv_tau - M, tab) * inv_S : 0.0;
+      const int y = y0 + e;
+      const double pe = exp_nonpos(shifted(row[min(y, V - 1)], inv_tau, M), tab) * inv_S;
+      pv[e] = y < V ? pe : 0.0;
     }
     for (uint64_t rr = rej; rr; rr &= rr - 1) {
-      int src = __ffsll((unsigned long long)rr) - 1;
-      int x = __shfl(tok, src);
+      const int x = __shfl(tok, __ffsll((unsigned long long)rr) - 1);
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (y0 + e == x) pv[e] = 0.0;
     }
+    double lsum = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) lsum += pv[e];
     double li = lsum;
 #pragma unroll
     for (int w = 1; w < 64; w <<= 1) {
-      double y = __shfl_up(li, w);
+      const double y = __shfl_up(li, w);
       if (lane >= w) li += y;
     }
     double C = cbefore + (li - lsum);
@@ -294,10 +289,10 @@ __device__ int residual_draw(const AcceptArgs &a, const float *row, const RejSta
       if (first < 0 && pv[e] > 0.0 && C > t) first = y0 + e;
       if (pv[e] > 0.0) last = y0 + e;
     }
-    uint64_t fh = __ballot(first >= 0);
+    const uint64_t fh = __ballot(first >= 0);
     if (fh) return __shfl(first, __ffsll((unsigned long long)fh) - 1);
     // no crossing (rounding at a chunk edge or beyond the total): largest positive id
-    uint64_t lh = __ballot(last >= 0);
+    const uint64_t lh = __ballot(last >= 0);
     if (lh) return __shfl(last, 63 - __clzll((long long)lh));
     if (cstar == 0) return 0;
     --cstar;                             // empty chunk (all rejected / underflow): go down
@@ -311,8 +306,14 @@ __device__ int residual_draw(const AcceptArgs &a, const float *row, const RejSta
 constexpr int kMaxRows = 65535;
 constexpr size_t kCounterBytes = 2 * align_up((kMaxRows + 1) * sizeof(int32_t), 256);
 
+// Counter slot of row (or sequence) r: up to 4096 consecutive ids land on distinct 64-byte
+// lines (ids r and r + 4096 share one).  Arrivals on one line serialise in the memory
+// system, so packing the counters of neighbouring rows together would make every
+// workgroup of a launch queue on a handful of lines.
+__device__ inline int counter_slot(int64_t r) { return (int)((r & 4095) * 16 + (r >> 12)); }
+
 struct WsLayout {
-  size_t row_cnt, seq_cnt, stats, nodes, total;
+  size_t row_cnt, seq_cnt, stats, node_out, total;
 };
 
 inline WsLayout ws_layout(int B, int T, int V) {
@@ -321,40 +322,30 @@ inline WsLayout ws_layout(int B, int T, int V) {
   w.row_cnt = 0;
   w.seq_cnt = kCounterBytes / 2;
   w.stats = kCounterBytes;
-  w.nodes = w.stats + align_up(rows * n_chunks_of(V) * sizeof(RejStat), 256);
-  w.total = w.nodes + align_up(rows * sizeof(NodeOut), 256);
+  w.node_out = w.stats + align_up(rows * n_chunks_of(V) * sizeof(RejStat), 256);
+  w.total = w.node_out + align_up(rows * sizeof(uint64_t), 256);
   return w;
 }
 
-// Node data of sequence b, lane i = node i; false when parent[] or a token is invalid.
-__device__ inline bool load_tree(const AcceptArgs &a, int b, int &par, int &tok) {
-  const int lane = threadIdx.x & 63;
-  const bool live = lane < a.T;
-  par = live ? a.parent[(int64_t)b * a.T + lane] : -2;
-  tok = live ? a.tokens[(int64_t)b * a.T + lane] : -1;
-  const bool pok = !live || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
-  if (__any(!pok)) {
-    if (lane == 0) report(a.dev_status, EV_DERR_PARENT);
-    return false;
-  }
-  if (__any(live && lane > 0 && (tok < 0 || tok >= a.V))) {
-    if (lane == 0) report(a.dev_status, EV_DERR_TOKEN);
-    return false;
-  }
-  return true;
-}
-
-// Outcome of node n of sequence b (one wavefront): greedy argmax and matching child, or
-// the rejection tests of its children in ascending index.
+// Outcome of node n of sequence b (one wavefront; lane i holds parent, token and uniform
+// of node i): greedy — the row's lowest argmax y, the lowest-index child drafting y, and y
+// as the bonus; rejection — the tests of its children in ascending index, and, when none
+// is accepted, the bonus drawn from the residual.  The bonus is only used if the walk
+// ends here, but it depends on nothing else, so every row draws its own in parallel.
 template <bool REJ>
-__device__ void settle_node(const AcceptArgs &a, int b, int n, const double *tab) {
+__device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok, double ul,
+                            const double *tab) {
   const int lane = threadIdx.x & 63;
   const int T = a.T, nc = a.n_chunks;
   const int64_t row_id = (int64_t)b * T + n;
-  int par, tok;
-  NodeOut out{1.0, NAN, NAN, 0.0, 0, -1, 0};
-  if (load_tree(a, b, par, tok)) {
-    const bool live = lane < T;
+  const bool live = lane < T;
+  const bool pok = !live || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+  int next = -2, bonus = 0;              // -2: invalid tree, the sequence is skipped
+  if (__any(!pok)) {
+    if (lane == 0) report(a.dev_status, EV_DERR_PARENT);
+  } else if (__any(live && lane > 0 && (tok < 0 || tok >= a.V))) {
+    if (lane == 0) report(a.dev_status, EV_DERR_TOKEN);
+  } else {
     const uint64_t kids = __ballot(live && par == n);
     if (!REJ) {
       const uint64_t *st = (const uint64_t *)a.stats + row_id * nc;
@@ -366,28 +357,28 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, const double *tab
       }
       wave_argmax(v, i);
       const uint64_t match = kids & __ballot(live && tok == i);
-      out.y = i;
-      out.next = match ? __ffsll((unsigned long long)match) - 1 : -1;
+      next = match ? __ffsll((unsigned long long)match) - 1 : -1;
+      bonus = i;
     } else {
       const RejStat *st = (const RejStat *)a.stats + row_id * nc;
+      const float *row = a.logits + row_id * a.V;
       RejStat cs[kChunkRegs];
 #pragma unroll
       for (int r = 0; r < kChunkRegs; ++r) {
         const int c = lane + 64 * r;
         cs[r] = c < nc ? RejStat{observe(&st[c].M), observe(&st[c].S)} : RejStat{-INFINITY, 0.0};
       }
-      const float lg = ((kids >> lane) & 1) ? a.logits[row_id * a.V + tok] : 0.f;
-      const double ul = live ? a.uniforms[(int64_t)b * T + lane] : 0.0;
+      const float lg = ((kids >> lane) & 1) ? row[tok] : 0.f;
       double M, S;
       row_stats_regs(cs, tab, M, S);
       double Z = 1.0, myp = 0.0;
       uint64_t rej = 0;
-      int next = -1;
+      next = -1;
       for (uint64_t kk = kids; kk; kk &= kk - 1) {
         const int c = __ffsll((unsigned long long)kk) - 1;
         const int x = __shfl(tok, c);
         if (__ballot(((rej >> lane) & 1) && tok == x)) continue;   // already rejected here
-        const double p = exp_nonpos((double)__shfl(lg, c) * a.inv_tau - M, tab) / S;
+        const double p = exp_nonpos(shifted(__shfl(lg, c), a.inv_tau, M), tab) / S;
         if (__shfl(ul, c) * Z < p) {
           next = c;
           break;
@@ -396,38 +387,23 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, const double *tab
         if (lane == c) myp = p;
         Z -= p;
       }
-      out.Z = Z;
-      out.M = M;
-      out.S = S;
-      out.rej = rej;
-      out.next = next;
-      if ((rej >> lane) & 1) publish(&a.nodes[(int64_t)b * T + lane].prej, myp);
+      bonus = next >= 0 ? -1
+                        : residual_draw(row, a.V, nc, a.inv_tau, cs, M, S, rej, tok, myp,
+                                        __shfl(ul, 0) * Z, tab);
     }
-  } else {
-    out.next = -2;                       // invalid tree: the sequence's outputs are skipped
   }
-  if (lane == 0) {
-    NodeOut *dst = a.nodes + row_id;
-    publish(&dst->Z, out.Z);
-    publish(&dst->M, out.M);
-    publish(&dst->S, out.S);
-    publish(&dst->rej, out.rej);
-    publish(&dst->next, out.next);
-    publish(&dst->y, out.y);
-  }
+  if (lane == 0) publish(&a.node_out[row_id], pack_node(next, bonus));
 }
 
-// Follow accepted children from the root of sequence b and draw the bonus token (one
-// wavefront); writes accept_len, path and out_tokens.
-template <bool REJ>
-__device__ void finish_sequence(const AcceptArgs &a, int b, const double *tab) {
+// Follow accepted children from the root of sequence b and emit the bonus token of the
+// last node (one wavefront; lane i holds the token of node i).
+__device__ void finish_sequence(const AcceptArgs &a, int b, int tok) {
   const int lane = threadIdx.x & 63;
   const int T = a.T;
   const bool live = lane < T;
-  const NodeOut *nodes = a.nodes + (int64_t)b * T;
-  const int next_l = live ? observe(&nodes[lane].next) : -1;
-  if (__any(next_l == -2)) return;      // invalid tree, already reported
-  const int tok = live ? a.tokens[(int64_t)b * T + lane] : -1;
+  const uint64_t w = live ? observe(&a.node_out[(int64_t)b * T + lane]) : pack_node(-1, -1);
+  const int next_l = (int)(uint32_t)w, bonus_l = (int)(uint32_t)(w >> 32);
+  if (__any(next_l == -2)) return;       // invalid tree, already reported
   int node = 0, k = 0;
   int my_path = lane == 0 ? 0 : -1;      // lane m holds path[m]
   int my_out = -1;                       // lane m holds out_tokens[m]
@@ -440,18 +416,7 @@ __device__ void finish_sequence(const AcceptArgs &a, int b, const double *tab) {
     if (lane == k) my_path = nxt;
     node = nxt;
   }
-  int bonus;
-  if (!REJ) {
-    bonus = observe(&nodes[node].y);
-  } else {
-    const int64_t row_id = (int64_t)b * T + node;
-    const uint64_t rej = observe(&nodes[node].rej);
-    const double prej = ((rej >> lane) & 1) ? observe(&nodes[lane].prej) : 0.0;
-    const double u0 = a.uniforms[(int64_t)b * T];
-    bonus = residual_draw(a, a.logits + row_id * a.V, (const RejStat *)a.stats + row_id * a.n_chunks,
-                          observe(&nodes[node].M), observe(&nodes[node].S), rej, tok, prej,
-                          u0 * observe(&nodes[node].Z), tab);
-  }
+  const int bonus = __shfl(bonus_l, node);
   if (lane == k) my_out = bonus;
   if (live) {
     a.path[(int64_t)b * T + lane] = my_path;
@@ -465,31 +430,50 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ double tab[64];
   __shared__ int s_last;
   if (REJ) fill_exp_table(tab);
-  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x * kChunksPerWG + wave;
   const int64_t row = blockIdx.y;
   const int nc = a.n_chunks;
+  const int b = (int)(row / a.T), n = (int)(row % a.T);
+  // The tree of this sequence, for the settle and walk steps below (loaded up front so
+  // that its latency hides behind the logit stream).
+  int par = -2, tok = -1;
+  double ul = 0.0;
+  if (wave == 0 && lane < a.T) {
+    par = a.parent[(int64_t)b * a.T + lane];
+    tok = a.tokens[(int64_t)b * a.T + lane];
+    if (REJ) ul = a.uniforms[(int64_t)b * a.T + lane];
+  }
+  __syncthreads();
 
   // ---- this wavefront's chunk statistics ----
   if (chunk < nc) {
     float v[16];
     int idx[16];
     load_chunk(a.logits + row * a.V, a.V, chunk * kChunk, (a.V & 3) == 0, v, idx);
-    float best = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) better(best, bi, v[e], idx[e]);
-    wave_argmax(best, bi);
     if (!REJ) {
+      // a lane visits its ids in increasing order, so a strict > keeps the lowest index
+      float best = -INFINITY;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool gt = v[e] > best;
+        best = gt ? v[e] : best;
+        bi = gt ? idx[e] : bi;
+      }
+      wave_argmax(best, bi);
       if (lane == 0) publish((uint64_t *)a.stats + row * nc + chunk, pack(GreedyStat{best, bi}));
     } else {
-      const double M = (double)best * a.inv_tau;
+      float best = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) best = fmaxf(best, v[e]);
+      const double M = (double)wave_max_f(best) * a.inv_tau;
+      // Padding past V holds -inf: its term is clamped to at most 5e-324, which vanishes
+      // next to the chunk's own maximum term (1), so no per-element test is needed.
       double sum = 0.0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (idx[e] != INT_MAX) sum += exp_nonpos((double)v[e] * a.inv_tau - M, tab);
+      for (int e = 0; e < 16; ++e) sum += exp_nonpos(shifted(v[e], a.inv_tau, M), tab);
       sum = wave_sum(sum);
       if (lane == 0) {
         RejStat *dst = (RejStat *)a.stats + row * nc + chunk;
@@ -498,15 +482,14 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
       }
     }
   }
-  if (!last_arrival(&a.row_cnt[row], gridDim.x, &s_last)) return;
+  if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
 
   // ---- last workgroup of this row: settle the node ----
-  const int b = (int)(row / a.T), n = (int)(row % a.T);
-  if (wave == 0) settle_node<REJ>(a, b, n, tab);
-  if (!last_arrival(&a.seq_cnt[b], a.T, &s_last)) return;
+  if (wave == 0) settle_node<REJ>(a, b, n, par, tok, ul, tab);
+  if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
 
-  // ---- last row of this sequence: walk and bonus ----
-  if (wave == 0) finish_sequence<REJ>(a, b, tab);
+  // ---- last row of this sequence: walk ----
+  if (wave == 0) finish_sequence(a, b, tok);
 }
 
 static ev_status check_common(const float *logits, const int32_t *tokens, const int32_t *parent,
@@ -529,7 +512,7 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
   char *base = (char *)ws;
   AcceptArgs a{logits, tokens, parent, B, T, V, n_chunks_of(V), inv_tau, uniforms,
                base + w.stats, (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
-               (NodeOut *)(base + w.nodes), accept_len, path, out_tokens, dev_status};
+               (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status};
   dim3 grid((a.n_chunks + kChunksPerWG - 1) / kChunksPerWG, B * T);
   if (rej)
     hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(256), 0, stream, a);
