@@ -114,31 +114,97 @@ __device__ inline void better(float &v, int &i, float v2, int i2) {
   i = take ? i2 : i;
 }
 
+// Whole-wavefront reductions (every lane active).  Within each row of 16 lanes, DPP
+// moves exchange with the neighbour in the pair, then the other pair of the quad, then
+// the mirrored quad of the half-row, then the mirrored half of the row; the four row
+// results are then read from lanes 0, 16, 32 and 48.  The result is wave-uniform and its
+// combination order is fixed.
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;    // row_half_mirror
+constexpr int kDppMirror = 0x140;        // row_mirror
+
+template <int CTRL>
+__device__ inline int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, true);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ inline double dpp_d(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ inline int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ inline float lane_f(float x, int l) { return __int_as_float(lane_i(__float_as_int(x), l)); }
+__device__ inline double lane_d(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)lane_i((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)lane_i((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele within each row of 16 (row_shr
+// by 1, 2, 4, 8; lanes shifted in from outside the row read 0), then each row adds the
+// totals of the rows before it.
+template <int SHR>
+__device__ inline double dpp_shr_d(double x) {
+  return dpp_d<0x110 + SHR>(x);
+}
+__device__ inline double wave_inclusive_sum(double x) {
+  x += dpp_shr_d<1>(x);
+  x += dpp_shr_d<2>(x);
+  x += dpp_shr_d<4>(x);
+  x += dpp_shr_d<8>(x);
+  const double t0 = lane_d(x, 15), t1 = lane_d(x, 31), t2 = lane_d(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  const double off = row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+  return x + off;
+}
+
+template <int CTRL>
+__device__ inline void argmax_step(float &v, int &i) {
+  better(v, i, dpp_f<CTRL>(v), dpp_i<CTRL>(i));
+}
 __device__ inline void wave_argmax(float &v, int &i) {
+  argmax_step<kDppQuadSwap1>(v, i);
+  argmax_step<kDppQuadSwap2>(v, i);
+  argmax_step<kDppHalfMirror>(v, i);
+  argmax_step<kDppMirror>(v, i);
+  float bv = lane_f(v, 0);
+  int bi = lane_i(i, 0);
 #pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    float v2 = __shfl_xor(v, w);
-    int i2 = __shfl_xor(i, w);
-    better(v, i, v2, i2);
-  }
+  for (int r = 16; r < 64; r += 16) better(bv, bi, lane_f(v, r), lane_i(i, r));
+  v = bv;
+  i = bi;
 }
 
 __device__ inline double wave_sum(double x) {
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) x += __shfl_xor(x, w);
-  return x;
+  x += dpp_d<kDppQuadSwap1>(x);
+  x += dpp_d<kDppQuadSwap2>(x);
+  x += dpp_d<kDppHalfMirror>(x);
+  x += dpp_d<kDppMirror>(x);
+  return (lane_d(x, 0) + lane_d(x, 16)) + (lane_d(x, 32) + lane_d(x, 48));
 }
 
 __device__ inline float wave_max_f(float x) {
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) x = fmaxf(x, __shfl_xor(x, w));
-  return x;
+  x = fmaxf(x, dpp_f<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppMirror>(x));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
 }
 
 __device__ inline double wave_max(double x) {
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) x = fmax(x, __shfl_xor(x, w));
-  return x;
+  x = fmax(x, dpp_d<kDppQuadSwap1>(x));
+  x = fmax(x, dpp_d<kDppQuadSwap2>(x));
+  x = fmax(x, dpp_d<kDppHalfMirror>(x));
+  x = fmax(x, dpp_d<kDppMirror>(x));
+  return fmax(fmax(lane_d(x, 0), lane_d(x, 16)), fmax(lane_d(x, 32), lane_d(x, 48)));
 }
 
 // 2^(j/64), j < 64, into LDS (one entry per thread of the first wavefront).
@@ -241,12 +307,7 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
 #pragma unroll
   for (int r = 0; r < kChunkRegs; ++r) {
     if (cstar < 0 && 64 * r < nc) {
-      double incl = mass[r];
-#pragma unroll
-      for (int w = 1; w < 64; w <<= 1) {
-        const double y = __shfl_up(incl, w);
-        if (lane >= w) incl += y;
-      }
+      const double incl = wave_inclusive_sum(mass[r]);
       const uint64_t hit = __ballot(lane + 64 * r < nc && base + incl > t);
       if (hit) {
         const int hl = __ffsll((unsigned long long)hit) - 1;
@@ -275,12 +336,7 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
     double lsum = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) lsum += pv[e];
-    double li = lsum;
-#pragma unroll
-    for (int w = 1; w < 64; w <<= 1) {
-      const double y = __shfl_up(li, w);
-      if (lane >= w) li += y;
-    }
+    const double li = wave_inclusive_sum(lsum);
     double C = cbefore + (li - lsum);
     int first = -1, last = -1;
 #pragma unroll
@@ -371,6 +427,7 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
       const float lg = ((kids >> lane) & 1) ? row[tok] : 0.f;
       double M, S;
       row_stats_regs(cs, tab, M, S);
+      const double inv_S = 1.0 / S;
       double Z = 1.0, myp = 0.0;
       uint64_t rej = 0;
       next = -1;
@@ -378,7 +435,7 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
         const int c = __ffsll((unsigned long long)kk) - 1;
         const int x = __shfl(tok, c);
         if (__ballot(((rej >> lane) & 1) && tok == x)) continue;   // already rejected here
-        const double p = exp_nonpos(shifted(__shfl(lg, c), a.inv_tau, M), tab) / S;
+        const double p = exp_nonpos(shifted(__shfl(lg, c), a.inv_tau, M), tab) * inv_S;
         if (__shfl(ul, c) * Z < p) {
           next = c;
           break;
