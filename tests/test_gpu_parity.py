@@ -101,6 +101,7 @@ ATTN_SMALL = [
     ("C3_L64_aligned", scaled(C3, L=64, V=64)),
     ("C4_small", scaled(C4, B=4, L=(40, 400), V=64)),
     ("C5_small", scaled(C5, B=2, L=700, V=64)),
+    ("C3_varlen_contiguous", scaled(C3, B=3, L=(10, 900), V=64)),
     ("chain64_mha", scaled(C2, T=64, tree="chain", L=130, V=64, Hq=4, Hkv=4)),
     ("star64_gqa", scaled(C3, tree="star", L=77, V=64)),
     ("root_only", scaled(C3, T=1, tree="grow", L=200, V=64)),

@@ -382,10 +382,20 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
   const int ntiles = (nkeys + kKT - 1) / kKT;
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(t_begin + a.tiles_per_split, ntiles);
-  if (t_begin >= t_end) return;         // this split lies beyond the sequence
-
   const int rows = a.T * a.G;
   const int row0 = (rb * NW + wave) * QT * 32;
+  if (t_begin >= t_end) {               // this split lies beyond the sequence: no weight
+    if (a.n_splits > 1 && hh == 0) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        const int r = row0 + t * 32 + qn;
+        if (r >= rows) continue;
+        const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
+        a.part_lse[(int64_t)split * a.B * a.T * a.Hq + orow] = -INFINITY;
+      }
+    }
+    return;
+  }
   const __bf16 *Q = (const __bf16 *)a.q;
   const __bf16 *K = (const __bf16 *)a.k;
   const __bf16 *V = (const __bf16 *)a.v;
@@ -514,6 +524,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6;
   const int qn = lane & 31;
   const int hh = lane >> 5;
+  const int rows = a.T * a.G;
+  const int row0 = (rb * NW + wave) * 32;
 
   const int L = a.prefix_len[b];
   const int nkeys = L + a.T;
@@ -524,10 +536,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int ntiles = (nkeys + kKT - 1) / kKT;
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(t_begin + a.tiles_per_split, ntiles);
-  if (t_begin >= t_end) return;
+  if (t_begin >= t_end) {
+    // an empty split (a shorter sequence of the batch): its partial carries no weight
+    if (a.n_splits > 1 && hh == 0 && row0 + qn < rows) {
+      const int r = row0 + qn;
+      const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
+      a.part_lse[(int64_t)split * a.B * a.T * a.Hq + orow] = -INFINITY;
+    }
+    return;
+  }
 
-  const int rows = a.T * a.G;
-  const int row0 = (rb * NW + wave) * 32;
   const __bf16 *Q = (const __bf16 *)a.q;
   const __bf16 *K = (const __bf16 *)a.k;
   const __bf16 *V = (const __bf16 *)a.v;
@@ -704,11 +722,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int c = threadIdx.x & 31;
   if (row >= nrows) return;
-  const int b = (int)(row / ((int64_t)a.T * a.Hq));
-  const int L = a.prefix_len[b];
-  if (L < 0 || !a.kv.fits(L + a.T)) return;
-  const int ntiles = (L + a.T + kKT - 1) / kKT;
-  const int nvalid = min(a.n_splits, (ntiles + a.tiles_per_split - 1) / a.tiles_per_split);
+  // Every split wrote its partial LSE (an empty split -inf), so all n_splits are read
+  // without waiting for the sequence length.
+  const int nvalid = a.n_splits;
   float mx = -INFINITY, wsum = 0.f;
   float acc[E] = {};
   for (int s0 = 0; s0 < nvalid; s0 += BATCH) {
@@ -732,11 +748,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     for (int e = 0; e < E; ++e) acc[e] *= r;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const float w = ls[u] == -INFINITY ? 0.f : exp2f((ls[u] - bm) * kLog2e);
+      // a split without weight (LSE -inf) may hold unwritten partials: select, not multiply
+      const bool live = ls[u] != -INFINITY;
+      const float w = live ? exp2f((ls[u] - bm) * kLog2e) : 0.f;
       wsum += w;
       const float ws = w * sc[u];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += ws * (float)x[u][e];
+      for (int e = 0; e < E; ++e) acc[e] += live ? ws * (float)x[u][e] : 0.f;
     }
     mx = bm;
   }
