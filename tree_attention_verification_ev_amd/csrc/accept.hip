@@ -31,7 +31,7 @@
 namespace ev {
 
 constexpr int kChunk = 1024;       // logits per wavefront chunk (16 per lane)
-constexpr int kChunksPerWG = 4;    // one chunk per wavefront
+constexpr int kChunksPerWG = 4;    // wavefronts per workgroup (one chunk each per step)
 
 struct GreedyStat {                      // stored as one 64-bit word: value bits, index
   float val;
@@ -482,14 +482,53 @@ __device__ void finish_sequence(const AcceptArgs &a, int b, int tok) {
   if (lane == 0) a.accept_len[b] = k;
 }
 
+// Statistics of one 1024-logit chunk (already in registers) of row `row`.
 template <bool REJ>
+__device__ __forceinline__ void chunk_stats(const AcceptArgs &a, int64_t row, int chunk,
+                                            const float (&v)[16], const double *tab) {
+  const int lane = threadIdx.x & 63;
+  const int nc = a.n_chunks;
+  if (!REJ) {
+    // a lane visits its ids in increasing order, so a strict > keeps the lowest index
+    float best = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool gt = v[e] > best;
+      best = gt ? v[e] : best;
+      bi = gt ? chunk * kChunk + ((e >> 2) * 64 + lane) * 4 + (e & 3) : bi;
+    }
+    wave_argmax(best, bi);
+    if (lane == 0) publish((uint64_t *)a.stats + row * nc + chunk, pack(GreedyStat{best, bi}));
+  } else {
+    float best = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) best = fmaxf(best, v[e]);
+    const double M = (double)wave_max_f(best) * a.inv_tau;
+    // Padding past V holds -inf: its term is clamped to at most 5e-324, which vanishes
+    // next to the chunk's own maximum term (1), so no per-element test is needed.
+    double sum = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum += exp_nonpos(shifted(v[e], a.inv_tau, M), tab);
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      RejStat *dst = (RejStat *)a.stats + row * nc + chunk;
+      publish(&dst->M, M);
+      publish(&dst->S, sum);
+    }
+  }
+}
+
+// grid (chunk groups, rows); a workgroup's four wavefronts stream CPW chunks each, the
+// wavefronts of a workgroup interleaved chunk by chunk, with the next chunk's loads in
+// flight while the current one is reduced.
+template <bool REJ, int CPW>
 __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ double tab[64];
   __shared__ int s_last;
   if (REJ) fill_exp_table(tab);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int chunk = blockIdx.x * kChunksPerWG + wave;
   const int64_t row = blockIdx.y;
   const int nc = a.n_chunks;
   const int b = (int)(row / a.T), n = (int)(row % a.T);
@@ -505,39 +544,18 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __syncthreads();
 
   // ---- this wavefront's chunk statistics ----
-  if (chunk < nc) {
-    float v[16];
-    int idx[16];
-    load_chunk(a.logits + row * a.V, a.V, chunk * kChunk, (a.V & 3) == 0, v, idx);
-    if (!REJ) {
-      // a lane visits its ids in increasing order, so a strict > keeps the lowest index
-      float best = -INFINITY;
-      int bi = INT_MAX;
+  const float *lrow = a.logits + row * a.V;
+  const bool vec_ok = (a.V & 3) == 0;
+  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
+  float v[2][16];
+  int idx_unused[16];
+  if (c0 < nc) load_chunk(lrow, a.V, c0 * kChunk, vec_ok, v[0], idx_unused);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const bool gt = v[e] > best;
-        best = gt ? v[e] : best;
-        bi = gt ? idx[e] : bi;
-      }
-      wave_argmax(best, bi);
-      if (lane == 0) publish((uint64_t *)a.stats + row * nc + chunk, pack(GreedyStat{best, bi}));
-    } else {
-      float best = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) best = fmaxf(best, v[e]);
-      const double M = (double)wave_max_f(best) * a.inv_tau;
-      // Padding past V holds -inf: its term is clamped to at most 5e-324, which vanishes
-      // next to the chunk's own maximum term (1), so no per-element test is needed.
-      double sum = 0.0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sum += exp_nonpos(shifted(v[e], a.inv_tau, M), tab);
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        RejStat *dst = (RejStat *)a.stats + row * nc + chunk;
-        publish(&dst->M, M);
-        publish(&dst->S, sum);
-      }
-    }
+  for (int m = 0; m < CPW; ++m) {
+    const int c = c0 + kChunksPerWG * m;
+    if (m + 1 < CPW && c + kChunksPerWG < nc)
+      load_chunk(lrow, a.V, (c + kChunksPerWG) * kChunk, vec_ok, v[(m + 1) & 1], idx_unused);
+    if (c < nc) chunk_stats<REJ>(a, row, c, v[m & 1], tab);
   }
   if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
 
@@ -570,11 +588,24 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
   AcceptArgs a{logits, tokens, parent, B, T, V, n_chunks_of(V), inv_tau, uniforms,
                base + w.stats, (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
                (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status};
-  dim3 grid((a.n_chunks + kChunksPerWG - 1) / kChunksPerWG, B * T);
-  if (rej)
-    hipLaunchKernelGGL(accept_kernel<true>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(accept_kernel<false>, grid, dim3(256), 0, stream, a);
+  // Chunks per wavefront: as many as keep at least 2048 workgroups in the grid (a few per
+  // CU), so that large batches stream with loads in flight behind the reduction.
+  const int64_t rows = (int64_t)B * T;
+  int cpw = 4;
+  while (cpw > 1 && rows * ((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw)) < 2048)
+    cpw /= 2;
+  dim3 grid((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw), (unsigned)rows);
+#define EV_LAUNCH_ACCEPT(R, C) hipLaunchKernelGGL((accept_kernel<R, C>), grid, dim3(256), 0, stream, a)
+  if (rej) {
+    if (cpw == 4) EV_LAUNCH_ACCEPT(true, 4);
+    else if (cpw == 2) EV_LAUNCH_ACCEPT(true, 2);
+    else EV_LAUNCH_ACCEPT(true, 1);
+  } else {
+    if (cpw == 4) EV_LAUNCH_ACCEPT(false, 4);
+    else if (cpw == 2) EV_LAUNCH_ACCEPT(false, 2);
+    else EV_LAUNCH_ACCEPT(false, 1);
+  }
+#undef EV_LAUNCH_ACCEPT
   return launch_status();
 }
 
