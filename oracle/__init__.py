@@ -6,6 +6,7 @@ is involved) of what one verification pass of a drafted token tree computes:
   tree.py       ancestor mask of a parent[] tree
   attention.py  tree-masked attention with an explicit mask, contiguous or paged KV
   accept.py     greedy longest-matching walk and rejection-sampling walk
+  stochastic.py rejection-sampling walk for drafts sampled from a draft distribution
   compact.py    accepted-path KV compaction
 
 It shares no code with the HIP library and imports nothing from it.  Only the test
@@ -30,9 +31,10 @@ from .attention import tree_attention, tree_attention_batch, gather_paged
 from .accept import (greedy_walk, greedy_batch, target_probs, rejection_walk,
                      rejection_batch)
 from .compact import kv_compact
+from .stochastic import stochastic_walk, stochastic_batch
 
 __all__ = [
     "tree_mask", "tree_mask_batch", "tree_attention", "tree_attention_batch", "gather_paged",
     "greedy_walk", "greedy_batch", "target_probs", "rejection_walk", "rejection_batch",
-    "kv_compact",
+    "kv_compact", "stochastic_walk", "stochastic_batch",
 ]
