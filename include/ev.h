@@ -55,7 +55,8 @@ enum {
   EV_DERR_PARENT = 101,   /* parent[] is not a topological tree rooted at node 0 */
   EV_DERR_BOUNDS = 102,   /* prefix + tree does not fit the cache, or a block id is out of range */
   EV_DERR_TOKEN = 103,    /* a draft token id is outside [0, V) */
-  EV_DERR_PATH = 104      /* path / accept_len given to compaction is not a valid root path */
+  EV_DERR_PATH = 104,     /* path / accept_len given to compaction is not a valid root path */
+  EV_DERR_WIDTH = 105     /* a node has more children than the max_children bound */
 };
 
 typedef enum { EV_F32 = 0, EV_BF16 = 1 } ev_dtype;
@@ -148,6 +149,34 @@ ev_status ev_accept_rejection(const float *logits, const int32_t *tokens, const 
                               const double *uniforms,
                               int32_t *accept_len, int32_t *path, int32_t *out_tokens,
                               void *ws, size_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/* Bytes of workspace ev_accept_sampled needs (same limits and zero-fill contract as the
+ * acceptance workspace above). */
+size_t ev_accept_sampled_workspace(int32_t B, int32_t T, int32_t V);
+
+/* ev_accept_sampled — the accept-or-resample rule ([EX] "Why it works"; [SN] case 3) for
+ * drafts that were SAMPLED from a draft distribution instead of taken by argmax.
+ *   draft_logits [B][T][V] float: row a is the drafter's logits at node a; its children
+ *   were drawn independently from q_a = softmax(draft_logits[b][a] / draft_temperature)
+ *   (duplicate siblings allowed, each tested on its own).
+ *   p_a as in ev_accept_rejection; q_a by the same float64 contract with draft_temperature.
+ *   At node a the children are tried in ascending index against the residual
+ *   r = W / Z, W(y) = max(0, p_a(y) - s q_a(y)), Z = sum_y W(y), starting at s = 0: child c
+ *   drafting x is accepted iff uniforms[b][c] * q_a(x) * Z < W(x) (probability
+ *   min(1, r(x) / q_a(x))); a rejection adds Z to s (r becomes max(0, r - q_a),
+ *   renormalised).  When no child is accepted the emitted token is the inverse-CDF draw of
+ *   W in ascending token id with t = uniforms[b][0] * Z.
+ *   max_children: (host) bound on the children of any node, 0 <= max_children <= T; it
+ *   fixes the work (one pass over the undecided rows per child tested).  A node with more
+ *   children sets EV_DERR_WIDTH.
+ *   Outputs as for ev_accept_greedy.  EV_ERR_ARG unless both temperatures are finite and
+ *   > 0. */
+ev_status ev_accept_sampled(const float *logits, const float *draft_logits, const int32_t *tokens,
+                            const int32_t *parent, int32_t B, int32_t T, int32_t V,
+                            float temperature, float draft_temperature, const double *uniforms,
+                            int32_t max_children, int32_t *accept_len, int32_t *path,
+                            int32_t *out_tokens, void *ws, size_t ws_bytes, int32_t *dev_status,
+                            hipStream_t stream);
 
 /* ev_kv_compact — keep the accepted branch's KV ([TR] sec. 2 sequence diagram).
  * For m = 1..k (k = accept_len[b], path from an acceptance call), logical slot

@@ -2,7 +2,7 @@
 
 This package only *draws* inputs: token trees as parent arrays, Q/K/V, KV-cache layouts
 (contiguous or paged with a shuffled block table), target logits, draft tokens and
-uniform draws.  It holds none of the method's arithmetic (no masks, no softmax, no
+uniform draws, and a sampling drafter's logits and tokens.  It holds none of the method's arithmetic (no masks, no softmax, no
 acceptance, no compaction); both the CPU oracle and the HIP library receive the same
 arrays from here and compute independently.
 
@@ -12,9 +12,9 @@ tree-attention masking: trees of at most 64 nodes, depth 4-6, width 8) and the
 Llama-2-7B / Llama-3-70B layer shapes.
 """
 from .configs import CONFIGS, Config, config_by_name, scaled
-from .generate import Inputs, generate, round_to_bf16, static_tree_26
+from .generate import Inputs, generate, round_to_bf16, sampled_drafts, static_tree_26
 
 __all__ = [
     "CONFIGS", "Config", "config_by_name", "scaled",
-    "Inputs", "generate", "round_to_bf16", "static_tree_26",
+    "Inputs", "generate", "round_to_bf16", "sampled_drafts", "static_tree_26",
 ]

@@ -240,3 +240,28 @@ def generate(cfg: Config, tokens: str = "planted", layout: Optional[str] = None,
     return Inputs(cfg=cfg, layout=layout, parent=parent, tokens=tok, prefix_len=prefix_len,
                   q=q, k=k, v=v, block_table=block_table, cap=cap, logits=logits,
                   uniforms=uniforms, tau=np.float32(cfg.tau), planted=planted)
+
+
+def sampled_drafts(inp: Inputs, draft_tau: float = 0.8, noise: float = 1.0):
+    """Draft logits and draft tokens for acceptance with a sampling drafter.
+
+    The drafter's logits are the target's plus N(0, noise^2) noise (a drafter that mostly
+    agrees with the target).  Each node's children draw their tokens independently from
+    softmax(draft_logits[parent] / draft_tau) by the Gumbel-max trick (the argmax of the
+    scaled logits plus Gumbel noise), so no distribution is formed here.  The generator
+    is seeded from the configuration index, apart from generate()'s streams.
+    Returns (draft_logits float32 [B][T][V], tokens int32 [B][T], root token 0).
+    """
+    cfg = inp.cfg
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2000 + cfg.index])))
+    B, T, V = inp.logits.shape
+    draft = (inp.logits + noise * rng.standard_normal((B, T, V), dtype=np.float32)).astype(np.float32)
+    inv = 1.0 / float(np.float32(draft_tau))
+    tokens = np.zeros((B, T), np.int32)
+    for b in range(B):
+        for c in range(1, T):
+            a = int(inp.parent[b, c])
+            with np.errstate(divide="ignore"):
+                gumbel = -np.log(-np.log(rng.random(V)))
+            tokens[b, c] = int(np.argmax(draft[b, a].astype(np.float64) * inv + gumbel))
+    return draft, tokens

@@ -84,6 +84,18 @@ def test_host_errors_return_before_launch(lib):
     assert lib.ev_accept_rejection(P, P, P, 1, 8, 100, 0.0, P, P, P, P, P, 10**6, None, None) == 5
     assert lib.ev_accept_rejection(P, P, P, 1, 8, 100, float("inf"), P, P, P, P, P, 10**6, None, None) == 5
     assert lib.ev_accept_rejection(P, P, P, 1, 8, 100, 0.7, None, P, P, P, P, 10**6, None, None) == 1
+    samp = lambda tau=0.7, dtau=0.9, mc=3, ws=P, nbytes=10**8, logits=P, draft=P, T=8, V=100: \
+        lib.ev_accept_sampled(logits, draft, P, P, 1, T, V, tau, dtau, P, mc, P, P, P, ws, nbytes,
+                              None, None)
+    assert samp(tau=0.0) == 5
+    assert samp(dtau=float("nan")) == 5
+    assert samp(mc=-1) == 2
+    assert samp(mc=9) == 2                          # more than T
+    assert samp(T=65) == 2
+    assert samp(V=0) == 2
+    assert samp(draft=None) == 1
+    assert samp(nbytes=100) == 4
+    assert lib.ev_accept_sampled_workspace(1, 64, 128256) >= 2 * 65536 * 4 + 64 * 126 * 40
     assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=0)), P, P, P, 1, 8, P, None, None) == 2
     assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=2, layer_stride=0)), P, P, P, 1, 8, P, None, None) == 2
     assert lib.ev_kv_compact(ctypes.byref(d), None, P, P, 1, 8, P, None, None) == 1

@@ -26,12 +26,12 @@ EV_F32, EV_BF16 = 0, 1
 STATUS_NAMES = {
     0: "EV_OK", 1: "EV_ERR_NULL", 2: "EV_ERR_SHAPE", 3: "EV_ERR_DTYPE", 4: "EV_ERR_WORKSPACE",
     5: "EV_ERR_ARG", 6: "EV_ERR_LAUNCH", 101: "EV_DERR_PARENT", 102: "EV_DERR_BOUNDS",
-    103: "EV_DERR_TOKEN", 104: "EV_DERR_PATH",
+    103: "EV_DERR_TOKEN", 104: "EV_DERR_PATH", 105: "EV_DERR_WIDTH",
 }
 EXPORTED = (
     "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
-    "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection", "ev_kv_compact",
-    "ev_status_string",
+    "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection",
+    "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact", "ev_status_string",
 )
 
 
@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
             "ev_accept_greedy": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_rejection": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _P,
                                            _SZ, _P, _P]),
+            "ev_accept_sampled_workspace": (_SZ, [_I32, _I32, _I32]),
+            "ev_accept_sampled": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _I32,
+                                         _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_kv_compact": (_I32, [kv, _P, _P, _P, _I32, _I32, _P, _P, _P]),
             "ev_status_string": (ctypes.c_char_p, [_I32]),
         }
@@ -270,6 +273,38 @@ def ev_accept_rejection(logits: torch.Tensor, tokens: torch.Tensor, parent: torc
                                      _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
                                      _ptr(status), _stream(dev))
     _finish(code, "ev_accept_rejection", status, check)
+    return accept_len, path, out_tokens
+
+
+def ev_accept_sampled_workspace(B: int, T: int, V: int) -> int:
+    return int(lib().ev_accept_sampled_workspace(B, T, V))
+
+
+def ev_accept_sampled(logits: torch.Tensor, draft_logits: torch.Tensor, tokens: torch.Tensor,
+                      parent: torch.Tensor, temperature: float, draft_temperature: float,
+                      uniforms: torch.Tensor, max_children: int, accept_len=None, path=None,
+                      out_tokens=None, ws=None, dev_status=None, check: bool = False):
+    """Acceptance of drafts sampled from a draft distribution; returns
+    (accept_len, path, out_tokens).  ws must be zero-filled before its first use."""
+    _dev(logits, "logits", torch.float32)
+    _dev(draft_logits, "draft_logits", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    _dev(uniforms, "uniforms", torch.float64)
+    B, T, V = logits.shape
+    if tuple(draft_logits.shape) != (B, T, V):
+        raise ValueError("draft_logits must have the shape of logits")
+    dev = logits.device
+    accept_len, path, out_tokens = _accept_outputs(B, T, dev, accept_len, path, out_tokens)
+    if ws is None:
+        ws = torch.zeros(max(1, ev_accept_sampled_workspace(B, T, V)), dtype=torch.uint8, device=dev)
+    status = _status_word(dev, dev_status)
+    code = lib().ev_accept_sampled(_ptr(logits), _ptr(draft_logits), _ptr(tokens), _ptr(parent),
+                                   B, T, V, float(temperature), float(draft_temperature),
+                                   _ptr(uniforms), int(max_children), _ptr(accept_len), _ptr(path),
+                                   _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _ptr(status), _stream(dev))
+    _finish(code, "ev_accept_sampled", status, check)
     return accept_len, path, out_tokens
 
 

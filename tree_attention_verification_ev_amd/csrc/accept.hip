@@ -454,7 +454,8 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
 
 // Follow accepted children from the root of sequence b and emit the bonus token of the
 // last node (one wavefront; lane i holds the token of node i).
-__device__ void finish_sequence(const AcceptArgs &a, int b, int tok) {
+template <class Args>
+__device__ void finish_sequence(const Args &a, int b, int tok) {
   const int lane = threadIdx.x & 63;
   const int T = a.T;
   const bool live = lane < T;
@@ -609,6 +610,352 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
   return launch_status();
 }
 
+// ---------------------------------------------------------------------------------------
+// Acceptance with drafts sampled from a draft distribution q (one per node, from its own
+// logit row at its own temperature).  At a node the children are tested in ascending
+// index against the residual r = W / Z, W(y) = max(0, p(y) - s q(y)), Z = sum W: a child
+// drafting x is accepted iff u * q(x) * Z < W(x); a rejection grows s by Z.  When no
+// child is accepted the bonus token is drawn from W.  Z changes with every rejection, so
+// each rejection needs one more pass over the node's row: the work runs in rounds, one
+// launch per round, every launch one pass over the rows still being decided (a row
+// whose node is settled returns at once).  A node with c children is settled by round
+// c + 1, so the caller's bound on children per node fixes the number of launches.
+struct SampledRow {
+  double Mp, Sp, Mq, Sq;                 // row statistics of the target and draft rows
+  double s;                              // residual shift after the rejections so far
+  int32_t active;                        // still being decided
+  int32_t tried;                         // children tested so far
+};
+
+struct SampledArgs {
+  const float *logits;
+  const float *draft;
+  const int32_t *tokens;
+  const int32_t *parent;
+  int B, T, V, n_chunks, max_children;
+  double inv_tau, inv_tau_q;
+  const double *uniforms;
+  RejStat *pstat;                        // [B*T][n_chunks]
+  RejStat *qstat;                        // [B*T][n_chunks]
+  double *wpart;                         // [B*T][n_chunks] residual mass per chunk, this round
+  SampledRow *state;                     // [B*T]
+  int32_t *row_cnt;
+  int32_t *seq_cnt;
+  uint64_t *node_out;
+  int32_t *accept_len;
+  int32_t *path;
+  int32_t *out_tokens;
+  int32_t *dev_status;
+};
+
+struct SampledWs {
+  size_t row_cnt, seq_cnt, pstat, qstat, wpart, state, node_out, total;
+};
+
+inline SampledWs sampled_ws_layout(int B, int T, int V) {
+  SampledWs w;
+  const size_t rows = (size_t)B * T, per_chunk = rows * n_chunks_of(V);
+  w.row_cnt = 0;
+  w.seq_cnt = kCounterBytes / 2;
+  w.pstat = kCounterBytes;
+  w.qstat = w.pstat + align_up(per_chunk * sizeof(RejStat), 256);
+  w.wpart = w.qstat + align_up(per_chunk * sizeof(RejStat), 256);
+  w.state = w.wpart + align_up(per_chunk * sizeof(double), 256);
+  w.node_out = w.state + align_up(rows * sizeof(SampledRow), 256);
+  w.total = w.node_out + align_up(rows * sizeof(uint64_t), 256);
+  return w;
+}
+
+// Row statistics of one distribution from its chunk statistics (published this launch).
+__device__ inline void observed_row_stats(const RejStat *st, int nc, const double *tab, double &M,
+                                          double &S) {
+  const int lane = threadIdx.x & 63;
+  RejStat cs[kChunkRegs];
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) {
+    const int c = lane + 64 * r;
+    cs[r] = c < nc ? RejStat{observe(&st[c].M), observe(&st[c].S)} : RejStat{-INFINITY, 0.0};
+  }
+  row_stats_regs(cs, tab, M, S);
+}
+
+// Residual weight of logit pair (target, draft) under row state st (shift s).
+__device__ inline double residual_weight(float lp, float lq, const SampledArgs &a,
+                                         const SampledRow &st, double inv_sp, double inv_sq,
+                                         const double *tab) {
+  const double p = exp_nonpos(shifted(lp, a.inv_tau, st.Mp), tab) * inv_sp;
+  const double q = exp_nonpos(shifted(lq, a.inv_tau_q, st.Mq), tab) * inv_sq;
+  return fmax(0.0, fma(-st.s, q, p));
+}
+
+// Statistics launch: per-chunk (M, S) of both rows; the row's last workgroup validates
+// the tree and sets up the row state.
+template <int CPW>
+__global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
+  __shared__ double tab[64];
+  __shared__ int s_last;
+  fill_exp_table(tab);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.y;
+  const int nc = a.n_chunks;
+  const int b = (int)(row / a.T), n = (int)(row % a.T);
+  __syncthreads();
+  const float *lp = a.logits + row * a.V;
+  const float *lq = a.draft + row * a.V;
+  const bool vec_ok = (a.V & 3) == 0;
+  int idx_unused[16];
+  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
+#pragma unroll
+  for (int m = 0; m < CPW; ++m) {
+    const int c = c0 + kChunksPerWG * m;
+    if (c >= nc) continue;
+    float vp[16], vq[16];
+    load_chunk(lp, a.V, c * kChunk, vec_ok, vp, idx_unused);
+    load_chunk(lq, a.V, c * kChunk, vec_ok, vq, idx_unused);
+    float bp = -INFINITY, bq = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      bp = fmaxf(bp, vp[e]);
+      bq = fmaxf(bq, vq[e]);
+    }
+    const double Mp = (double)wave_max_f(bp) * a.inv_tau;
+    const double Mq = (double)wave_max_f(bq) * a.inv_tau_q;
+    double sp = 0.0, sq = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sp += exp_nonpos(shifted(vp[e], a.inv_tau, Mp), tab);
+      sq += exp_nonpos(shifted(vq[e], a.inv_tau_q, Mq), tab);
+    }
+    sp = wave_sum(sp);
+    sq = wave_sum(sq);
+    if (lane == 0) {
+      publish(&a.pstat[row * nc + c].M, Mp);
+      publish(&a.pstat[row * nc + c].S, sp);
+      publish(&a.qstat[row * nc + c].M, Mq);
+      publish(&a.qstat[row * nc + c].S, sq);
+    }
+  }
+  if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
+  if (wave == 0) {
+    const bool live = lane < a.T;
+    const int par = live ? a.parent[(int64_t)b * a.T + lane] : -2;
+    const int tok = live ? a.tokens[(int64_t)b * a.T + lane] : -1;
+    const bool pok = !live || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+    bool ok = true;
+    if (__any(!pok)) {
+      if (lane == 0) report(a.dev_status, EV_DERR_PARENT);
+      ok = false;
+    } else if (__any(live && lane > 0 && (tok < 0 || tok >= a.V))) {
+      if (lane == 0) report(a.dev_status, EV_DERR_TOKEN);
+      ok = false;
+    } else if (__popcll(__ballot(live && par == n)) > a.max_children) {
+      if (lane == 0) report(a.dev_status, EV_DERR_WIDTH);
+      ok = false;
+    }
+    SampledRow st{};
+    if (ok) {
+      observed_row_stats(a.pstat + row * nc, nc, tab, st.Mp, st.Sp);
+      observed_row_stats(a.qstat + row * nc, nc, tab, st.Mq, st.Sq);
+    }
+    if (lane == 0) {
+      st.s = 0.0;
+      st.active = ok ? 1 : 0;
+      st.tried = 0;
+      a.state[row] = st;
+      if (!ok) publish(&a.node_out[row], pack_node(-2, 0));
+      s_last = ok ? 0 : 1;               // an invalid tree settles the row at once
+    }
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // the sequence is skipped by the walk (its outputs are left as they were)
+  if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
+  if (wave == 0) {
+    const int tok = lane < a.T ? a.tokens[(int64_t)b * a.T + lane] : -1;
+    finish_sequence(a, b, tok);
+  }
+}
+
+// Bonus token of a node from the residual W of this round: the chunk whose cumulative
+// residual mass first exceeds t is found from the per-chunk masses (wp, lane-strided),
+// then that chunk is scanned element by element (one wavefront).
+__device__ int sampled_draw(const SampledArgs &a, int64_t row, const SampledRow &st, double t,
+                            const double *tab) {
+  const int lane = threadIdx.x & 63;
+  const int nc = a.n_chunks;
+  const double *wp = a.wpart + row * nc;
+  double mass[kChunkRegs];
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) {
+    const int c = lane + 64 * r;
+    mass[r] = c < nc ? observe(&wp[c]) : 0.0;
+  }
+  int cstar = -1;
+  double cbefore = -INFINITY, base = 0.0;
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) {
+    if (cstar < 0 && 64 * r < nc) {
+      const double incl = wave_inclusive_sum(mass[r]);
+      const uint64_t hit = __ballot(lane + 64 * r < nc && base + incl > t);
+      if (hit) {
+        const int hl = __ffsll((unsigned long long)hit) - 1;
+        cstar = hl + 64 * r;
+        cbefore = base + __shfl(incl - mass[r], hl);
+      }
+      base += __shfl(incl, 63);
+    }
+  }
+  if (cstar < 0) cstar = nc - 1;
+  const double inv_sp = 1.0 / st.Sp, inv_sq = 1.0 / st.Sq;
+  const float *lp = a.logits + row * a.V;
+  const float *lq = a.draft + row * a.V;
+  for (;;) {
+    const int y0 = cstar * kChunk + lane * 16;
+    double w[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int y = min(y0 + e, a.V - 1);
+      const double we = residual_weight(lp[y], lq[y], a, st, inv_sp, inv_sq, tab);
+      w[e] = y0 + e < a.V ? we : 0.0;
+    }
+    double lsum = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lsum += w[e];
+    const double li = wave_inclusive_sum(lsum);
+    double C = cbefore + (li - lsum);
+    int first = -1, last = -1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      C += w[e];
+      if (first < 0 && w[e] > 0.0 && C > t) first = y0 + e;
+      if (w[e] > 0.0) last = y0 + e;
+    }
+    const uint64_t fh = __ballot(first >= 0);
+    if (fh) return __shfl(first, __ffsll((unsigned long long)fh) - 1);
+    const uint64_t lh = __ballot(last >= 0);
+    if (lh) return __shfl(last, 63 - __clzll((long long)lh));
+    if (cstar == 0) return 0;
+    --cstar;
+    cbefore = -INFINITY;
+  }
+}
+
+// One round: every row still being decided takes one pass over its target and draft
+// logits for the residual mass Z at its current shift; its last workgroup then tests the
+// next child (or draws the bonus when every child has been rejected).
+template <int CPW>
+__global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
+  __shared__ double tab[64];
+  __shared__ int s_last;
+  const int64_t row = blockIdx.y;
+  const SampledRow st = a.state[row];    // written by an earlier launch
+  if (!st.active) return;                // settled: no workgroup of this row arrives
+  fill_exp_table(tab);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nc = a.n_chunks;
+  const int b = (int)(row / a.T), n = (int)(row % a.T);
+  __syncthreads();
+  const float *lp = a.logits + row * a.V;
+  const float *lq = a.draft + row * a.V;
+  const bool vec_ok = (a.V & 3) == 0;
+  const double inv_sp = 1.0 / st.Sp, inv_sq = 1.0 / st.Sq;
+  int idx_unused[16];
+  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
+#pragma unroll
+  for (int m = 0; m < CPW; ++m) {
+    const int c = c0 + kChunksPerWG * m;
+    if (c >= nc) continue;
+    float vp[16], vq[16];
+    load_chunk(lp, a.V, c * kChunk, vec_ok, vp, idx_unused);
+    load_chunk(lq, a.V, c * kChunk, vec_ok, vq, idx_unused);
+    double w = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w += residual_weight(vp[e], vq[e], a, st, inv_sp, inv_sq, tab);
+    w = wave_sum(w);
+    if (lane == 0) publish(&a.wpart[row * nc + c], w);
+  }
+  if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
+  if (wave == 0) {
+    double Z = 0.0;
+    for (int c = lane; c < nc; c += 64) Z += observe(&a.wpart[row * nc + c]);
+    Z = wave_sum(Z);
+    const bool live = lane < a.T;
+    const int par = live ? a.parent[(int64_t)b * a.T + lane] : -2;
+    const int tok = live ? a.tokens[(int64_t)b * a.T + lane] : -1;
+    uint64_t kids = __ballot(live && par == n);
+    for (int i = 0; i < st.tried; ++i) kids &= kids - 1;   // children tested in earlier rounds
+    int next = -1, bonus = -1;
+    bool done = true;
+    if (kids) {
+      const int c = __ffsll((unsigned long long)kids) - 1;
+      const int x = __shfl(tok, c);
+      const float lpx = lp[x], lqx = lq[x];
+      const double qx = exp_nonpos(shifted(lqx, a.inv_tau_q, st.Mq), tab) * inv_sq;
+      const double wx = residual_weight(lpx, lqx, a, st, inv_sp, inv_sq, tab);
+      const double u = a.uniforms[(int64_t)b * a.T + c];
+      if (u * qx * Z < wx) {
+        next = c;
+      } else {
+        done = false;
+        if (lane == 0) {
+          SampledRow nst = st;
+          nst.s = st.s + Z;
+          nst.tried = st.tried + 1;
+          a.state[row] = nst;              // read by the next launch
+        }
+      }
+    } else {
+      const double u0 = a.uniforms[(int64_t)b * a.T];
+      bonus = sampled_draw(a, row, st, u0 * Z, tab);
+    }
+    if (done && lane == 0) {
+      a.state[row].active = 0;
+      publish(&a.node_out[row], pack_node(next, bonus));
+    }
+    if (__shfl(done ? 1 : 0, 0)) s_last = 1;
+    else s_last = 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
+  if (wave == 0) {
+    const int tok = lane < a.T ? a.tokens[(int64_t)b * a.T + lane] : -1;
+    finish_sequence(a, b, tok);
+  }
+}
+
+static ev_status launch_sampled(const float *logits, const float *draft, const int32_t *tokens,
+                                const int32_t *parent, int32_t B, int32_t T, int32_t V,
+                                double inv_tau, double inv_tau_q, const double *uniforms,
+                                int32_t max_children, int32_t *accept_len, int32_t *path,
+                                int32_t *out_tokens, void *ws, int32_t *dev_status,
+                                hipStream_t stream) {
+  const SampledWs w = sampled_ws_layout(B, T, V);
+  char *base = (char *)ws;
+  SampledArgs a{logits, draft, tokens, parent, B, T, V, n_chunks_of(V), max_children, inv_tau,
+                inv_tau_q, uniforms, (RejStat *)(base + w.pstat), (RejStat *)(base + w.qstat),
+                (double *)(base + w.wpart), (SampledRow *)(base + w.state),
+                (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
+                (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status};
+  const int64_t rows = (int64_t)B * T;
+  int cpw = 4;
+  while (cpw > 1 && rows * ((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw)) < 2048)
+    cpw /= 2;
+  dim3 grid((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw), (unsigned)rows);
+#define EV_LAUNCH_SAMPLED(K, C) hipLaunchKernelGGL((K<C>), grid, dim3(256), 0, stream, a)
+  if (cpw == 4) EV_LAUNCH_SAMPLED(sampled_stats_kernel, 4);
+  else if (cpw == 2) EV_LAUNCH_SAMPLED(sampled_stats_kernel, 2);
+  else EV_LAUNCH_SAMPLED(sampled_stats_kernel, 1);
+  for (int r = 0; r <= max_children; ++r) {
+    if (cpw == 4) EV_LAUNCH_SAMPLED(sampled_round_kernel, 4);
+    else if (cpw == 2) EV_LAUNCH_SAMPLED(sampled_round_kernel, 2);
+    else EV_LAUNCH_SAMPLED(sampled_round_kernel, 1);
+  }
+#undef EV_LAUNCH_SAMPLED
+  return launch_status();
+}
 }  // namespace ev
 
 EV_API size_t ev_accept_workspace(int32_t B, int32_t T, int32_t V) {
@@ -640,4 +987,32 @@ EV_API ev_status ev_accept_rejection(const float *logits, const int32_t *tokens,
   if (!uniforms) return EV_ERR_NULL;
   return ev::launch_accept(true, logits, tokens, parent, B, T, V, 1.0 / (double)temperature,
                            uniforms, accept_len, path, out_tokens, ws, dev_status, stream);
+}
+
+EV_API size_t ev_accept_sampled_workspace(int32_t B, int32_t T, int32_t V) {
+  if (B < 1 || T < 1 || V < 1) return 0;
+  return ev::sampled_ws_layout(B, T, V).total;
+}
+
+EV_API ev_status ev_accept_sampled(const float *logits, const float *draft_logits,
+                                   const int32_t *tokens, const int32_t *parent, int32_t B,
+                                   int32_t T, int32_t V, float temperature,
+                                   float draft_temperature, const double *uniforms,
+                                   int32_t max_children, int32_t *accept_len, int32_t *path,
+                                   int32_t *out_tokens, void *ws, size_t ws_bytes,
+                                   int32_t *dev_status, hipStream_t stream) {
+  if (!(temperature > 0.f) || !isfinite(temperature)) return EV_ERR_ARG;
+  if (!(draft_temperature > 0.f) || !isfinite(draft_temperature)) return EV_ERR_ARG;
+  if (B < 0 || T < 1 || T > ev::kMaxNodes || V < 1 || V > 64 * ev::kChunkRegs * ev::kChunk)
+    return EV_ERR_SHAPE;
+  if ((int64_t)B * T > ev::kMaxRows || max_children < 0 || max_children >= T + 1)
+    return EV_ERR_SHAPE;
+  if (B == 0) return EV_OK;
+  if (!logits || !draft_logits || !tokens || !parent || !uniforms || !accept_len || !path ||
+      !out_tokens)
+    return EV_ERR_NULL;
+  if (!ws || ws_bytes < ev::sampled_ws_layout(B, T, V).total) return EV_ERR_WORKSPACE;
+  return ev::launch_sampled(logits, draft_logits, tokens, parent, B, T, V,
+                            1.0 / (double)temperature, 1.0 / (double)draft_temperature, uniforms,
+                            max_children, accept_len, path, out_tokens, ws, dev_status, stream);
 }

@@ -14,6 +14,7 @@ EV_API const char *ev_status_string(ev_status s) {
     case EV_DERR_BOUNDS: return "prefix and tree do not fit the cache, or a block id is out of range";
     case EV_DERR_TOKEN: return "a draft token id is outside [0, V)";
     case EV_DERR_PATH: return "path / accept_len is not a valid root path";
+    case EV_DERR_WIDTH: return "a node has more children than max_children";
     default: return "unknown status";
   }
 }
