@@ -167,8 +167,9 @@ size_t ev_accept_sampled_workspace(int32_t B, int32_t T, int32_t V);
  *   renormalised).  When no child is accepted the emitted token is the inverse-CDF draw of
  *   W in ascending token id with t = uniforms[b][0] * Z.
  *   max_children: (host) bound on the children of any node, 0 <= max_children <= T; it
- *   fixes the work (one pass over the undecided rows per child tested).  A node with more
- *   children sets EV_DERR_WIDTH.
+ *   fixes the number of launches: one pass over every row (which also takes each node's
+ *   first decision), then max_children passes over the rows still undecided.  A node
+ *   with more children sets EV_DERR_WIDTH.
  *   Outputs as for ev_accept_greedy.  EV_ERR_ARG unless both temperatures are finite and
  *   > 0. */
 ev_status ev_accept_sampled(const float *logits, const float *draft_logits, const int32_t *tokens,

@@ -618,8 +618,11 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
 // child is accepted the bonus token is drawn from W.  Z changes with every rejection, so
 // each rejection needs one more pass over the node's row: the work runs in rounds, one
 // launch per round, every launch one pass over the rows still being decided (a row
-// whose node is settled returns at once).  A node with c children is settled by round
-// c + 1, so the caller's bound on children per node fixes the number of launches.
+// whose node is settled returns at once).  The statistics launch already takes each
+// node's first decision: with s = 0 the residual is p itself, whose mass per chunk
+// follows from the chunk statistics, so leaves draw their bonus and first children are
+// tested there.  A node with c children is therefore settled by round c, and the
+// caller's bound on children per node fixes the number of launches.
 struct SampledRow {
   double Mp, Sp, Mq, Sq;                 // row statistics of the target and draft rows
   double s;                              // residual shift after the rejections so far
@@ -666,19 +669,6 @@ inline SampledWs sampled_ws_layout(int B, int T, int V) {
   return w;
 }
 
-// Row statistics of one distribution from its chunk statistics (published this launch).
-__device__ inline void observed_row_stats(const RejStat *st, int nc, const double *tab, double &M,
-                                          double &S) {
-  const int lane = threadIdx.x & 63;
-  RejStat cs[kChunkRegs];
-#pragma unroll
-  for (int r = 0; r < kChunkRegs; ++r) {
-    const int c = lane + 64 * r;
-    cs[r] = c < nc ? RejStat{observe(&st[c].M), observe(&st[c].S)} : RejStat{-INFINITY, 0.0};
-  }
-  row_stats_regs(cs, tab, M, S);
-}
-
 // Residual weight of logit pair (target, draft) under row state st (shift s).
 __device__ inline double residual_weight(float lp, float lq, const SampledArgs &a,
                                          const SampledRow &st, double inv_sp, double inv_sq,
@@ -688,109 +678,13 @@ __device__ inline double residual_weight(float lp, float lq, const SampledArgs &
   return fmax(0.0, fma(-st.s, q, p));
 }
 
-// Statistics launch: per-chunk (M, S) of both rows; the row's last workgroup validates
-// the tree and sets up the row state.
-template <int CPW>
-__global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
-  __shared__ double tab[64];
-  __shared__ int s_last;
-  fill_exp_table(tab);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row = blockIdx.y;
-  const int nc = a.n_chunks;
-  const int b = (int)(row / a.T), n = (int)(row % a.T);
-  __syncthreads();
-  const float *lp = a.logits + row * a.V;
-  const float *lq = a.draft + row * a.V;
-  const bool vec_ok = (a.V & 3) == 0;
-  int idx_unused[16];
-  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
-#pragma unroll
-  for (int m = 0; m < CPW; ++m) {
-    const int c = c0 + kChunksPerWG * m;
-    if (c >= nc) continue;
-    float vp[16], vq[16];
-    load_chunk(lp, a.V, c * kChunk, vec_ok, vp, idx_unused);
-    load_chunk(lq, a.V, c * kChunk, vec_ok, vq, idx_unused);
-    float bp = -INFINITY, bq = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      bp = fmaxf(bp, vp[e]);
-      bq = fmaxf(bq, vq[e]);
-    }
-    const double Mp = (double)wave_max_f(bp) * a.inv_tau;
-    const double Mq = (double)wave_max_f(bq) * a.inv_tau_q;
-    double sp = 0.0, sq = 0.0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sp += exp_nonpos(shifted(vp[e], a.inv_tau, Mp), tab);
-      sq += exp_nonpos(shifted(vq[e], a.inv_tau_q, Mq), tab);
-    }
-    sp = wave_sum(sp);
-    sq = wave_sum(sq);
-    if (lane == 0) {
-      publish(&a.pstat[row * nc + c].M, Mp);
-      publish(&a.pstat[row * nc + c].S, sp);
-      publish(&a.qstat[row * nc + c].M, Mq);
-      publish(&a.qstat[row * nc + c].S, sq);
-    }
-  }
-  if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
-  if (wave == 0) {
-    const bool live = lane < a.T;
-    const int par = live ? a.parent[(int64_t)b * a.T + lane] : -2;
-    const int tok = live ? a.tokens[(int64_t)b * a.T + lane] : -1;
-    const bool pok = !live || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
-    bool ok = true;
-    if (__any(!pok)) {
-      if (lane == 0) report(a.dev_status, EV_DERR_PARENT);
-      ok = false;
-    } else if (__any(live && lane > 0 && (tok < 0 || tok >= a.V))) {
-      if (lane == 0) report(a.dev_status, EV_DERR_TOKEN);
-      ok = false;
-    } else if (__popcll(__ballot(live && par == n)) > a.max_children) {
-      if (lane == 0) report(a.dev_status, EV_DERR_WIDTH);
-      ok = false;
-    }
-    SampledRow st{};
-    if (ok) {
-      observed_row_stats(a.pstat + row * nc, nc, tab, st.Mp, st.Sp);
-      observed_row_stats(a.qstat + row * nc, nc, tab, st.Mq, st.Sq);
-    }
-    if (lane == 0) {
-      st.s = 0.0;
-      st.active = ok ? 1 : 0;
-      st.tried = 0;
-      a.state[row] = st;
-      if (!ok) publish(&a.node_out[row], pack_node(-2, 0));
-      s_last = ok ? 0 : 1;               // an invalid tree settles the row at once
-    }
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // the sequence is skipped by the walk (its outputs are left as they were)
-  if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
-  if (wave == 0) {
-    const int tok = lane < a.T ? a.tokens[(int64_t)b * a.T + lane] : -1;
-    finish_sequence(a, b, tok);
-  }
-}
-
-// Bonus token of a node from the residual W of this round: the chunk whose cumulative
-// residual mass first exceeds t is found from the per-chunk masses (wp, lane-strided),
+// Bonus token of a node from its residual W: the chunk whose cumulative residual mass
+// first exceeds t is found from the chunk masses (lane-strided as in row_stats_regs),
 // then that chunk is scanned element by element (one wavefront).
-__device__ int sampled_draw(const SampledArgs &a, int64_t row, const SampledRow &st, double t,
-                            const double *tab) {
+__device__ int sampled_draw(const SampledArgs &a, int64_t row, const SampledRow &st,
+                            const double (&mass)[kChunkRegs], double t, const double *tab) {
   const int lane = threadIdx.x & 63;
   const int nc = a.n_chunks;
-  const double *wp = a.wpart + row * nc;
-  double mass[kChunkRegs];
-#pragma unroll
-  for (int r = 0; r < kChunkRegs; ++r) {
-    const int c = lane + 64 * r;
-    mass[r] = c < nc ? observe(&wp[c]) : 0.0;
-  }
   int cstar = -1;
   double cbefore = -INFINITY, base = 0.0;
 #pragma unroll
@@ -841,9 +735,179 @@ __device__ int sampled_draw(const SampledArgs &a, int64_t row, const SampledRow 
   }
 }
 
+// What the decision of node n needs besides the residual, loaded by wave 0 of every
+// workgroup before its pass over the row so that these loads overlap the pass: lane i
+// holds node i's parent and token; then the next untested child, the two logits at its
+// drafted token, and the uniforms of the child test and of the bonus draw.  The token
+// index is clamped for the load (the tree is validated only after the pass).
+struct NodeView {
+  int par, tok;                          // of node `lane`
+  int c;                                 // next untested child of n, -1 if none
+  float lpx, lqx;                        // target and draft logits at c's token
+  double uc, u0;
+};
+
+__device__ inline NodeView node_view(const SampledArgs &a, int64_t row, int b, int n,
+                                     int tried) {
+  const int lane = threadIdx.x & 63;
+  const bool live = lane < a.T;
+  NodeView v;
+  v.par = live ? a.parent[(int64_t)b * a.T + lane] : -2;
+  v.tok = live ? a.tokens[(int64_t)b * a.T + lane] : -1;
+  uint64_t kids = __ballot(live && v.par == n);
+  for (int i = 0; i < tried; ++i) kids &= kids - 1;     // children tested already
+  v.c = kids ? __ffsll((unsigned long long)kids) - 1 : -1;
+  const int x = min(max(__shfl(v.tok, max(v.c, 0)), 0), a.V - 1);
+  v.lpx = a.logits[row * a.V + x];
+  v.lqx = a.draft[row * a.V + x];
+  v.uc = a.uniforms[(int64_t)b * a.T + max(v.c, 0)];
+  v.u0 = a.uniforms[(int64_t)b * a.T];
+  return v;
+}
+
+// Decision of node n (row `row`) once the residual at shift st.s is known through its
+// chunk masses: the next untested child is accepted or rejected, or, with no child left,
+// the bonus token is drawn.  One wavefront.  Returns whether the node is settled (its
+// node_out published); a rejection instead advances the row state.
+__device__ bool sampled_decide(const SampledArgs &a, int64_t row, const SampledRow &st,
+                               const NodeView &v, const double (&mass)[kChunkRegs],
+                               const double *tab) {
+  const int lane = threadIdx.x & 63;
+  double Z = 0.0;
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) Z += mass[r];
+  Z = wave_sum(Z);
+  int next = -1, bonus = -1;
+  if (v.c >= 0) {
+    const double inv_sp = 1.0 / st.Sp, inv_sq = 1.0 / st.Sq;
+    const double qx = exp_nonpos(shifted(v.lqx, a.inv_tau_q, st.Mq), tab) * inv_sq;
+    const double wx = residual_weight(v.lpx, v.lqx, a, st, inv_sp, inv_sq, tab);
+    if (!(v.uc * qx * Z < wx)) {
+      if (lane == 0) {
+        SampledRow nst = st;
+        nst.s = st.s + Z;
+        nst.tried = st.tried + 1;
+        nst.active = 1;
+        a.state[row] = nst;                // read by the next launch
+      }
+      return false;
+    }
+    next = v.c;
+  } else {
+    bonus = sampled_draw(a, row, st, mass, v.u0 * Z, tab);
+  }
+  if (lane == 0) {
+    SampledRow nst = st;
+    nst.active = 0;
+    a.state[row] = nst;
+    publish(&a.node_out[row], pack_node(next, bonus));
+  }
+  return true;
+}
+
+// Statistics launch: per-chunk (M, S) of both rows; the row's last workgroup validates
+// the tree and sets up the row state.
+template <int CPW>
+__global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
+  __shared__ double tab[64];
+  __shared__ int s_last;
+  fill_exp_table(tab);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.y;
+  const int nc = a.n_chunks;
+  const int b = (int)(row / a.T), n = (int)(row % a.T);
+  NodeView v{};
+  if (wave == 0) v = node_view(a, row, b, n, 0);
+  __syncthreads();
+  const float *lp = a.logits + row * a.V;
+  const float *lq = a.draft + row * a.V;
+  const bool vec_ok = (a.V & 3) == 0;
+  int idx_unused[16];
+  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
+#pragma unroll
+  for (int m = 0; m < CPW; ++m) {
+    const int c = c0 + kChunksPerWG * m;
+    if (c >= nc) continue;
+    float vp[16], vq[16];
+    load_chunk(lp, a.V, c * kChunk, vec_ok, vp, idx_unused);
+    load_chunk(lq, a.V, c * kChunk, vec_ok, vq, idx_unused);
+    float bp = -INFINITY, bq = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      bp = fmaxf(bp, vp[e]);
+      bq = fmaxf(bq, vq[e]);
+    }
+    const double Mp = (double)wave_max_f(bp) * a.inv_tau;
+    const double Mq = (double)wave_max_f(bq) * a.inv_tau_q;
+    double sp = 0.0, sq = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sp += exp_nonpos(shifted(vp[e], a.inv_tau, Mp), tab);
+      sq += exp_nonpos(shifted(vq[e], a.inv_tau_q, Mq), tab);
+    }
+    sp = wave_sum(sp);
+    sq = wave_sum(sq);
+    if (lane == 0) {
+      publish(&a.pstat[row * nc + c].M, Mp);
+      publish(&a.pstat[row * nc + c].S, sp);
+      publish(&a.qstat[row * nc + c].M, Mq);
+      publish(&a.qstat[row * nc + c].S, sq);
+    }
+  }
+  if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
+  if (wave == 0) {
+    const bool live = lane < a.T;
+    const int par = v.par, tok = v.tok;
+    const bool pok = !live || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+    bool ok = true;
+    if (__any(!pok)) {
+      if (lane == 0) report(a.dev_status, EV_DERR_PARENT);
+      ok = false;
+    } else if (__any(live && lane > 0 && (tok < 0 || tok >= a.V))) {
+      if (lane == 0) report(a.dev_status, EV_DERR_TOKEN);
+      ok = false;
+    } else if (__popcll(__ballot(live && par == n)) > a.max_children) {
+      if (lane == 0) report(a.dev_status, EV_DERR_WIDTH);
+      ok = false;
+    }
+    if (ok) {
+      // Row statistics of both rows.  Before any rejection (s = 0) the residual is p, so
+      // its chunk masses follow from the chunk statistics and the first decision needs
+      // no further pass over the row.
+      RejStat cp[kChunkRegs], cq[kChunkRegs];
+#pragma unroll
+      for (int r = 0; r < kChunkRegs; ++r) {
+        const int c = lane + 64 * r;
+        const RejStat *sp = a.pstat + row * nc + c, *sq = a.qstat + row * nc + c;
+        cp[r] = c < nc ? RejStat{observe(&sp->M), observe(&sp->S)} : RejStat{-INFINITY, 0.0};
+        cq[r] = c < nc ? RejStat{observe(&sq->M), observe(&sq->S)} : RejStat{-INFINITY, 0.0};
+      }
+      SampledRow st{};
+      row_stats_regs(cp, tab, st.Mp, st.Sp);
+      row_stats_regs(cq, tab, st.Mq, st.Sq);
+      const double inv_sp = 1.0 / st.Sp;
+      double mass[kChunkRegs];
+#pragma unroll
+      for (int r = 0; r < kChunkRegs; ++r)
+        mass[r] = cp[r].S > 0.0 ? cp[r].S * exp_nonpos(cp[r].M - st.Mp, tab) * inv_sp : 0.0;
+      const bool done = sampled_decide(a, row, st, v, mass, tab);
+      if (lane == 0) s_last = done ? 1 : 0;
+    } else if (lane == 0) {
+      a.state[row] = SampledRow{};       // inactive
+      publish(&a.node_out[row], pack_node(-2, 0));
+      s_last = 1;                        // an invalid tree settles the row at once
+    }
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // the sequence is skipped by the walk (its outputs are left as they were)
+  if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
+  if (wave == 0) finish_sequence(a, b, v.tok);
+}
+
 // One round: every row still being decided takes one pass over its target and draft
-// logits for the residual mass Z at its current shift; its last workgroup then tests the
-// next child (or draws the bonus when every child has been rejected).
+// logits for the residual mass at its current shift; its last workgroup then decides.
 template <int CPW>
 __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
   __shared__ double tab[64];
@@ -856,6 +920,8 @@ __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
   const int wave = threadIdx.x >> 6;
   const int nc = a.n_chunks;
   const int b = (int)(row / a.T), n = (int)(row % a.T);
+  NodeView v{};
+  if (wave == 0) v = node_view(a, row, b, n, st.tried);
   __syncthreads();
   const float *lp = a.logits + row * a.V;
   const float *lq = a.draft + row * a.V;
@@ -878,52 +944,19 @@ __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
   }
   if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
   if (wave == 0) {
-    double Z = 0.0;
-    for (int c = lane; c < nc; c += 64) Z += observe(&a.wpart[row * nc + c]);
-    Z = wave_sum(Z);
-    const bool live = lane < a.T;
-    const int par = live ? a.parent[(int64_t)b * a.T + lane] : -2;
-    const int tok = live ? a.tokens[(int64_t)b * a.T + lane] : -1;
-    uint64_t kids = __ballot(live && par == n);
-    for (int i = 0; i < st.tried; ++i) kids &= kids - 1;   // children tested in earlier rounds
-    int next = -1, bonus = -1;
-    bool done = true;
-    if (kids) {
-      const int c = __ffsll((unsigned long long)kids) - 1;
-      const int x = __shfl(tok, c);
-      const float lpx = lp[x], lqx = lq[x];
-      const double qx = exp_nonpos(shifted(lqx, a.inv_tau_q, st.Mq), tab) * inv_sq;
-      const double wx = residual_weight(lpx, lqx, a, st, inv_sp, inv_sq, tab);
-      const double u = a.uniforms[(int64_t)b * a.T + c];
-      if (u * qx * Z < wx) {
-        next = c;
-      } else {
-        done = false;
-        if (lane == 0) {
-          SampledRow nst = st;
-          nst.s = st.s + Z;
-          nst.tried = st.tried + 1;
-          a.state[row] = nst;              // read by the next launch
-        }
-      }
-    } else {
-      const double u0 = a.uniforms[(int64_t)b * a.T];
-      bonus = sampled_draw(a, row, st, u0 * Z, tab);
+    double mass[kChunkRegs];
+#pragma unroll
+    for (int r = 0; r < kChunkRegs; ++r) {
+      const int c = lane + 64 * r;
+      mass[r] = c < nc ? observe(&a.wpart[row * nc + c]) : 0.0;
     }
-    if (done && lane == 0) {
-      a.state[row].active = 0;
-      publish(&a.node_out[row], pack_node(next, bonus));
-    }
-    if (__shfl(done ? 1 : 0, 0)) s_last = 1;
-    else s_last = 0;
+    const bool done = sampled_decide(a, row, st, v, mass, tab);
+    if (lane == 0) s_last = done ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
   if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
-  if (wave == 0) {
-    const int tok = lane < a.T ? a.tokens[(int64_t)b * a.T + lane] : -1;
-    finish_sequence(a, b, tok);
-  }
+  if (wave == 0) finish_sequence(a, b, v.tok);
 }
 
 static ev_status launch_sampled(const float *logits, const float *draft, const int32_t *tokens,
@@ -948,7 +981,7 @@ static ev_status launch_sampled(const float *logits, const float *draft, const i
   if (cpw == 4) EV_LAUNCH_SAMPLED(sampled_stats_kernel, 4);
   else if (cpw == 2) EV_LAUNCH_SAMPLED(sampled_stats_kernel, 2);
   else EV_LAUNCH_SAMPLED(sampled_stats_kernel, 1);
-  for (int r = 0; r <= max_children; ++r) {
+  for (int r = 0; r < max_children; ++r) {
     if (cpw == 4) EV_LAUNCH_SAMPLED(sampled_round_kernel, 4);
     else if (cpw == 2) EV_LAUNCH_SAMPLED(sampled_round_kernel, 2);
     else EV_LAUNCH_SAMPLED(sampled_round_kernel, 1);
