@@ -8,6 +8,7 @@ is involved) of what one verification pass of a drafted token tree computes:
   accept.py     greedy longest-matching walk and rejection-sampling walk
   stochastic.py rejection-sampling walk for drafts sampled from a draft distribution
   compact.py    accepted-path KV compaction
+  tree_build.py dynamic draft-tree construction (entropy-guided beam expansion)
 
 It shares no code with the HIP library and imports nothing from it.  Only the test
 suite, the package's smoke check and the benchmark's CPU-baseline leg may import it;
@@ -32,9 +33,10 @@ from .accept import (greedy_walk, greedy_batch, target_probs, rejection_walk,
                      rejection_batch)
 from .compact import kv_compact
 from .stochastic import stochastic_walk, stochastic_batch
+from .tree_build import TreeBuilder, build_batch, entropy
 
 __all__ = [
     "tree_mask", "tree_mask_batch", "tree_attention", "tree_attention_batch", "gather_paged",
     "greedy_walk", "greedy_batch", "target_probs", "rejection_walk", "rejection_batch",
-    "kv_compact", "stochastic_walk", "stochastic_batch",
+    "kv_compact", "stochastic_walk", "stochastic_batch", "TreeBuilder", "build_batch", "entropy",
 ]

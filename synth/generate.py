@@ -265,3 +265,25 @@ def sampled_drafts(inp: Inputs, draft_tau: float = 0.8, noise: float = 1.0):
                 gumbel = -np.log(-np.log(rng.random(V)))
             tokens[b, c] = int(np.argmax(draft[b, a].astype(np.float64) * inv + gumbel))
     return draft, tokens
+
+
+def draft_tree_logits(B: int, V: int, depths: int = 6, beam: int = 8,
+                      sharpness: Optional[tuple] = None, seed: int = 3000):
+    """Stand-in for the drafter's outputs while a draft tree grows (no trained head exists).
+
+    Returns a list of `depths` float32 arrays [B][beam][V]; row w of sequence b at depth d
+    is the drafter's next-token logits after frontier slot w (depth 0: slot 0 is the root).
+    Each row is s * N(0, 1) with its own sharpness s, drawn uniformly from `sharpness`.
+    A sharp row has a low-entropy distribution and a blunt one a flat distribution, so
+    the tree grows deep in some places and wide in others.  The default range spreads
+    the perplexity over about 1 to 60 at the vocabulary size given.
+    """
+    if sharpness is None:
+        sharpness = (4.0, 9.0) if V >= 65536 else (6.0, 16.0)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, B, V, depths, beam])))
+    out = []
+    for _ in range(depths):
+        s = rng.uniform(sharpness[0], sharpness[1], size=(B, beam, 1)).astype(np.float32)
+        z = rng.standard_normal((B, beam, V), dtype=np.float32)
+        out.append((s * z).astype(np.float32))
+    return out
