@@ -189,6 +189,54 @@ ev_status ev_kv_compact(const ev_kv_desc *kv, const int32_t *prefix_len, const i
                         const int32_t *accept_len, int32_t B, int32_t T,
                         int32_t *new_len, int32_t *dev_status, hipStream_t stream);
 
+/* ---- Draft-tree construction ([TR] sec. 2: sequence diagram, "Dynamic Tree-Attention
+ * Masking") ----
+ * The drafter grows the tree depth by depth: after each expansion it runs on the new
+ * frontier and hands its next-token logits back.  Frontier node n, with
+ * q_n = softmax(draft_logits_n / temperature) (float64 as in ev_accept_rejection), gets
+ * k_n = min(k_max, max(1, floor(exp(H(q_n)) + 1/2))) children, where H is the entropy in
+ * nats.  They are its k_n most probable tokens; equal logits go to the lower token id.
+ * A node's value is the product of q along its path (root 1).  Each depth keeps the
+ * `beam` best new candidates as the next frontier.  The tree is the root plus the
+ * n_nodes - 1 best candidates of all depths, numbered by depth and then by value rank.
+ * Equal values go to the lower candidate id: depth first, then frontier slot, then
+ * child rank.  A child's value never exceeds its parent's, so every chosen node's
+ * ancestors are chosen too.
+ * The workspace carries the tree under construction from call to call: zero-fill it
+ * before its first use (it is left with its counters at zero), and use one workspace
+ * per tree being built at a time. */
+
+/* Bytes of workspace for B sequences, beam width `beam` (1..8) and V-token logit rows. */
+size_t ev_draft_tree_workspace(int32_t B, int32_t beam, int32_t V);
+
+/* ev_draft_tree_expand — one depth of the beam expansion.  Calls go depth = 0, 1, 2, ...
+ * (< 16) on the same workspace.  Depth 0 expands the root.
+ *   draft_logits [B][beam][V] float: row w is the drafter's logits after frontier slot w
+ *   of this depth (depth 0: row 0 is the root's; rows at or beyond the frontier count are
+ *   not read).
+ *   k_max in 1..8: most children per node.
+ *   Outputs, the next frontier, for the drafter: frontier_tokens [B][beam] (its tokens,
+ *   best first), frontier_slots [B][beam] (the slot of each one's parent at this depth),
+ *   both -1 beyond frontier_count [B].
+ *   EV_ERR_ARG unless temperature is finite and > 0.  EV_DERR_TOKEN when NaN logits
+ *   leave fewer real tokens than a node's width (the token is clamped to V - 1). */
+ev_status ev_draft_tree_expand(const float *draft_logits, int32_t B, int32_t beam, int32_t V,
+                               int32_t depth, float temperature, int32_t k_max,
+                               int32_t *frontier_tokens, int32_t *frontier_slots,
+                               int32_t *frontier_count, void *ws, size_t ws_bytes,
+                               int32_t *dev_status, hipStream_t stream);
+
+/* ev_draft_tree_finalize — the tree after the expansions made so far.  B, beam and V are
+ * those of the expansions.
+ *   root_tokens [B]: the last committed token of each sequence (node 0's token).
+ *   Outputs parent [B][n_nodes] (parent[0] = -1, 0 <= parent[i] < i) and tokens
+ *   [B][n_nodes], both -1 beyond tree_size [B] (at most n_nodes, 1..64); ready for
+ *   ev_tree_mask_build and the verification pass. */
+ev_status ev_draft_tree_finalize(const int32_t *root_tokens, int32_t B, int32_t beam, int32_t V,
+                                 int32_t n_nodes, int32_t *parent, int32_t *tokens,
+                                 int32_t *tree_size, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* (host) Static description of a status code. */
 const char *ev_status_string(ev_status s);
 

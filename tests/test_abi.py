@@ -96,6 +96,24 @@ def test_host_errors_return_before_launch(lib):
     assert samp(draft=None) == 1
     assert samp(nbytes=100) == 4
     assert lib.ev_accept_sampled_workspace(1, 64, 128256) >= 2 * 65536 * 4 + 64 * 126 * 40
+    exp = lambda B=1, W=8, V=1000, depth=0, tau=1.0, k=8, ws=P, nbytes=10**8, logits=P: \
+        lib.ev_draft_tree_expand(logits, B, W, V, depth, tau, k, P, P, P, ws, nbytes, None, None)
+    assert exp(tau=0.0) == 5
+    assert exp(tau=float("inf")) == 5
+    assert exp(W=0) == 2 and exp(W=9) == 2
+    assert exp(k=0) == 2 and exp(k=9) == 2
+    assert exp(depth=-1) == 2 and exp(depth=16) == 2
+    assert exp(V=0) == 2
+    assert exp(logits=None) == 1
+    assert exp(nbytes=100) == 4
+    assert exp(B=0, logits=None) == 0               # empty batch
+    fin = lambda B=1, W=8, V=1000, n=64, nbytes=10**8: lib.ev_draft_tree_finalize(
+        P, B, W, V, n, P, P, P, P, nbytes, None)
+    assert fin(n=0) == 2 and fin(n=65) == 2
+    assert fin(W=9) == 2
+    assert fin(nbytes=100) == 4
+    assert lib.ev_draft_tree_workspace(1, 9, 100) == 0
+    assert lib.ev_draft_tree_workspace(16, 8, 128256) % 256 == 0
     assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=0)), P, P, P, 1, 8, P, None, None) == 2
     assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=2, layer_stride=0)), P, P, P, 1, 8, P, None, None) == 2
     assert lib.ev_kv_compact(ctypes.byref(d), None, P, P, 1, 8, P, None, None) == 1

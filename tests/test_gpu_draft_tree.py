@@ -1,0 +1,125 @@
+"""GPU parity of draft-tree construction (ev_draft_tree_expand / ev_draft_tree_finalize)
+against the oracle.
+
+Bar: every frontier (tokens, parent slots, counts) and the final tree (parent, tokens,
+size) identical to the oracle's on the same float32 draft logits.  On random inputs no
+compared decision may be a rounding tie: width margins > 1e-9 (relative to the
+perplexity) and value gaps > 1e-12 (relative).  Flat rows exercise exact ties, which
+both sides break by candidate id.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_attention_verification_ev_amd as ev
+from synth import draft_tree_logits
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_gpu(depth_logits, k_max, tau, n_nodes, root_tokens, ws=None):
+    B, W, V = depth_logits[0].shape
+    if ws is None:
+        ws = torch.zeros(ev.ev_draft_tree_workspace(B, W, V), dtype=torch.uint8, device="cuda")
+    fronts = []
+    for d, dl in enumerate(depth_logits):
+        t = torch.from_numpy(np.ascontiguousarray(dl)).cuda()
+        ft, fs, fc = ev.ev_draft_tree_expand(t, d, tau, k_max, ws, check=True)
+        fronts.append((ft.cpu().numpy(), fs.cpu().numpy(), fc.cpu().numpy()))
+    root = torch.from_numpy(np.asarray(root_tokens, np.int32)).cuda()
+    p, tk, n = ev.ev_draft_tree_finalize(root, W, V, n_nodes, ws)
+    return p.cpu().numpy(), tk.cpu().numpy(), n.cpu().numpy(), fronts
+
+
+def compare(depth_logits, k_max, tau, n_nodes, check_margins=True, ws=None):
+    B, W, V = depth_logits[0].shape
+    root = np.arange(B, dtype=np.int32) % V
+    gp, gt, gn, gf = run_gpu(depth_logits, k_max, tau, n_nodes, root, ws)
+    rp, rt, rn, rf, margins = oracle.build_batch(depth_logits, W, k_max, tau, n_nodes, root)
+    if check_margins:
+        for m in margins:
+            assert min(x for k, x in m if k == "width") > 1e-9
+            assert min((x for k, x in m if k != "width"), default=1.0) > 1e-12
+    for d in range(len(depth_logits)):
+        for g, r in zip(gf[d], rf[d]):
+            assert np.array_equal(g, r), d
+    assert np.array_equal(gn, rn)
+    assert np.array_equal(gp, rp)
+    assert np.array_equal(gt, rt)
+
+
+CASES = [
+    ("B3_V2000", 3, 2000, 6, 8, 8, 64),
+    ("B2_V5001_odd", 2, 5001, 6, 8, 8, 64),
+    ("B4_V4096_beam3_k5_n20", 4, 4096, 5, 3, 5, 20),
+    ("B2_V12_tiny", 2, 12, 4, 8, 8, 64),
+    ("B1_V128256", 1, 128256, 6, 8, 8, 64),
+    ("B4_V128256", 4, 128256, 6, 8, 8, 64),
+]
+
+
+@pytest.mark.parametrize("name,B,V,depths,beam,k_max,n_nodes", CASES, ids=[c[0] for c in CASES])
+def test_draft_tree_matches_oracle(name, B, V, depths, beam, k_max, n_nodes):
+    sharp = (0.3, 2.0) if V < 100 else None
+    dl = draft_tree_logits(B, V, depths=depths, beam=beam, sharpness=sharp)
+    compare(dl, k_max, 1.0, n_nodes)
+
+
+def test_draft_tree_temperature():
+    dl = draft_tree_logits(2, 3000, depths=4, beam=8, seed=77)
+    compare(dl, 8, 0.6, 64)
+
+
+def test_flat_rows_golden_on_gpu():
+    """Exact ties everywhere: the tie order (lower candidate id) must match by hand."""
+    g = json.load(open(os.path.join(GOLDEN, "draft_tree_flat.json")))
+    rows = [np.zeros((1, g["beam"], g["V"]), np.float32) for _ in range(g["depths"])]
+    p, t, n, fronts = run_gpu(rows, g["k_max"], 1.0, g["n_nodes"], [g["root_token"]])
+    assert p[0].tolist() == g["parent"]
+    assert t[0].tolist() == g["tokens"]
+    assert n[0] == g["n_nodes"]
+    for d in range(g["depths"]):
+        assert fronts[d][0][0].tolist() == g["frontier_tokens"][d]
+        assert fronts[d][1][0].tolist() == g["frontier_slots"][d]
+
+
+def test_one_hot_rows_make_a_chain_on_gpu():
+    depths, V = 6, 70000
+    rng = np.random.default_rng(3)
+    spikes = rng.integers(0, V, size=(depths, 8))
+    rows = []
+    for d in range(depths):
+        r = np.zeros((1, 8, V), np.float32)
+        r[0, np.arange(8), spikes[d]] = 60.0
+        rows.append(r)
+    p, t, n, _ = run_gpu(rows, 8, 1.0, 64, [1])
+    assert n[0] == depths + 1
+    assert p[0, :depths + 1].tolist() == [-1] + list(range(depths))
+    assert t[0, 1:depths + 1].tolist() == [int(spikes[d, 0]) for d in range(depths)]
+
+
+@pytest.mark.parametrize("m", [2, 3, 7, 12])
+def test_m_equal_tokens_give_m_children_on_gpu(m):
+    V = 3000
+    rng = np.random.default_rng(m)
+    row = np.full((1, 8, V), -1e4, np.float32)
+    top = np.sort(rng.choice(V, size=m, replace=False))
+    row[0, :, top] = 3.0
+    p, t, n, fronts = run_gpu([row], 8, 1.0, 64, [0])
+    k = min(m, 8)
+    assert n[0] == 1 + k
+    assert sorted(t[0, 1:1 + k].tolist()) == [int(x) for x in top[:k]]
+    assert fronts[0][2][0] == k
+
+
+def test_workspace_reuse_across_trees():
+    B, V = 2, 6000
+    ws = torch.zeros(ev.ev_draft_tree_workspace(B, 8, V), dtype=torch.uint8, device="cuda")
+    compare(draft_tree_logits(B, V, depths=6, seed=5), 8, 1.0, 64, ws=ws)
+    compare(draft_tree_logits(B, V, depths=3, seed=6), 8, 1.0, 40, ws=ws)
+    assert int(ws[:2 * 65536 * 4].count_nonzero()) == 0

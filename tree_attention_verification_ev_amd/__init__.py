@@ -31,7 +31,9 @@ STATUS_NAMES = {
 EXPORTED = (
     "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
     "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection",
-    "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact", "ev_status_string",
+    "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact",
+    "ev_draft_tree_workspace", "ev_draft_tree_expand", "ev_draft_tree_finalize",
+    "ev_status_string",
 )
 
 
@@ -77,6 +79,11 @@ def lib() -> ctypes.CDLL:
             "ev_accept_sampled": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _I32,
                                          _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_kv_compact": (_I32, [kv, _P, _P, _P, _I32, _I32, _P, _P, _P]),
+            "ev_draft_tree_workspace": (_SZ, [_I32, _I32, _I32]),
+            "ev_draft_tree_expand": (_I32, [_P, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P,
+                                            _P, _SZ, _P, _P]),
+            "ev_draft_tree_finalize": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ,
+                                              _P]),
             "ev_status_string": (ctypes.c_char_p, [_I32]),
         }
         for name, (res, args) in sigs.items():
@@ -322,6 +329,56 @@ def ev_kv_compact(kv: KvCache, prefix_len: torch.Tensor, path: torch.Tensor, acc
                                _ptr(new_len), _ptr(status), _stream(dev))
     _finish(code, "ev_kv_compact", status, check)
     return new_len
+
+
+def ev_draft_tree_workspace(B: int, beam: int, V: int) -> int:
+    return int(lib().ev_draft_tree_workspace(B, beam, V))
+
+
+def ev_draft_tree_expand(draft_logits: torch.Tensor, depth: int, temperature: float, k_max: int,
+                         ws: torch.Tensor, frontier_tokens=None, frontier_slots=None,
+                         frontier_count=None, dev_status=None, check: bool = False):
+    """One depth of the draft-tree beam expansion over draft_logits [B][beam][V]; returns
+    the next frontier (tokens [B][beam], parent slots [B][beam], counts [B]).  ws carries
+    the tree between calls (zero-filled before the first tree, one tree at a time)."""
+    _dev(draft_logits, "draft_logits", torch.float32)
+    _dev(ws, "ws", torch.uint8)
+    B, W, V = draft_logits.shape
+    dev = draft_logits.device
+    if frontier_tokens is None:
+        frontier_tokens = torch.empty((B, W), dtype=torch.int32, device=dev)
+    if frontier_slots is None:
+        frontier_slots = torch.empty((B, W), dtype=torch.int32, device=dev)
+    if frontier_count is None:
+        frontier_count = torch.empty(B, dtype=torch.int32, device=dev)
+    status = _status_word(dev, dev_status)
+    code = lib().ev_draft_tree_expand(_ptr(draft_logits), B, W, V, int(depth), float(temperature),
+                                      int(k_max), _ptr(frontier_tokens), _ptr(frontier_slots),
+                                      _ptr(frontier_count), _ptr(ws), ws.numel(), _ptr(status),
+                                      _stream(dev))
+    _finish(code, "ev_draft_tree_expand", status, check)
+    return frontier_tokens, frontier_slots, frontier_count
+
+
+def ev_draft_tree_finalize(root_tokens: torch.Tensor, beam: int, V: int, n_nodes: int,
+                           ws: torch.Tensor, parent=None, tokens=None, tree_size=None):
+    """The tree after the expansions so far; returns (parent [B][n_nodes], tokens
+    [B][n_nodes], tree_size [B])."""
+    _dev(root_tokens, "root_tokens", torch.int32)
+    _dev(ws, "ws", torch.uint8)
+    B = root_tokens.shape[0]
+    dev = root_tokens.device
+    if parent is None:
+        parent = torch.empty((B, n_nodes), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, n_nodes), dtype=torch.int32, device=dev)
+    if tree_size is None:
+        tree_size = torch.empty(B, dtype=torch.int32, device=dev)
+    code = lib().ev_draft_tree_finalize(_ptr(root_tokens), B, int(beam), int(V), int(n_nodes),
+                                        _ptr(parent), _ptr(tokens), _ptr(tree_size), _ptr(ws),
+                                        ws.numel(), _stream(dev))
+    _finish(code, "ev_draft_tree_finalize", None, False)
+    return parent, tokens, tree_size
 
 
 def ev_status_string(code: int) -> str:
