@@ -14,11 +14,11 @@
 //     depth, then by value rank.  Equal values go to the lower candidate id, and ids run
 //     depth by depth, frontier slot, child rank.
 //
-// Expansion is one launch per depth over (chunk group, frontier row) workgroups:
-//   * each wavefront streams one 1024-logit chunk and stores float64 (M_c, S_c, T_c),
-//     S_c = sum e, T_c = sum e (s - M_c), e = exp(s - M_c), s = logit / tau, and the
-//     chunk's best (logit, token);
-//   * the workgroup that completes a row merges them.  The entropy is
+// Expansion is two launches per depth:
+//   * over (chunk group, frontier row) workgroups, each wavefront streams one 1024-logit
+//     chunk and stores float64 (M_c, S_c, T_c), S_c = sum e, T_c = sum e (s - M_c),
+//     e = exp(s - M_c), s = logit / tau, and the chunk's best (logit, token);
+//   * one workgroup per frontier row then merges them.  The entropy is
 //     H = log S - T / S, so the perplexity is exp(H) = S / exp(T / S) (T <= 0).  The
 //     row's k best tokens lie in the k chunks with the best maxima, which it re-reads;
 //     their probabilities follow from (M, S);
@@ -98,24 +98,49 @@ __device__ inline bool after(float v, int i, float lv, int li) {
   return (v < lv) | ((v == lv) & (i > li));
 }
 
-// The lane's two best of its n (value, index) pairs that come after (lv, li).
+// A lane's best two (value, index) pairs, best first.
+struct Top2 {
+  float v1;
+  int i1;
+  float v2;
+  int i2;
+};
+
+__device__ inline bool beats(float v, int i, float v2, int i2) {
+  return (v > v2) | ((v == v2) & (i < i2));
+}
+
+// Best two of two best-two lists: the winner of the two leaders, then the better of the
+// losing leader and the winner's runner-up.
+__device__ inline Top2 merge_top2(const Top2 &a, const Top2 &b) {
+  const bool bw = beats(b.v1, b.i1, a.v1, a.i1);
+  const float lv = bw ? a.v1 : b.v1, sv = bw ? b.v2 : a.v2;
+  const int li = bw ? a.i1 : b.i1, si = bw ? b.i2 : a.i2;
+  const bool sw = beats(sv, si, lv, li);
+  return Top2{bw ? b.v1 : a.v1, bw ? b.i1 : a.i1, sw ? sv : lv, sw ? si : li};
+}
+
+// The lane's two best of its N (value, index) pairs that come after (lv, li), by a
+// tournament (log2 N dependent merge levels).
 template <int N>
 __device__ inline void best_two_after(const float (&v)[N], const int (&idx)[N], float lv, int li,
                                       float &v1, int &i1, float &v2, int &i2) {
-  v1 = v2 = -INFINITY;
-  i1 = i2 = INT_MAX;
+  static_assert((N & (N - 1)) == 0, "power of two");
+  Top2 t[N];
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     const bool ok = after(v[e], idx[e], lv, li);
-    const float x = ok ? v[e] : -INFINITY;
-    const int xi = ok ? idx[e] : INT_MAX;
-    const bool top = (x > v1) | ((x == v1) & (xi < i1));
-    const bool second = (x > v2) | ((x == v2) & (xi < i2));
-    v2 = top ? v1 : (second ? x : v2);
-    i2 = top ? i1 : (second ? xi : i2);
-    v1 = top ? x : v1;
-    i1 = top ? xi : i1;
+    t[e] = Top2{ok ? v[e] : -INFINITY, ok ? idx[e] : INT_MAX, -INFINITY, INT_MAX};
   }
+#pragma unroll
+  for (int n = N / 2; n >= 1; n /= 2) {
+#pragma unroll
+    for (int p = 0; p < n; ++p) t[p] = merge_top2(t[p], t[p + n]);
+  }
+  v1 = t[0].v1;
+  i1 = t[0].i1;
+  v2 = t[0].v2;
+  i2 = t[0].i2;
 }
 
 // The wave's `rounds` best pairs over the lanes' arrays, best first, into (tv, ti) (wave-
@@ -175,17 +200,21 @@ __device__ inline void wave_best_d(double &v, int &i) {
   i = bi;
 }
 
-// Merge of a completed row (the whole workgroup): statistics, width, best tokens.  The
-// row's k best tokens lie in the k chunks whose own best tokens rank first: a token in
-// any other chunk is preceded by at least k chunk maxima.  Wavefront 0 finds those
-// chunks, the four wavefronts take each one's k best (the chunks are re-read, from
-// cache), and wavefront 0 merges the at most k * k pairs.
+// Merge of a streamed row (the whole workgroup of kTreeTop wavefronts): statistics,
+// width, best tokens.  The row's k best tokens lie in the k chunks whose own best tokens
+// rank first: a token in any other chunk is preceded by at least k chunk maxima.
+// Wavefront 0 finds those chunks; wavefront j re-reads the j-th (from cache) and takes
+// its best tokens among those not after the k-th chunk maximum; each of the at most
+// k * k pairs then finds its rank among all of them.
+constexpr int kMergeThreads = 64 * kTreeTop;
+
 struct MergeShared {
   double M, S;
   int k;
+  float tv;                            // the k-th best chunk maximum
+  int ti;
   int chunk[kTreeTop];
-  float v[kTreeTop * kTreeTop];
-  int i[kTreeTop * kTreeTop];
+  uint64_t ent[kTreeTop * kTreeTop];   // the wavefronts' lists, packed
 };
 
 __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, MergeShared &sh) {
@@ -201,11 +230,8 @@ __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, M
 #pragma unroll
     for (int r = 0; r < kChunkRegs; ++r) {
       const int c = lane + 64 * r;
-      const TreeChunk *p = a.chunk + row * nc + c;
-      cs[r] = c < nc ? TreeChunk{observe(&p->M), observe(&p->S), observe(&p->T)}
-                     : TreeChunk{-INFINITY, 0.0, 0.0};
-      const GreedyStat g = c < nc ? unpack(observe(&a.top[row * nc + c]))
-                                  : GreedyStat{-INFINITY, INT_MAX};
+      cs[r] = c < nc ? a.chunk[row * nc + c] : TreeChunk{-INFINITY, 0.0, 0.0};
+      const GreedyStat g = c < nc ? unpack(a.top[row * nc + c]) : GreedyStat{-INFINITY, INT_MAX};
       cv[r] = g.val;
       ci[r] = g.idx;
       M = fmax(M, cs[r].M);
@@ -225,13 +251,18 @@ __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, M
     const double ppl = S / exp_nonpos(T / S, tab);
     const double half_up = ppl + 0.5;
     const int k = half_up >= (double)a.k_max ? a.k_max : max(1, (int)floor(half_up));
+    // the k chunks whose maxima rank first (k rounds over the lanes' chunk maxima); the
+    // k-th of them bounds the row's k best tokens: none comes after it
     float tv[kTreeTop];
     int ti[kTreeTop];
-    wave_top(cv, ci, k, tv, ti);       // the k chunks with the best maxima
+    wave_top(cv, ci, k, tv, ti);
     if (lane == 0) {
       sh.M = M;
       sh.S = S;
       sh.k = k;
+      const bool full = ti[k - 1] >= 0 && ti[k - 1] < a.V;
+      sh.tv = full ? tv[k - 1] : -INFINITY;   // fewer than k chunks: every token qualifies
+      sh.ti = full ? ti[k - 1] : INT_MAX;
 #pragma unroll
       for (int r = 0; r < kTreeTop; ++r)
         sh.chunk[r] = (r < k && ti[r] >= 0 && ti[r] < a.V) ? ti[r] / kChunk : -1;
@@ -239,81 +270,64 @@ __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, M
   }
   __syncthreads();
   const int k = sh.k;
-  const float *lr = a.logits + row * a.V;
-  const bool vec_ok = (a.V & 3) == 0;
   {
-    // wavefront w takes chunks w and w + 4 of the k in one selection
-    const int ca = wave < k ? sh.chunk[wave] : -1;
-    const int cb = wave + kChunksPerWG < k ? sh.chunk[wave + kChunksPerWG] : -1;
+    const int c = wave < k ? sh.chunk[wave] : -1;
     float tv[kTreeTop];
     int ti[kTreeTop];
-    const bool any = ca >= 0 || cb >= 0;
-    if (any) {
-      float v[2 * 16];
-      int idx[2 * 16];
-      if (ca >= 0) {
-        load_chunk(lr, a.V, ca * kChunk, vec_ok, v, idx);
-      } else {
+    int n_cand = 0;
+    if (c >= 0) {
+      float v[16];
+      int idx[16];
+      load_chunk(a.logits + row * a.V, a.V, c * kChunk, (a.V & 3) == 0, v, idx);
+      const float thv = sh.tv;
+      const int thi = sh.ti;
+      int mine = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { v[e] = -INFINITY; idx[e] = INT_MAX; }
+      for (int e = 0; e < 16; ++e) {
+        const bool keep = !after(v[e], idx[e], thv, thi);
+        v[e] = keep ? v[e] : -INFINITY;
+        idx[e] = keep ? idx[e] : INT_MAX;
+        mine += keep ? 1 : 0;
       }
-      if (cb >= 0) {
-        load_chunk(lr, a.V, cb * kChunk, vec_ok, v + 16, idx + 16);
-      } else {
+      // rounds needed: the chunk's qualifying tokens (a wave sum of `mine`, bit by bit),
+      // at most k
+      int total = 0;
 #pragma unroll
-        for (int e = 16; e < 32; ++e) { v[e] = -INFINITY; idx[e] = INT_MAX; }
-      }
-      wave_top(v, idx, k, tv, ti);
+      for (int m = 1; m <= 16; m <<= 1) total += __popcll(__ballot((mine & m) != 0)) * m;
+      n_cand = min(total, k);
+      wave_top(v, idx, n_cand, tv, ti);
     }
     if (lane == 0) {
 #pragma unroll
-      for (int r = 0; r < kTreeTop; ++r) {
-        sh.v[wave * kTreeTop + r] = any && r < k ? tv[r] : -INFINITY;
-        sh.i[wave * kTreeTop + r] = any && r < k ? ti[r] : INT_MAX;
-      }
+      for (int r = 0; r < kTreeTop; ++r)
+        sh.ent[wave * kTreeTop + r] = pack(r < n_cand ? GreedyStat{tv[r], ti[r]}
+                                                      : GreedyStat{-INFINITY, INT_MAX});
     }
   }
   __syncthreads();
   if (wave != 0) return;
-  // merge of the four lists: entry e (lane e < 32) goes to its rank among all of them
-  constexpr int kEntries = kChunksPerWG * kTreeTop;
-  const float ve = lane < kEntries ? sh.v[lane] : -INFINITY;
-  const int ie = lane < kEntries ? sh.i[lane] : INT_MAX;
+  // entry e = lane goes to its rank among all the lists' entries; the lane holding rank r
+  // writes the row's r-th token
+  const GreedyStat me = unpack(sh.ent[lane]);
   int rank = 0;
-#pragma unroll 8
-  for (int f = 0; f < kEntries; ++f) {
-    const float vf = sh.v[f];
-    const int i_f = sh.i[f];
-    rank += ((vf > ve) | ((vf == ve) & (i_f < ie))) ? 1 : 0;
-  }
-  const bool real = lane < kEntries && ie != INT_MAX;
-  if (lane == 0) {
-    TreeRow *out = a.rows + row;
-    publish(&out->k, k);
-  }
-  const double inv_S = 1.0 / sh.S;
 #pragma unroll
-  for (int r = 0; r < kTreeTop; ++r) {
-    if (r >= k) break;
-    const uint64_t hit = __ballot(real && rank == r);
-    const int hl = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
-    int t = hit ? __shfl(ie, hl) : INT_MAX;
-    const float tvr = hit ? __shfl(ve, hl) : -INFINITY;
-    if (lane == 0) {
-      if (t >= a.V) {                  // only NaN logits leave fewer real tokens than k
-        report(a.dev_status, EV_DERR_TOKEN);
-        t = a.V - 1;
-      }
-      const double q = hit ? exp_nonpos(shifted(tvr, a.inv_tau, sh.M), tab) * inv_S : 0.0;
-      publish(&a.rows[row].tok[r], t);
-      publish(&a.rows[row].q[r], q);
-    }
+  for (int f = 0; f < kTreeTop * kTreeTop; ++f) {
+    const GreedyStat o = unpack(sh.ent[f]);
+    rank += beats(o.val, o.idx, me.val, me.idx) ? 1 : 0;
   }
-  if (lane == 0)
-    for (int r = k; r < kTreeTop; ++r) {
-      publish(&a.rows[row].tok[r], -1);
-      publish(&a.rows[row].q[r], 0.0);
-    }
+  const bool real = me.idx != INT_MAX;
+  const int n_real = __popcll(__ballot(real));
+  TreeRow *out = a.rows + row;
+  if (lane == 0) publish(&out->k, k);
+  if (real && rank < k) {
+    publish(&out->tok[rank], me.idx);
+    publish(&out->q[rank], exp_nonpos(shifted(me.val, a.inv_tau, sh.M), tab) / sh.S);
+  }
+  if (lane < kTreeTop && lane >= min(k, n_real)) {
+    if (lane < k) report(a.dev_status, EV_DERR_TOKEN);   // only NaN logits: too few tokens
+    publish(&out->tok[lane], lane < k ? a.V - 1 : -1);
+    publish(&out->q[lane], 0.0);
+  }
 }
 
 // New candidates of a sequence and the next frontier (one wavefront).
@@ -372,16 +386,14 @@ __device__ void expand_sequence(const ExpandArgs &a, int b, int count, double *s
   }
 }
 
+// Streaming launch: one 1024-logit chunk per wavefront per step.
 template <int CPW>
-__global__ __launch_bounds__(256) void tree_expand_kernel(ExpandArgs a) {
+__global__ __launch_bounds__(256) void tree_chunk_kernel(ExpandArgs a) {
   __shared__ double tab[64];
-  __shared__ int s_last;
-  __shared__ MergeShared sh;
-  __shared__ double s_rank[64];
   const int64_t row = blockIdx.y;
   const int b = (int)(row / a.W), w = (int)(row % a.W);
-  const int count = a.depth == 0 ? 1 : a.front_in[b].count;   // written by the last launch
-  if (w >= count) return;              // unused frontier slot: nothing waits for it
+  const int count = a.depth == 0 ? 1 : a.front_in[b].count;   // written by the last depth
+  if (w >= count) return;              // unused frontier slot
   fill_exp_table(tab);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -414,17 +426,28 @@ __global__ __launch_bounds__(256) void tree_expand_kernel(ExpandArgs a) {
     S = wave_sum(S);
     T = wave_sum(T);
     if (lane == 0) {
-      TreeChunk *p = a.chunk + row * nc + c;
-      publish(&p->M, M);
-      publish(&p->S, S);
-      publish(&p->T, T);
-      publish(&a.top[row * nc + c], pack(GreedyStat{bv, bi}));
+      a.chunk[row * nc + c] = TreeChunk{M, S, T};
+      a.top[row * nc + c] = pack(GreedyStat{bv, bi});
     }
   }
-  if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
+}
+
+// Merge launch: one workgroup per frontier row; the workgroup that completes a
+// sequence's frontier forms its candidates and the next beam.
+__global__ __launch_bounds__(kMergeThreads) void tree_merge_kernel(ExpandArgs a) {
+  __shared__ double tab[64];
+  __shared__ int s_last;
+  __shared__ MergeShared sh;
+  __shared__ double s_rank[64];
+  const int64_t row = blockIdx.x;
+  const int b = (int)(row / a.W), w = (int)(row % a.W);
+  const int count = a.depth == 0 ? 1 : a.front_in[b].count;
+  if (w >= count) return;
+  fill_exp_table(tab);
+  __syncthreads();
   merge_row(a, row, tab, sh);
   if (!last_arrival(&a.seq_cnt[counter_slot(b)], count, &s_last)) return;
-  if (wave == 0) expand_sequence(a, b, count, s_rank);
+  if ((threadIdx.x >> 6) == 0) expand_sequence(a, b, count, s_rank);
 }
 
 struct FinalArgs {
@@ -440,7 +463,7 @@ struct FinalArgs {
 // value rank.  One workgroup per sequence: the candidates (id = depth * 64 + slot) are
 // sorted in LDS by a bitonic network into the order "larger value first, then lower id",
 // then one wavefront numbers the first n_nodes - 1.
-constexpr int kFinalThreads = 256;
+constexpr int kFinalThreads = 512;
 constexpr int kFinalKeys = kMaxExpansions * kCandSlots;
 
 __device__ inline bool key_before(double v, int i, double v2, int i2) {
@@ -478,26 +501,38 @@ __global__ __launch_bounds__(kFinalThreads) void tree_finalize_kernel(FinalArgs 
     pos_of[i] = 0;
   }
   __syncthreads();
+  // bitonic network: each stage is n_keys / 2 compare-exchanges, pair p of a stage with
+  // distance j joins t (bit j clear) and t + j.  For j <= 64 both elements of every pair
+  // of wavefront w lie in its own 128-element block (pairs 64 w .. 64 w + 63), and LDS
+  // accesses of one wavefront take effect in order.  So the whole workgroup must have
+  // finished the previous stage only where one of the two stages crosses blocks: a stage
+  // with j >= 128, or the j = 64 stage that follows one.
   for (int k = 2; k <= n_keys; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < n_keys; t += kFinalThreads) {
-        const int u = t ^ j;
-        if (u > t) {
-          const double vt = kv[t], vu = kv[u];
-          const int it = ki[t], iu = ki[u];
-          const bool first_half = (t & k) == 0;   // this run sorts best-first
-          const bool swap = first_half ? key_before(vu, iu, vt, it) : key_before(vt, it, vu, iu);
-          if (swap) {
-            kv[t] = vu;
-            kv[u] = vt;
-            ki[t] = iu;
-            ki[u] = it;
-          }
+      if (j >= 128 || (j == 64 && k >= 256)) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      for (int p = tid; p < n_keys / 2; p += kFinalThreads) {
+        const int t = ((p & ~(j - 1)) << 1) | (p & (j - 1));
+        const int u = t + j;
+        const double vt = kv[t], vu = kv[u];
+        const int it = ki[t], iu = ki[u];
+        const bool first_half = (t & k) == 0;     // this run sorts best-first
+        const bool swap = first_half ? key_before(vu, iu, vt, it) : key_before(vt, it, vu, iu);
+        if (swap) {
+          kv[t] = vu;
+          kv[u] = vt;
+          ki[t] = iu;
+          ki[u] = it;
         }
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
   // numbering (wavefront 0): by depth, then by rank (lane r holds the r-th best)
   const int lane = tid & 63;
   const int n_sel = min(a.n_nodes - 1, total);
@@ -576,9 +611,10 @@ EV_API ev_status ev_draft_tree_expand(const float *draft_logits, int32_t B, int3
   while (cpw > 1 && rows * ((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw)) < 2048)
     cpw /= 2;
   dim3 grid((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw), (unsigned)rows);
-  if (cpw == 4) hipLaunchKernelGGL((tree_expand_kernel<4>), grid, dim3(256), 0, stream, a);
-  else if (cpw == 2) hipLaunchKernelGGL((tree_expand_kernel<2>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((tree_expand_kernel<1>), grid, dim3(256), 0, stream, a);
+  if (cpw == 4) hipLaunchKernelGGL((tree_chunk_kernel<4>), grid, dim3(256), 0, stream, a);
+  else if (cpw == 2) hipLaunchKernelGGL((tree_chunk_kernel<2>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((tree_chunk_kernel<1>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(tree_merge_kernel, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
   return launch_status();
 }
 
