@@ -31,7 +31,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import tree_attention_verification_ev_amd as ev  # noqa: E402
-from synth import config_by_name, generate  # noqa: E402
+from synth import config_by_name, draft_tree_logits, generate, sampled_drafts  # noqa: E402
 from synth.device import to_device  # noqa: E402
 
 METRIC = "verified tree-nodes/s + KV HBM GB/s (% roofline), GQA 64/8 d128 L=4096 T=64"
@@ -250,12 +250,170 @@ def cpu_baseline(inp, budget_s: float):
                       f"{el:.1f} s on the host"}
 
 
+def timed_rotation(step_fns, steps, warmup):
+    """Wall time of exactly `steps` steps replayed from graphs (one per step function, plus
+    one of a whole rotation), after `warmup` untimed steps."""
+    graphs = [capture(f) for f in step_fns]
+    rotation = capture(lambda: [f() for f in step_fns])
+
+    def run(n):
+        done = 0
+        while n - done >= len(step_fns):
+            rotation.replay()
+            done += len(step_fns)
+        for i in range(n - done):
+            graphs[i].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def call_time_us(step_fns, reps=10):
+    """Mean device time of one step from HIP events around a graph of about 32 steps."""
+    n = len(step_fns) * max(1, math.ceil(32 / len(step_fns)))
+    g = capture(lambda: [step_fns[i % len(step_fns)]() for i in range(n)])
+    g.replay()
+    torch.cuda.synchronize()
+    keep = prime_gpu()
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    del keep
+    return statistics.fmean(a.elapsed_time(b) * 1e3 / n for a, b in pairs)
+
+
+def bench_sampled(args, cfg):
+    """Acceptance with sampled drafts (target and draft logit rows of every node)."""
+    inp = generate(cfg, with_kv=False)
+    draft, tokens = sampled_drafts(inp)
+    mc = max(int((p == a).sum()) for p in inp.parent for a in range(cfg.T))
+    to = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+    tk, pa, un = to(tokens, torch.int32), to(inp.parent, torch.int32), to(inp.uniforms, torch.float64)
+    per_set = 2 * inp.logits.nbytes
+    n_sets = max(1, math.ceil(FOOTPRINT_BYTES / per_set))
+    lg = [to(inp.logits, torch.float32) for _ in range(n_sets)]
+    dr = [to(draft, torch.float32) for _ in range(n_sets)]
+    B, T, V = cfg.B, cfg.T, cfg.V
+    ws = torch.zeros(ev.ev_accept_sampled_workspace(B, T, V), dtype=torch.uint8, device="cuda")
+    z = lambda *sh: torch.zeros(sh, dtype=torch.int32, device="cuda")
+    acc, path, out, st = z(B), z(B, T), z(B, T), z(1)
+    fns = [lambda i=i: ev.ev_accept_sampled(lg[i], dr[i], tk, pa, inp.tau, 0.8, un, mc, acc, path,
+                                            out, ws, st) for i in range(n_sets)]
+    fns[0]()
+    torch.cuda.synchronize()
+    if int(st.item()) != 0:
+        raise ev.EvError(int(st.item()), "bench eager step")
+    elapsed = timed_rotation(fns, args.steps, args.warmup)
+    t_call = call_time_us(fns) * 1e-6
+    useful = 8 * B * T * V                     # both logit rows of every node, read once
+    achieved = useful / t_call / 1e9
+    result = {
+        "metric": "verified tree-nodes/s, acceptance with sampled drafts (target + draft logits)",
+        "value": B * T * args.steps / elapsed, "unit": "tree-nodes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": cfg.workload + ", sampled drafts", "B": B, "T": T, "V": V,
+                   "tau": cfg.tau, "draft_tau": 0.8, "max_children": mc, "buffer_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "kernel": "ev_accept_sampled (statistics launch + rounds)",
+                     "algorithmic_bytes": useful},
+        "call_us": t_call * 1e6,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_budget:
+            oracle.stochastic_batch(inp.logits, draft, tokens, inp.parent, inp.tau, 0.8, inp.uniforms)
+            n += 1
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": B * T * n / el, "unit": "tree-nodes/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"{n} full call(s) of the oracle's sampled-draft walk "
+                                            f"(B={B}, T={T}, V={V}) in {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_draft_tree(args, cfg, depths=6, beam=8, k_max=8, n_nodes=64):
+    """Dynamic draft-tree construction: `depths` beam expansions over the drafter's logit
+    rows (a synthetic stand-in) and the final rerank, for the configuration's batch and
+    vocabulary."""
+    B, V = cfg.B, cfg.V
+    host = draft_tree_logits(B, V, depths=depths, beam=beam)
+    per_set = sum(x.nbytes for x in host)
+    n_sets = max(1, math.ceil(FOOTPRINT_BYTES / per_set))
+    sets = [[torch.from_numpy(x).cuda() for x in host] for _ in range(n_sets)]
+    ws = torch.zeros(ev.ev_draft_tree_workspace(B, beam, V), dtype=torch.uint8, device="cuda")
+    z = lambda *sh: torch.zeros(sh, dtype=torch.int32, device="cuda")
+    ft = [z(B, beam) for _ in range(depths)]
+    fs = [z(B, beam) for _ in range(depths)]
+    fc = [z(B) for _ in range(depths)]
+    root, par, tok, size, st = z(B), z(B, n_nodes), z(B, n_nodes), z(B), z(1)
+
+    def build(i):
+        for d in range(depths):
+            ev.ev_draft_tree_expand(sets[i][d], d, 1.0, k_max, ws, ft[d], fs[d], fc[d], st)
+        ev.ev_draft_tree_finalize(root, beam, V, n_nodes, ws, par, tok, size)
+
+    fns = [lambda i=i: build(i) for i in range(n_sets)]
+    fns[0]()
+    torch.cuda.synchronize()
+    if int(st.item()) != 0:
+        raise ev.EvError(int(st.item()), "bench eager tree")
+    rows = sum(int(c.sum().item()) for c in fc[:-1]) + B     # live frontier rows, all depths
+    elapsed = timed_rotation(fns, args.steps, args.warmup)
+    t_call = call_time_us(fns) * 1e-6
+    useful = 4 * V * rows                      # each live frontier row's logits, read once
+    achieved = useful / t_call / 1e9
+    result = {
+        "metric": "draft trees/s (entropy-guided beam expansion + rerank to <= 64 nodes)",
+        "value": B * args.steps / elapsed, "unit": "trees/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"draft-tree construction, {cfg.workload} batch and vocabulary",
+                   "B": B, "V": V, "depths": depths, "beam": beam, "k_max": k_max,
+                   "n_nodes": n_nodes, "frontier_rows": rows, "buffer_sets": n_sets,
+                   "mean_tree_size": float(size.float().mean().item())},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "kernel": "ev_draft_tree_expand x depths + ev_draft_tree_finalize",
+                     "algorithmic_bytes": useful},
+        "tree_us": t_call * 1e6,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = [x[:1] for x in host]
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_budget:
+            oracle.build_batch(sample, beam, k_max, 1.0, n_nodes, [0])
+            n += 1
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": n / el, "unit": "trees/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"{n} tree(s) of sequence 0 built by the oracle "
+                                            f"({depths} depths, V={V}) in {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama3_70b_layer")
+    ap.add_argument("--path", default="verify", choices=("verify", "sampled", "draft_tree"),
+                    help="verify: the verification step (default); sampled: acceptance with "
+                         "sampled drafts; draft_tree: dynamic draft-tree construction")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -278,6 +436,10 @@ def main():
         sys.exit(2)
     ev.lib()
     cfg = config_by_name(args.config)
+    if args.path == "sampled":
+        return bench_sampled(args, cfg)
+    if args.path == "draft_tree":
+        return bench_draft_tree(args, cfg)
     inp = generate(cfg)
     dev0 = to_device(inp)
     per_set = sum(t.numel() * t.element_size() for t in (dev0.q, dev0.k, dev0.v, dev0.logits))
