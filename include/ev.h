@@ -189,6 +189,36 @@ ev_status ev_kv_compact(const ev_kv_desc *kv, const int32_t *prefix_len, const i
                         const int32_t *accept_len, int32_t B, int32_t T,
                         int32_t *new_len, int32_t *dev_status, hipStream_t stream);
 
+/* Bytes of workspace ev_kv_compact_remap needs for B sequences (no zero-fill needed). */
+size_t ev_kv_compact_remap_workspace(int32_t B);
+
+/* ev_kv_compact_remap — zero-copy pruning of a PAGED cache ([TR] sec. 2: keep the accepted
+ * branch's KV and drop the rest; sec. 4: KV fragmentation and the radix prefix cache):
+ * the same logical result as ev_kv_compact, with block-table entries remapped instead of
+ * rows copied wherever the moves allow it.
+ *   Destination slots L_b + m (m = 1..k) lie in logical blocks X.  A block wholly past the
+ *   root (X * block_size > L_b) whose moves share one offset D = path[m] - m, a multiple
+ *   of block_size, moves no data: D = 0 leaves it in place; D > 0 points its entry at the
+ *   physical block of X + D / block_size.  Every other destination block is written by
+ *   copying rows (K and V, every KV head and layer).  A remap whose source block receives
+ *   such copies is copied instead, repeated until none is left.  With block_size 1 (pages
+ *   of one token) nothing is copied.
+ *   The table kv->block_table points to is updated in place (writable device memory):
+ *   remapped entries change, and entries of blocks from ceil(new_len / block_size) up to
+ *   ceil((L_b + T) / block_size) become -1.  Blocks before L_b / block_size are untouched.
+ *   Outputs: new_len[B] = L_b + k + 1; freed [B][max_blocks_per_seq]: in ascending logical
+ *   block order, the distinct physical blocks of the tree's blocks (from L_b / block_size
+ *   on) that no live block references any more, freed_count[B] of them; copied[B]: slots
+ *   moved by copying.  The caller returns the freed blocks to its pool.
+ *   EV_ERR_ARG for a contiguous cache; device errors as ev_kv_compact (EV_DERR_PATH,
+ *   EV_DERR_BOUNDS, also for a table entry outside [0, n_blocks)); a sequence with a device
+ *   error is left unchanged. */
+ev_status ev_kv_compact_remap(const ev_kv_desc *kv, const int32_t *prefix_len,
+                              const int32_t *path, const int32_t *accept_len, int32_t B,
+                              int32_t T, int32_t *new_len, int32_t *freed, int32_t *freed_count,
+                              int32_t *copied, void *ws, size_t ws_bytes, int32_t *dev_status,
+                              hipStream_t stream);
+
 /* ---- Draft-tree construction ([TR] sec. 2: sequence diagram, "Dynamic Tree-Attention
  * Masking") ----
  * The drafter grows the tree depth by depth: after each expansion it runs on the new

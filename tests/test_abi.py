@@ -114,6 +114,14 @@ def test_host_errors_return_before_launch(lib):
     assert fin(nbytes=100) == 4
     assert lib.ev_draft_tree_workspace(1, 9, 100) == 0
     assert lib.ev_draft_tree_workspace(16, 8, 128256) % 256 == 0
+    rm = lambda desc, ws=P, nbytes=10**6, pl=P: lib.ev_kv_compact_remap(
+        ctypes.byref(desc), pl, P, P, 1, 8, P, P, P, P, ws, nbytes, None, None)
+    paged = dict(paged=1, block_table=P, block_size=16, max_blocks_per_seq=8, n_blocks=64)
+    assert rm(_kv()) == 5                            # contiguous: nothing to remap
+    assert rm(_kv(**paged), pl=None) == 1
+    assert rm(_kv(**paged), nbytes=8) == 4
+    assert rm(_kv(**dict(paged, block_size=12))) == 2
+    assert lib.ev_kv_compact_remap_workspace(0) == 0
     assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=0)), P, P, P, 1, 8, P, None, None) == 2
     assert lib.ev_kv_compact(ctypes.byref(_kv(n_layers=2, layer_stride=0)), P, P, P, 1, 8, P, None, None) == 2
     assert lib.ev_kv_compact(ctypes.byref(d), None, P, P, 1, 8, P, None, None) == 1

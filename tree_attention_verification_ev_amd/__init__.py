@@ -32,6 +32,7 @@ EXPORTED = (
     "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
     "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection",
     "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact",
+    "ev_kv_compact_remap_workspace", "ev_kv_compact_remap",
     "ev_draft_tree_workspace", "ev_draft_tree_expand", "ev_draft_tree_finalize",
     "ev_status_string",
 )
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
             "ev_accept_sampled": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _I32,
                                          _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_kv_compact": (_I32, [kv, _P, _P, _P, _I32, _I32, _P, _P, _P]),
+            "ev_kv_compact_remap_workspace": (_SZ, [_I32]),
+            "ev_kv_compact_remap": (_I32, [kv, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P,
+                                           _P]),
             "ev_draft_tree_workspace": (_SZ, [_I32, _I32, _I32]),
             "ev_draft_tree_expand": (_I32, [_P, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _P,
                                             _P, _SZ, _P, _P]),
@@ -329,6 +333,38 @@ def ev_kv_compact(kv: KvCache, prefix_len: torch.Tensor, path: torch.Tensor, acc
                                _ptr(new_len), _ptr(status), _stream(dev))
     _finish(code, "ev_kv_compact", status, check)
     return new_len
+
+
+def ev_kv_compact_remap_workspace(B: int) -> int:
+    return int(lib().ev_kv_compact_remap_workspace(B))
+
+
+def ev_kv_compact_remap(kv: "KvCache", prefix_len: torch.Tensor, path: torch.Tensor,
+                        accept_len: torch.Tensor, new_len=None, freed=None, freed_count=None,
+                        copied=None, ws=None, dev_status=None, check: bool = False):
+    """Zero-copy pruning of a paged cache: remaps kv's block table in place (copying rows
+    only where the moves do not fill aligned blocks); returns (new_len [B], freed
+    [B][max_blocks_per_seq], freed_count [B], copied [B])."""
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(path, "path", torch.int32)
+    _dev(accept_len, "accept_len", torch.int32)
+    if kv.block_table is None:
+        raise ValueError("ev_kv_compact_remap needs a paged cache")
+    B, T = path.shape
+    dev = path.device
+    e = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
+    new_len = e(B) if new_len is None else new_len
+    freed = e(B, kv.block_table.shape[1]) if freed is None else freed
+    freed_count = e(B) if freed_count is None else freed_count
+    copied = e(B) if copied is None else copied
+    if ws is None:
+        ws = torch.empty(max(1, ev_kv_compact_remap_workspace(B)), dtype=torch.uint8, device=dev)
+    status = _status_word(dev, dev_status)
+    code = lib().ev_kv_compact_remap(kv.ref(), _ptr(prefix_len), _ptr(path), _ptr(accept_len), B, T,
+                                     _ptr(new_len), _ptr(freed), _ptr(freed_count), _ptr(copied),
+                                     _ptr(ws), ws.numel(), _ptr(status), _stream(dev))
+    _finish(code, "ev_kv_compact_remap", status, check)
+    return new_len, freed, freed_count, copied
 
 
 def ev_draft_tree_workspace(B: int, beam: int, V: int) -> int:

@@ -27,6 +27,8 @@ struct CompactArgs {
   int T;
   int32_t *new_len;
   int32_t *dev_status;
+  const uint64_t *copy_mask;   // slots L + m copied (bit m), sequence b at b * mask_stride;
+  int mask_stride;             // null: every m
 };
 
 __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(CompactArgs a) {
@@ -62,9 +64,11 @@ __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(CompactArgs
   const int row_bytes = a.kv.d * a.esz;
   const int cpr = row_bytes / 16;           // 16-byte chunks per row
   const int total = k * cpr;
+  const uint64_t mask = a.copy_mask ? a.copy_mask[(int64_t)b * a.mask_stride] : ~0ull;
   // gather
   for (int c = tid; c < total; c += kCompactThreads) {
     int m = c / cpr + 1, ch = c % cpr;
+    if (!((mask >> m) & 1)) continue;
     int64_t off = a.kv.slot_offset(b, g, L + path[m]);
     f32x4 val = {};
     if (off >= 0) val = *(const f32x4 *)(base + off * a.esz + ch * 16);
@@ -79,10 +83,152 @@ __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(CompactArgs
   // scatter
   for (int c = tid; c < total; c += kCompactThreads) {
     int m = c / cpr + 1, ch = c % cpr;
+    if (!((mask >> m) & 1)) continue;
     int64_t off = a.kv.slot_offset(b, g, L + m);
     if (off >= 0)
       *(f32x4 *)(base + off * a.esz + ch * 16) = *(const f32x4 *)(stage + (m - 1) * row_bytes + ch * 16);
   }
+}
+
+// Zero-copy compaction of a paged cache ([TR] sec. 4: KV fragmentation and the radix
+// cache; sec. 2: keep the accepted branch's KV).  Destination slots L+1 .. L+k lie in
+// logical blocks X.  A block wholly past the root whose moves share one offset
+// D = a_m - m, a multiple of the block size, needs no data movement: D = 0 keeps it in
+// place, D > 0 gives X the physical block of X + D/bs.  The other destination blocks are
+// written by copying rows, and a remap whose source block receives copies falls back to
+// a copy (repeated until stable).  Three launches: the plan (one wavefront per sequence,
+// lane j = logical block L/bs + j), the row copies through the unchanged table, and the
+// table commit.
+struct RemapWs {                       // per sequence, in the caller's workspace
+  uint64_t copy_mask;
+  int32_t n_stage;                     // table entries to commit from block L / bs on
+  int32_t pad;
+  int32_t stage[kMaxNodes];
+};
+
+enum : int { kBlkNone = 0, kBlkCopy = 1, kBlkKeep = 2, kBlkRemap = 3 };
+
+struct RemapArgs {
+  int32_t *table;                      // [B][max_blocks], updated in place by the commit
+  int bs, max_blocks, n_blocks;
+  const int32_t *prefix_len;
+  const int32_t *path;
+  const int32_t *accept_len;
+  int T;
+  RemapWs *ws;
+  int32_t *new_len, *freed, *freed_count, *copied;
+  int32_t *dev_status;
+};
+
+__global__ __launch_bounds__(64) void kv_remap_plan_kernel(RemapArgs a) {
+  __shared__ int s_path[kMaxNodes];
+  __shared__ int s_cls[kMaxNodes];
+  __shared__ int s_new[kMaxNodes];
+  __shared__ int s_old[kMaxNodes];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int L = a.prefix_len[b];
+  const int k = a.accept_len[b];
+  const int32_t *path = a.path + (int64_t)b * a.T;
+  RemapWs *w = a.ws + b;
+  s_path[lane] = lane < a.T ? path[lane] : -1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  bool ok = k >= 0 && k < a.T && s_path[0] == 0;
+  for (int m = 1; ok && m <= k; ++m) ok = s_path[m] > s_path[m - 1] && s_path[m] < a.T;
+  const int bs = a.bs;
+  const int n_old = L >= 0 ? (L + a.T + bs - 1) / bs : 0;
+  if (ok && (L < 0 || n_old > a.max_blocks)) {
+    if (lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    ok = false;
+  } else if (!ok && lane == 0) {
+    report(a.dev_status, EV_DERR_PATH);
+  }
+  const int X0 = ok ? L / bs : 0;
+  const int X = X0 + lane;
+  const bool in_tree = ok && X < n_old;
+  const int old = in_tree ? a.table[(int64_t)b * a.max_blocks + X] : -1;
+  if (ok && __any(in_tree && (old < 0 || old >= a.n_blocks))) {
+    if (lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    ok = false;
+  }
+  if (!ok) {                           // nothing is copied or committed
+    if (lane == 0) {
+      w->copy_mask = 0;
+      w->n_stage = 0;
+    }
+    return;
+  }
+  // class of block X
+  const int m_lo = max(1, X * bs - L), m_hi = min(k, X * bs + bs - 1 - L);
+  int cls = kBlkNone, src = -1;
+  if (in_tree && m_lo <= m_hi) {
+    if (X * bs <= L) {
+      cls = kBlkCopy;
+    } else {
+      const int D = s_path[m_lo] - m_lo;
+      bool same = true;
+      for (int m = m_lo + 1; m <= m_hi; ++m) same = same && (s_path[m] - m == D);
+      if (!same || D % bs != 0) cls = kBlkCopy;
+      else if (D == 0) cls = kBlkKeep;
+      else {
+        cls = kBlkRemap;
+        src = X + D / bs;                // < n_old, so src - X0 < 64
+      }
+    }
+  }
+  s_cls[lane] = cls;
+  s_old[lane] = old;
+  // a remap whose source block receives copies becomes a copy, until none is left
+  for (;;) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool demote = cls == kBlkRemap && s_cls[max(src - X0, 0)] == kBlkCopy;
+    if (!__any(demote)) break;
+    __builtin_amdgcn_wave_barrier();
+    if (demote) {
+      cls = kBlkCopy;
+      s_cls[lane] = cls;
+    }
+  }
+  // copies: slot L + m (lane m) when its block is a copy block
+  const bool copy_m = lane >= 1 && lane <= k && s_cls[(L + lane) / bs - X0] == kBlkCopy;
+  const uint64_t mask = __ballot(copy_m);
+  // the new table of the tree's blocks
+  const int n_new = (L + k + 1 + bs - 1) / bs;
+  int nw = old;
+  if (in_tree) {
+    if (X >= n_new) nw = -1;
+    else if (cls == kBlkRemap) nw = s_old[max(src - X0, 0)];
+  }
+  s_new[lane] = nw;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // freed: old tree blocks no longer referenced by a live block (first occurrence only)
+  bool fr = in_tree;
+  for (int j = 0; fr && j < n_new - X0; ++j) fr = s_new[j] != old;
+  for (int j = 0; fr && j < lane; ++j) fr = s_old[j] != old;
+  const uint64_t fm = __ballot(fr);
+  if (fr) a.freed[(int64_t)b * a.max_blocks + __popcll(fm & ((1ull << lane) - 1ull))] = old;
+  w->stage[lane] = nw;
+  if (lane == 0) {
+    w->copy_mask = mask;
+    w->n_stage = n_old - X0;
+    a.new_len[b] = L + k + 1;
+    a.freed_count[b] = __popcll(fm);
+    a.copied[b] = __popcll(mask);
+  }
+}
+
+__global__ __launch_bounds__(64) void kv_remap_commit_kernel(RemapArgs a) {
+  const int b = blockIdx.x;
+  const RemapWs *w = a.ws + b;
+  const int lane = threadIdx.x;
+  if (lane < w->n_stage)
+    a.table[(int64_t)b * a.max_blocks + a.prefix_len[b] / a.bs + lane] = w->stage[lane];
 }
 
 }  // namespace ev
@@ -113,5 +259,53 @@ EV_API ev_status ev_kv_compact(const ev_kv_desc *kv, const int32_t *prefix_len, 
   a.dev_status = dev_status;
   dim3 grid(B, kv->n_layers * kv->n_kv_heads * 2);
   hipLaunchKernelGGL(ev::kv_compact_kernel, grid, dim3(ev::kCompactThreads), 0, stream, a);
+  return ev::launch_status();
+}
+
+EV_API size_t ev_kv_compact_remap_workspace(int32_t B) {
+  if (B < 1) return 0;
+  return ev::align_up((size_t)B * sizeof(ev::RemapWs), 256);
+}
+
+EV_API ev_status ev_kv_compact_remap(const ev_kv_desc *kv, const int32_t *prefix_len,
+                                     const int32_t *path, const int32_t *accept_len, int32_t B,
+                                     int32_t T, int32_t *new_len, int32_t *freed,
+                                     int32_t *freed_count, int32_t *copied, void *ws,
+                                     size_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
+  ev::KvAddr addr;
+  ev_status st = ev::make_kv_addr(kv, &addr);
+  if (st != EV_OK) return st;
+  if (!kv->paged) return EV_ERR_ARG;
+  if (B < 0 || T < 1 || T > ev::kMaxNodes) return EV_ERR_SHAPE;
+  if ((int64_t)kv->n_layers * kv->n_kv_heads * 2 > 65535) return EV_ERR_SHAPE;
+  if (kv->n_layers > 1 && kv->layer_stride <= 0) return EV_ERR_SHAPE;
+  if (B == 0) return EV_OK;
+  if (!prefix_len || !path || !accept_len || !new_len || !freed || !freed_count || !copied)
+    return EV_ERR_NULL;
+  if (!ws || ws_bytes < ev_kv_compact_remap_workspace(B)) return EV_ERR_WORKSPACE;
+  // the table the descriptor points to is the caller's writable device array
+  ev::RemapArgs r{const_cast<int32_t *>(kv->block_table), kv->block_size, kv->max_blocks_per_seq, kv->n_blocks,
+                  prefix_len, path, accept_len, T, (ev::RemapWs *)ws, new_len, freed,
+                  freed_count, copied, dev_status};
+  hipLaunchKernelGGL(ev::kv_remap_plan_kernel, dim3(B), dim3(64), 0, stream, r);
+  ev::CompactArgs a{};
+  a.k = (char *)kv->k;
+  a.v = (char *)kv->v;
+  a.kv = addr;
+  a.esz = kv->dtype == EV_F32 ? 4 : 2;
+  a.layer_stride = kv->layer_stride;
+  a.n_layers = kv->n_layers;
+  a.prefix_len = prefix_len;
+  a.path = path;
+  a.accept_len = accept_len;
+  a.T = T;
+  a.new_len = new_len;
+  a.dev_status = dev_status;
+  a.copy_mask = &((const ev::RemapWs *)ws)->copy_mask;
+  static_assert(sizeof(ev::RemapWs) % sizeof(uint64_t) == 0, "mask stride");
+  a.mask_stride = (int)(sizeof(ev::RemapWs) / sizeof(uint64_t));
+  dim3 grid(B, kv->n_layers * kv->n_kv_heads * 2);
+  hipLaunchKernelGGL(ev::kv_compact_kernel, grid, dim3(ev::kCompactThreads), 0, stream, a);
+  hipLaunchKernelGGL(ev::kv_remap_commit_kernel, dim3(B), dim3(64), 0, stream, r);
   return ev::launch_status();
 }
