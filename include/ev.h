@@ -209,7 +209,8 @@ size_t ev_kv_compact_remap_workspace(int32_t B);
  *   Outputs: new_len[B] = L_b + k + 1; freed [B][max_blocks_per_seq]: in ascending logical
  *   block order, the distinct physical blocks of the tree's blocks (from L_b / block_size
  *   on) that no live block references any more, freed_count[B] of them; copied[B]: slots
- *   moved by copying.  The caller returns the freed blocks to its pool.
+ *   moved by copying.  The caller returns the freed blocks to its pool.  The table entries
+ *   of a sequence's tree blocks must be distinct (as an allocator hands them out).
  *   EV_ERR_ARG for a contiguous cache; device errors as ev_kv_compact (EV_DERR_PATH,
  *   EV_DERR_BOUNDS, also for a table entry outside [0, n_blocks)); a sequence with a device
  *   error is left unchanged. */

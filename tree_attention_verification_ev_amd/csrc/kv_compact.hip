@@ -3,16 +3,20 @@
 //
 // The tree's KV sits in slots L .. L+T-1 in node order; keeping the accepted path
 // 0 = a_0 < a_1 < ... < a_k moves slot L + a_m to slot L + m (m = 1..k).  Because a
-// destination L + m can be the source of another move (a_{m'} = m), one workgroup owns a
-// whole (sequence, layer, KV head, K|V) slice and gathers every source row into LDS
-// before it writes any destination.  This is a bandwidth-bound copy: 16-byte loads and
-// stores, one row per 16 (bf16, d = 128) lanes.
+// destination L + m can be the source of another move (a_{m'} = m), a workgroup reads
+// every source row of a layer into registers before it writes any destination of that
+// layer.  One workgroup covers a (sequence, KV head, K|V) slice across a group of layers,
+// sized so a launch has about 2048 workgroups; 16-byte loads and stores.
 #include "ev_internal.h"
+
+#include <algorithm>
 
 namespace ev {
 
 constexpr int kCompactThreads = 256;
-constexpr int kMaxRowBytes = 128 * 4;
+constexpr int kStageChunks = 2048;     // 16-byte chunks staged in LDS (32 KB): a layer's
+                                       // rows at most, 63 rows of 512 bytes
+constexpr int kCompactWGs = 2048;      // workgroups one launch aims for
 
 struct CompactArgs {
   char *k;
@@ -21,6 +25,7 @@ struct CompactArgs {
   int esz;                 // element size in bytes
   int64_t layer_stride;    // elements
   int n_layers;
+  int layers_per_wg;
   const int32_t *prefix_len;
   const int32_t *path;
   const int32_t *accept_len;
@@ -28,66 +33,100 @@ struct CompactArgs {
   int32_t *new_len;
   int32_t *dev_status;
   const uint64_t *copy_mask;   // slots L + m copied (bit m), sequence b at b * mask_stride;
-  int mask_stride;             // null: every m
+  int mask_stride;             // null: every m (and the path is validated here)
 };
 
+// One workgroup per (sequence, KV head, K|V, group of layers).  The rows of one layer are
+// all read into LDS before any of them is written (a destination L + m can be the source
+// of another move); layers are disjoint, so a pass stages as many whole layers as fit.
 __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(CompactArgs a) {
-  __shared__ __attribute__((aligned(16))) char stage[(kMaxNodes - 1) * kMaxRowBytes];
-  __shared__ int bad;
+  __shared__ f32x4 stage[kStageChunks];
+  __shared__ int s_path[kMaxNodes];
+  __shared__ int s_list[kMaxNodes];
+  __shared__ int s_n, s_bad;
   const int b = blockIdx.x;
   const int z = blockIdx.y;
   const int which = z & 1;
   const int g = (z >> 1) % a.kv.hkv;
-  const int layer = (z >> 1) / a.kv.hkv;
+  const int group = (z >> 1) / a.kv.hkv;
   const int tid = threadIdx.x;
+  const uint64_t mask = a.copy_mask ? a.copy_mask[(int64_t)b * a.mask_stride] : ~0ull;
+  if (mask == 0) return;                 // remap mode: nothing to copy (or an invalid tree)
   const int L = a.prefix_len[b];
   const int k = a.accept_len[b];
-  const int32_t *path = a.path + (int64_t)b * a.T;
-
-  // Validate the path: node 0 first, strictly increasing, inside the tree.
-  bool ok = k >= 0 && k < a.T && path[0] == 0;
-  for (int m = 1; ok && m <= k; ++m) ok = path[m] > path[m - 1] && path[m] < a.T;
-  if (!ok) {
-    if (tid == 0 && z == 0) report(a.dev_status, EV_DERR_PATH);
-    return;
-  }
-  if (L < 0 || !a.kv.fits(L + a.T)) {
-    if (tid == 0 && z == 0) report(a.dev_status, EV_DERR_BOUNDS);
-    return;
-  }
-  if (tid == 0) bad = 0;
-  if (z == 0 && tid == 0) a.new_len[b] = L + k + 1;
+  if (tid < kMaxNodes) s_path[tid] = tid < a.T ? a.path[(int64_t)b * a.T + tid] : -1;
+  if (tid == 0) s_bad = 0;
   __syncthreads();
-  if (k == 0) return;
-
-  char *base = (which ? a.v : a.k) + (int64_t)layer * a.layer_stride * a.esz;
-  const int row_bytes = a.kv.d * a.esz;
-  const int cpr = row_bytes / 16;           // 16-byte chunks per row
-  const int total = k * cpr;
-  const uint64_t mask = a.copy_mask ? a.copy_mask[(int64_t)b * a.mask_stride] : ~0ull;
-  // gather
-  for (int c = tid; c < total; c += kCompactThreads) {
-    int m = c / cpr + 1, ch = c % cpr;
-    if (!((mask >> m) & 1)) continue;
-    int64_t off = a.kv.slot_offset(b, g, L + path[m]);
-    f32x4 val = {};
-    if (off >= 0) val = *(const f32x4 *)(base + off * a.esz + ch * 16);
-    else bad = 1;
-    *(f32x4 *)(stage + (m - 1) * row_bytes + ch * 16) = val;
+  if (!a.copy_mask) {
+    // validate the path (node 0 first, strictly increasing, inside the tree), the slots
+    // and, for a paged cache, the table entries of the tree's blocks
+    bool bad_path = k < 0 || k >= a.T || s_path[0] != 0;
+    if (!bad_path && tid >= 1 && tid <= k)
+      bad_path = !(s_path[tid] > s_path[tid - 1] && s_path[tid] < a.T);
+    bool bad_slot = L < 0 || !a.kv.fits(L + a.T);
+    if (!bad_slot && a.kv.paged) {
+      const int bs = 1 << a.kv.block_shift;
+      const int X = L / bs + tid;
+      if (X <= (L + a.T - 1) / bs) {
+        const int blk = a.kv.table[(int64_t)b * a.kv.max_blocks + X];
+        bad_slot = blk < 0 || blk >= a.kv.n_blocks;
+      }
+    }
+    if (bad_path) atomicOr(&s_bad, 1);
+    if (bad_slot) atomicOr(&s_bad, 2);
+    __syncthreads();
+    const int bad = s_bad;
+    if (bad) {
+      if (tid == 0 && z == 0) report(a.dev_status, (bad & 1) ? EV_DERR_PATH : EV_DERR_BOUNDS);
+      return;
+    }
+    if (z == 0 && tid == 0) a.new_len[b] = L + k + 1;
+  }
+  // the moves this call makes, in ascending m
+  if (tid < 64) {
+    const bool mv = tid >= 1 && tid <= k && ((mask >> tid) & 1);
+    const uint64_t bal = __ballot(mv);
+    if (mv) s_list[__popcll(bal & ((1ull << tid) - 1ull))] = tid;
+    if (tid == 0) s_n = __popcll(bal);
   }
   __syncthreads();
-  if (bad) {
-    if (tid == 0) report(a.dev_status, EV_DERR_BOUNDS);
-    return;
+  const int n = s_n;
+  if (n == 0) return;
+  const int l_lo = group * a.layers_per_wg;
+  const int l_hi = min(a.n_layers, l_lo + a.layers_per_wg);
+  const int cpr = a.kv.d * a.esz / 16;   // 16-byte chunks per row: 8, 16 or 32
+  const int cshift = __ffs(cpr) - 1;
+  const int per_layer = n * cpr;
+  const int lpp = max(1, kStageChunks / per_layer);      // whole layers per pass
+  char *base = which ? a.v : a.k;
+  for (int l0 = l_lo; l0 < l_hi; l0 += lpp) {
+    const int nl = min(lpp, l_hi - l0);
+    for (int li = 0; li < nl; ++li) {
+      const char *lb = base + (int64_t)(l0 + li) * a.layer_stride * a.esz;
+      for (int r = tid; r < per_layer; r += kCompactThreads) {
+        const int m = s_list[r >> cshift], ch = r & (cpr - 1);
+        const int64_t off = a.kv.slot_offset(b, g, L + s_path[m]);
+        stage[li * per_layer + r] = *(const f32x4 *)(lb + off * a.esz + ch * 16);
+      }
+    }
+    __syncthreads();                     // every source of these layers read
+    for (int li = 0; li < nl; ++li) {
+      char *lb = base + (int64_t)(l0 + li) * a.layer_stride * a.esz;
+      for (int r = tid; r < per_layer; r += kCompactThreads) {
+        const int m = s_list[r >> cshift], ch = r & (cpr - 1);
+        const int64_t off = a.kv.slot_offset(b, g, L + m);
+        *(f32x4 *)(lb + off * a.esz + ch * 16) = stage[li * per_layer + r];
+      }
+    }
+    __syncthreads();                     // the stage is refilled by the next pass
   }
-  // scatter
-  for (int c = tid; c < total; c += kCompactThreads) {
-    int m = c / cpr + 1, ch = c % cpr;
-    if (!((mask >> m) & 1)) continue;
-    int64_t off = a.kv.slot_offset(b, g, L + m);
-    if (off >= 0)
-      *(f32x4 *)(base + off * a.esz + ch * 16) = *(const f32x4 *)(stage + (m - 1) * row_bytes + ch * 16);
-  }
+}
+
+// Layers per workgroup so that one launch has about kCompactWGs workgroups.
+inline int compact_layers_per_wg(int B, int hkv, int n_layers) {
+  const int64_t slices = (int64_t)B * hkv * 2;
+  const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(n_layers, (kCompactWGs + slices - 1) / slices));
+  return (int)((n_layers + groups - 1) / groups);
 }
 
 // Zero-copy compaction of a paged cache ([TR] sec. 4: KV fragmentation and the radix
@@ -123,7 +162,7 @@ struct RemapArgs {
 __global__ __launch_bounds__(64) void kv_remap_plan_kernel(RemapArgs a) {
   __shared__ int s_path[kMaxNodes];
   __shared__ int s_cls[kMaxNodes];
-  __shared__ int s_new[kMaxNodes];
+  __shared__ int s_ref[kMaxNodes];
   __shared__ int s_old[kMaxNodes];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
@@ -131,12 +170,15 @@ __global__ __launch_bounds__(64) void kv_remap_plan_kernel(RemapArgs a) {
   const int k = a.accept_len[b];
   const int32_t *path = a.path + (int64_t)b * a.T;
   RemapWs *w = a.ws + b;
-  s_path[lane] = lane < a.T ? path[lane] : -1;
+  const int pv = lane < a.T ? path[lane] : -1;
+  s_path[lane] = pv;
+  // node 0 first, strictly increasing, inside the tree (lane m checks step m)
+  const int prev = __shfl(pv, max(lane - 1, 0));
+  bool ok = k >= 0 && k < a.T && __shfl(pv, 0) == 0;
+  ok = ok && !__any(lane >= 1 && lane <= k && !(pv > prev && pv < a.T));
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  bool ok = k >= 0 && k < a.T && s_path[0] == 0;
-  for (int m = 1; ok && m <= k; ++m) ok = s_path[m] > s_path[m - 1] && s_path[m] < a.T;
   const int bs = a.bs;
   const int n_old = L >= 0 ? (L + a.T + bs - 1) / bs : 0;
   if (ok && (L < 0 || n_old > a.max_blocks)) {
@@ -203,14 +245,18 @@ __global__ __launch_bounds__(64) void kv_remap_plan_kernel(RemapArgs a) {
     if (X >= n_new) nw = -1;
     else if (cls == kBlkRemap) nw = s_old[max(src - X0, 0)];
   }
-  s_new[lane] = nw;
+  // freed: the tree's old blocks no live block references any more.  A live block keeps
+  // its own entry unless it is remapped, in which case it takes its source's entry (the
+  // entries of a sequence's blocks are distinct, as an allocator hands them out).
+  s_ref[lane] = 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // freed: old tree blocks no longer referenced by a live block (first occurrence only)
-  bool fr = in_tree;
-  for (int j = 0; fr && j < n_new - X0; ++j) fr = s_new[j] != old;
-  for (int j = 0; fr && j < lane; ++j) fr = s_old[j] != old;
+  if (in_tree && X < n_new) s_ref[cls == kBlkRemap ? max(src - X0, 0) : lane] = 1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool fr = in_tree && !s_ref[lane];
   const uint64_t fm = __ballot(fr);
   if (fr) a.freed[(int64_t)b * a.max_blocks + __popcll(fm & ((1ull << lane) - 1ull))] = old;
   w->stage[lane] = nw;
@@ -257,7 +303,9 @@ EV_API ev_status ev_kv_compact(const ev_kv_desc *kv, const int32_t *prefix_len, 
   a.T = T;
   a.new_len = new_len;
   a.dev_status = dev_status;
-  dim3 grid(B, kv->n_layers * kv->n_kv_heads * 2);
+  a.layers_per_wg = ev::compact_layers_per_wg(B, kv->n_kv_heads, kv->n_layers);
+  const int groups = (kv->n_layers + a.layers_per_wg - 1) / a.layers_per_wg;
+  dim3 grid(B, groups * kv->n_kv_heads * 2);
   hipLaunchKernelGGL(ev::kv_compact_kernel, grid, dim3(ev::kCompactThreads), 0, stream, a);
   return ev::launch_status();
 }
@@ -304,7 +352,9 @@ EV_API ev_status ev_kv_compact_remap(const ev_kv_desc *kv, const int32_t *prefix
   a.copy_mask = &((const ev::RemapWs *)ws)->copy_mask;
   static_assert(sizeof(ev::RemapWs) % sizeof(uint64_t) == 0, "mask stride");
   a.mask_stride = (int)(sizeof(ev::RemapWs) / sizeof(uint64_t));
-  dim3 grid(B, kv->n_layers * kv->n_kv_heads * 2);
+  a.layers_per_wg = ev::compact_layers_per_wg(B, kv->n_kv_heads, kv->n_layers);
+  const int groups = (kv->n_layers + a.layers_per_wg - 1) / a.layers_per_wg;
+  dim3 grid(B, groups * kv->n_kv_heads * 2);
   hipLaunchKernelGGL(ev::kv_compact_kernel, grid, dim3(ev::kCompactThreads), 0, stream, a);
   hipLaunchKernelGGL(ev::kv_remap_commit_kernel, dim3(B), dim3(64), 0, stream, r);
   return ev::launch_status();
