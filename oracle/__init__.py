@@ -9,6 +9,7 @@ is involved) of what one verification pass of a drafted token tree computes:
   stochastic.py rejection-sampling walk for drafts sampled from a draft distribution
   compact.py    accepted-path KV compaction
   tree_build.py dynamic draft-tree construction (entropy-guided beam expansion)
+  quant.py      INT4-quantised KV cache: unpacking and dequantisation
 
 It shares no code with the HIP library and imports nothing from it.  Only the test
 suite, the package's smoke check and the benchmark's CPU-baseline leg may import it;
@@ -34,9 +35,11 @@ from .accept import (greedy_walk, greedy_batch, target_probs, rejection_walk,
 from .compact import kv_compact
 from .stochastic import stochastic_walk, stochastic_batch
 from .tree_build import TreeBuilder, build_batch, entropy
+from .quant import bf16_nearest, dequant_int4, unpack_int4
 
 __all__ = [
     "tree_mask", "tree_mask_batch", "tree_attention", "tree_attention_batch", "gather_paged",
     "greedy_walk", "greedy_batch", "target_probs", "rejection_walk", "rejection_batch",
     "kv_compact", "stochastic_walk", "stochastic_batch", "TreeBuilder", "build_batch", "entropy",
+    "bf16_nearest", "dequant_int4", "unpack_int4",
 ]

@@ -12,10 +12,11 @@ tree-attention masking: trees of at most 64 nodes, depth 4-6, width 8) and the
 Llama-2-7B / Llama-3-70B layer shapes.
 """
 from .configs import CONFIGS, Config, config_by_name, scaled
-from .generate import (Inputs, draft_tree_logits, generate, round_to_bf16, sampled_drafts,
-                       static_tree_26)
+from .generate import (Inputs, draft_tree_logits, generate, quantize_int4, round_to_bf16,
+                       sampled_drafts, static_tree_26)
 
 __all__ = [
     "CONFIGS", "Config", "config_by_name", "scaled",
-    "Inputs", "draft_tree_logits", "generate", "round_to_bf16", "sampled_drafts", "static_tree_26",
+    "Inputs", "draft_tree_logits", "generate", "quantize_int4", "round_to_bf16", "sampled_drafts",
+    "static_tree_26",
 ]
