@@ -483,6 +483,67 @@ def bench_compact_remap(args, cfg, n_layers=80):
     print(json.dumps(result), flush=True)
 
 
+def bench_int4(args, cfg):
+    """Tree attention over an INT4-quantised KV cache (4-bit values, one float32 scale per
+    row) against the bfloat16 cache of the same workload."""
+    from synth import quantize_int4
+    inp = generate(cfg, with_logits=False)
+    kq, ks = quantize_int4(inp.k)
+    vq, vs = quantize_int4(inp.v)
+    c = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    per_set = kq.nbytes + vq.nbytes + ks.nbytes + vs.nbytes
+    n_sets = max(1, math.ceil(FOOTPRINT_BYTES / per_set))
+    bt = c(inp.block_table) if inp.block_table is not None else None
+    caches = [ev.KvCache(c(kq), c(vq), bt, k_scale=c(ks), v_scale=c(vs)) for _ in range(n_sets)]
+    dev = to_device(inp)
+    bf_sets = max(1, math.ceil(FOOTPRINT_BYTES / (dev.k.numel() * 4)))
+    bf = [ev.KvCache(dev.k.clone(), dev.v.clone(), dev.block_table) for _ in range(bf_sets)]
+    q = dev.q
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    scale = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    B, T, Hq = cfg.B, cfg.T, cfg.Hq
+    out = torch.empty_like(q)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, ev.ev_tree_attention_workspace(caches[0], B, T, Hq)), dtype=torch.uint8,
+                     device="cuda")
+    wsb = torch.empty(max(1, ev.ev_tree_attention_workspace(bf[0], B, T, Hq)), dtype=torch.uint8,
+                      device="cuda")
+    f4 = [lambda kv=kv: ev.ev_tree_attention(q, kv, dev.prefix_len, anc, scale, out, lse, ws, st)
+          for kv in caches]
+    fb = [lambda kv=kv: ev.ev_tree_attention(q, kv, dev.prefix_len, anc, scale, out, lse, wsb, st)
+          for kv in bf]
+    f4[0]()
+    torch.cuda.synchronize()
+    if int(st.item()) != 0:
+        raise ev.EvError(int(st.item()), "bench eager int4 attention")
+    elapsed = timed_rotation(f4, args.steps, args.warmup)
+    t4, tb = call_time_us(f4) * 1e-6, call_time_us(fb) * 1e-6
+    work = algorithmic_work(inp)
+    L = inp.prefix_len.astype(np.int64)
+    rows = int(sum(cfg.Hkv * (L[b] + T) for b in range(B)))
+    kv4 = 2 * rows * (cfg.d // 2 + 4)                    # packed values + scales, K and V
+    useful = kv4 + work["bytes"] - work["kv_bytes"]      # plus Q, O and LSE
+    achieved = useful / t4 / 1e9
+    result = {
+        "metric": "verified tree-nodes/s, tree attention over an INT4 KV cache",
+        "value": B * T * args.steps / elapsed, "unit": "tree-nodes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int4 KV, bf16 Q/O", "data": "synthetic",
+        "config": {"workload": cfg.workload + ", INT4 cache", "B": B, "Hq": Hq, "Hkv": cfg.Hkv,
+                   "d": cfg.d, "L": cfg.L, "T": T, "kv_layout": inp.layout, "buffer_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "kernel": "ev_tree_attention (INT4 cache; register-staged)",
+                     "algorithmic_bytes": useful},
+        "attention_int4_us": t4 * 1e6, "attention_bf16_us": tb * 1e6,
+        "kv_bytes_int4": kv4, "kv_bytes_bf16": work["kv_bytes"],
+        "attention_tflops_int4": work["flops"] / t4 / 1e12,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -490,10 +551,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama3_70b_layer")
     ap.add_argument("--path", default="verify",
-                    choices=("verify", "sampled", "draft_tree", "compact_remap"),
+                    choices=("verify", "sampled", "draft_tree", "compact_remap", "int4"),
                     help="verify: the verification step (default); sampled: acceptance with "
                          "sampled drafts; draft_tree: dynamic draft-tree construction; "
-                         "compact_remap: zero-copy pruning against row copies")
+                         "compact_remap: zero-copy pruning against row copies; int4: "
+                         "attention over an INT4 cache against the bf16 cache")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -522,6 +584,8 @@ def main():
         return bench_draft_tree(args, cfg)
     if args.path == "compact_remap":
         return bench_compact_remap(args, cfg)
+    if args.path == "int4":
+        return bench_int4(args, cfg)
     inp = generate(cfg)
     dev0 = to_device(inp)
     per_set = sum(t.numel() * t.element_size() for t in (dev0.q, dev0.k, dev0.v, dev0.logits))

@@ -59,7 +59,7 @@ enum {
   EV_DERR_WIDTH = 105     /* a node has more children than the max_children bound */
 };
 
-typedef enum { EV_F32 = 0, EV_BF16 = 1 } ev_dtype;
+typedef enum { EV_F32 = 0, EV_BF16 = 1, EV_INT4 = 2 } ev_dtype;
 
 /* (host) KV-cache descriptor shared by attention and compaction.
  *   contiguous (paged = 0): k, v are [B][n_kv_heads][cap][head_dim]
@@ -68,7 +68,16 @@ typedef enum { EV_F32 = 0, EV_BF16 = 1 } ev_dtype;
  *              (block_table is device int32 [B][max_blocks_per_seq]) at offset
  *              s % block_size.
  *   Compaction touches n_layers layers found at k + l * layer_stride (elements), same for v;
- *   attention reads layer 0 only. */
+ *   attention reads layer 0 only.
+ *   EV_INT4 (an INT4-quantised cache; [EX] pairs EAGLE with KV-cache quantisation): each
+ *   (slot, KV head) row holds head_dim signed 4-bit values q in [-8, 7], two per byte
+ *   (element 2j in the low nibble of byte j, two's complement), so k and v are uint8 with
+ *   head_dim / 2 bytes per row in the layouts above; k_scale and v_scale hold one float32
+ *   scale s per row ([B][n_kv_heads][cap] or [n_blocks][n_kv_heads][block_size]).  The
+ *   value used is bf16(s * q), the float32 product rounded to the nearest bfloat16.
+ *   layer_stride still counts values (a multiple of head_dim); the scales of layer l
+ *   start layer_stride / head_dim floats after layer 0's.  Queries and outputs of
+ *   attention over an EV_INT4 cache are bfloat16. */
 typedef struct {
   int32_t dtype;              /* ev_dtype of K and V (and of Q / O for attention) */
   int32_t n_kv_heads;
@@ -83,6 +92,8 @@ typedef struct {
   int32_t block_size;         /* paged: slots per block, a power of two in [1, 256] */
   int32_t max_blocks_per_seq; /* paged: columns of block_table */
   int32_t n_blocks;           /* paged: blocks in the pool */
+  const float *k_scale;       /* EV_INT4 only: per-row scales of k */
+  const float *v_scale;       /* EV_INT4 only: per-row scales of v */
 } ev_kv_desc;
 
 /* ev_tree_mask_build — ancestor mask of each tree ([TR] sec. 2, mask equation M).

@@ -292,12 +292,15 @@ def draft_tree_logits(B: int, V: int, depths: int = 6, beam: int = 8,
 def quantize_int4(x: np.ndarray):
     """Symmetric 4-bit quantisation of the last axis of a K or V cache, as a cache writer
     would store it: per row a float32 scale max|x| / 7 and values rint(x / scale) clipped
-    to [-8, 7], packed two per byte (element 2j in the low nibble).  Returns (packed uint8
-    [..., d/2], scales float32 [...])."""
+    to [-8, 7], packed two per byte (element 2j in the low nibble).  Rows holding NaN (the
+    poisoned unused slots) get a NaN scale, so a stray read still shows.  Returns (packed
+    uint8 [..., d/2], scales float32 [...])."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(np.nan_to_num(x)), axis=-1)
     scale = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
-    q = np.clip(np.rint(np.nan_to_num(x) / scale[..., None]), -8, 7).astype(np.int16)
+    scale = np.where(np.isnan(x).any(axis=-1), np.float32(np.nan), scale)   # keep poisoned rows
+    finite = np.where(np.isnan(scale), np.float32(1.0), scale)
+    q = np.clip(np.rint(np.nan_to_num(x) / finite[..., None]), -8, 7).astype(np.int16)
     u = (q & 0xF).astype(np.uint8)
     packed = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
     return packed, scale

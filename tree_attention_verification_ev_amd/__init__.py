@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libev.so")
 
 EV_OK = 0
-EV_F32, EV_BF16 = 0, 1
+EV_F32, EV_BF16, EV_INT4 = 0, 1, 2
 STATUS_NAMES = {
     0: "EV_OK", 1: "EV_ERR_NULL", 2: "EV_ERR_SHAPE", 3: "EV_ERR_DTYPE", 4: "EV_ERR_WORKSPACE",
     5: "EV_ERR_ARG", 6: "EV_ERR_LAUNCH", 101: "EV_DERR_PARENT", 102: "EV_DERR_BOUNDS",
@@ -51,6 +51,7 @@ class EvKvDesc(ctypes.Structure):
         ("n_layers", ctypes.c_int32), ("layer_stride", ctypes.c_int64), ("cap", ctypes.c_int64),
         ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -143,10 +144,13 @@ class KvCache:
     contiguous: k, v [B][Hkv][cap][d] (or [n_layers][B][Hkv][cap][d] with layered=True)
     paged:      k, v [n_blocks][Hkv][block_size][d] (or with a leading layer axis) and
                 block_table int32 [B][max_blocks_per_seq]
+    INT4:       k, v uint8 with d/2 bytes per row (two 4-bit values each) and k_scale,
+                v_scale float32 of the same shape without the last axis.
     """
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: Optional[torch.Tensor] = None,
-                 layered: bool = False):
+                 layered: bool = False, k_scale: Optional[torch.Tensor] = None,
+                 v_scale: Optional[torch.Tensor] = None):
         _dev(k, "k")
         _dev(v, "v")
         if k.shape != v.shape or k.dtype != v.dtype:
@@ -155,19 +159,29 @@ class KvCache:
             dtype = EV_F32
         elif k.dtype == torch.bfloat16:
             dtype = EV_BF16
+        elif k.dtype == torch.uint8:
+            dtype = EV_INT4
+            _dev(k_scale, "k_scale", torch.float32)
+            _dev(v_scale, "v_scale", torch.float32)
+            if tuple(k_scale.shape) != tuple(k.shape[:-1]) or tuple(v_scale.shape) != tuple(k.shape[:-1]):
+                raise ValueError("INT4 scales must have the cache's shape without its last axis")
         else:
             raise ValueError(f"unsupported KV dtype {k.dtype}")
         layer_shape = k.shape[1:] if layered else k.shape
         n_layers = k.shape[0] if layered else 1
-        layer_stride = k.stride(0) if layered else 0
+        per_value = 2 if dtype == EV_INT4 else 1         # values per stored element
+        layer_stride = k.stride(0) * per_value if layered else 0
         self.k, self.v, self.block_table, self.layered = k, v, block_table, layered
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.paged = block_table is not None
-        d = layer_shape[-1]
+        d = layer_shape[-1] * per_value
         hkv = layer_shape[1]
         desc = EvKvDesc()
         desc.dtype, desc.n_kv_heads, desc.head_dim, desc.paged = dtype, hkv, d, int(self.paged)
         desc.k, desc.v = k.data_ptr(), v.data_ptr()
         desc.n_layers, desc.layer_stride = n_layers, layer_stride
+        if dtype == EV_INT4:
+            desc.k_scale, desc.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
         if self.paged:
             _dev(block_table, "block_table", torch.int32)
             desc.cap = 0
@@ -213,7 +227,7 @@ def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, an
                       lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                       dev_status: Optional[torch.Tensor] = None, check: bool = False):
     """Tree-masked attention; returns (out [B][T][Hq][d], lse [B][T][Hq] float32)."""
-    _dev(q, "q", kv.dtype)
+    _dev(q, "q", torch.bfloat16 if kv.dtype == torch.uint8 else kv.dtype)
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(anc_mask, "anc_mask", torch.int64)
     B, T, Hq, d = q.shape

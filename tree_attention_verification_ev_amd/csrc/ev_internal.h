@@ -62,7 +62,8 @@ inline int ilog2_exact(int x) {
 // Host-side validation of a KV descriptor; fills `a` on success.
 inline ev_status make_kv_addr(const ev_kv_desc *kv, KvAddr *a) {
   if (!kv || !kv->k || !kv->v) return EV_ERR_NULL;
-  if (kv->dtype != EV_F32 && kv->dtype != EV_BF16) return EV_ERR_DTYPE;
+  if (kv->dtype != EV_F32 && kv->dtype != EV_BF16 && kv->dtype != EV_INT4) return EV_ERR_DTYPE;
+  if (kv->dtype == EV_INT4 && (!kv->k_scale || !kv->v_scale)) return EV_ERR_NULL;
   if (kv->n_kv_heads < 1 || (kv->head_dim != 64 && kv->head_dim != 128)) return EV_ERR_SHAPE;
   if (kv->n_layers < 1) return EV_ERR_SHAPE;
   a->paged = kv->paged ? 1 : 0;

@@ -21,9 +21,11 @@ constexpr int kCompactWGs = 2048;      // workgroups one launch aims for
 struct CompactArgs {
   char *k;
   char *v;
+  float *k_scale;          // INT4 caches: one scale per row, moved with it
+  float *v_scale;
   KvAddr kv;
-  int esz;                 // element size in bytes
-  int64_t layer_stride;    // elements
+  int row_bytes;           // bytes of one (slot, KV head) row
+  int64_t layer_stride;    // values
   int n_layers;
   int layers_per_wg;
   const int32_t *prefix_len;
@@ -41,6 +43,7 @@ struct CompactArgs {
 // of another move); layers are disjoint, so a pass stages as many whole layers as fit.
 __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(CompactArgs a) {
   __shared__ f32x4 stage[kStageChunks];
+  __shared__ float stage_s[kStageChunks / 2];
   __shared__ int s_path[kMaxNodes];
   __shared__ int s_list[kMaxNodes];
   __shared__ int s_n, s_bad;
@@ -94,28 +97,33 @@ __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(CompactArgs
   if (n == 0) return;
   const int l_lo = group * a.layers_per_wg;
   const int l_hi = min(a.n_layers, l_lo + a.layers_per_wg);
-  const int cpr = a.kv.d * a.esz / 16;   // 16-byte chunks per row: 8, 16 or 32
+  const int cpr = a.row_bytes / 16;      // 16-byte chunks per row: 2 .. 32
   const int cshift = __ffs(cpr) - 1;
+  const int dshift = __ffs(a.kv.d) - 1;  // element offset -> row
   const int per_layer = n * cpr;
   const int lpp = max(1, kStageChunks / per_layer);      // whole layers per pass
+  const int64_t layer_rows = a.layer_stride >> dshift;
   char *base = which ? a.v : a.k;
+  float *scales = which ? a.v_scale : a.k_scale;
   for (int l0 = l_lo; l0 < l_hi; l0 += lpp) {
     const int nl = min(lpp, l_hi - l0);
     for (int li = 0; li < nl; ++li) {
-      const char *lb = base + (int64_t)(l0 + li) * a.layer_stride * a.esz;
+      const int64_t lrow = (int64_t)(l0 + li) * layer_rows;
       for (int r = tid; r < per_layer; r += kCompactThreads) {
-        const int m = s_list[r >> cshift], ch = r & (cpr - 1);
-        const int64_t off = a.kv.slot_offset(b, g, L + s_path[m]);
-        stage[li * per_layer + r] = *(const f32x4 *)(lb + off * a.esz + ch * 16);
+        const int mi = r >> cshift, ch = r & (cpr - 1);
+        const int64_t row = lrow + (a.kv.slot_offset(b, g, L + s_path[s_list[mi]]) >> dshift);
+        stage[li * per_layer + r] = *(const f32x4 *)(base + row * a.row_bytes + ch * 16);
+        if (scales && ch == 0) stage_s[li * n + mi] = scales[row];
       }
     }
     __syncthreads();                     // every source of these layers read
     for (int li = 0; li < nl; ++li) {
-      char *lb = base + (int64_t)(l0 + li) * a.layer_stride * a.esz;
+      const int64_t lrow = (int64_t)(l0 + li) * layer_rows;
       for (int r = tid; r < per_layer; r += kCompactThreads) {
-        const int m = s_list[r >> cshift], ch = r & (cpr - 1);
-        const int64_t off = a.kv.slot_offset(b, g, L + m);
-        *(f32x4 *)(lb + off * a.esz + ch * 16) = stage[li * per_layer + r];
+        const int mi = r >> cshift, ch = r & (cpr - 1);
+        const int64_t row = lrow + (a.kv.slot_offset(b, g, L + s_list[mi]) >> dshift);
+        *(f32x4 *)(base + row * a.row_bytes + ch * 16) = stage[li * per_layer + r];
+        if (scales && ch == 0) scales[row] = stage_s[li * n + mi];
       }
     }
     __syncthreads();                     // the stage is refilled by the next pass
@@ -287,14 +295,17 @@ EV_API ev_status ev_kv_compact(const ev_kv_desc *kv, const int32_t *prefix_len, 
   if (st != EV_OK) return st;
   if (B < 0 || T < 1 || T > ev::kMaxNodes) return EV_ERR_SHAPE;
   if ((int64_t)kv->n_layers * kv->n_kv_heads * 2 > 65535) return EV_ERR_SHAPE;
-  if (kv->n_layers > 1 && kv->layer_stride <= 0) return EV_ERR_SHAPE;
+  if (kv->n_layers > 1 && (kv->layer_stride <= 0 || kv->layer_stride % kv->head_dim)) return EV_ERR_SHAPE;
   if (B == 0) return EV_OK;
   if (!prefix_len || !path || !accept_len || !new_len) return EV_ERR_NULL;
   ev::CompactArgs a{};
   a.k = (char *)kv->k;
   a.v = (char *)kv->v;
   a.kv = addr;
-  a.esz = kv->dtype == EV_F32 ? 4 : 2;
+  a.row_bytes = kv->dtype == EV_F32 ? 4 * kv->head_dim
+               : kv->dtype == EV_BF16 ? 2 * kv->head_dim : kv->head_dim / 2;
+  a.k_scale = kv->dtype == EV_INT4 ? const_cast<float *>(kv->k_scale) : nullptr;
+  a.v_scale = kv->dtype == EV_INT4 ? const_cast<float *>(kv->v_scale) : nullptr;
   a.layer_stride = kv->layer_stride;
   a.n_layers = kv->n_layers;
   a.prefix_len = prefix_len;
@@ -326,7 +337,7 @@ EV_API ev_status ev_kv_compact_remap(const ev_kv_desc *kv, const int32_t *prefix
   if (!kv->paged) return EV_ERR_ARG;
   if (B < 0 || T < 1 || T > ev::kMaxNodes) return EV_ERR_SHAPE;
   if ((int64_t)kv->n_layers * kv->n_kv_heads * 2 > 65535) return EV_ERR_SHAPE;
-  if (kv->n_layers > 1 && kv->layer_stride <= 0) return EV_ERR_SHAPE;
+  if (kv->n_layers > 1 && (kv->layer_stride <= 0 || kv->layer_stride % kv->head_dim)) return EV_ERR_SHAPE;
   if (B == 0) return EV_OK;
   if (!prefix_len || !path || !accept_len || !new_len || !freed || !freed_count || !copied)
     return EV_ERR_NULL;
@@ -340,7 +351,10 @@ EV_API ev_status ev_kv_compact_remap(const ev_kv_desc *kv, const int32_t *prefix
   a.k = (char *)kv->k;
   a.v = (char *)kv->v;
   a.kv = addr;
-  a.esz = kv->dtype == EV_F32 ? 4 : 2;
+  a.row_bytes = kv->dtype == EV_F32 ? 4 * kv->head_dim
+               : kv->dtype == EV_BF16 ? 2 * kv->head_dim : kv->head_dim / 2;
+  a.k_scale = kv->dtype == EV_INT4 ? const_cast<float *>(kv->k_scale) : nullptr;
+  a.v_scale = kv->dtype == EV_INT4 ? const_cast<float *>(kv->v_scale) : nullptr;
   a.layer_stride = kv->layer_stride;
   a.n_layers = kv->n_layers;
   a.prefix_len = prefix_len;

@@ -63,6 +63,8 @@ struct AttnArgs {
   float *part_lse;         // [n_splits][B][T][Hq]
   float *part_scale;       // [n_splits][B][T][Hq]
   int32_t *dev_status;
+  const float *k_scale;    // INT4 caches: one scale per (slot, KV head) row
+  const float *v_scale;
 };
 
 // Is logical slot `slot` visible to a query whose ancestor row is `anc` (prefix length L)?
@@ -252,9 +254,23 @@ constexpr int kTableCache = 1024;
 // reads its block ids from the LDS cache.  Only the last tile of a sequence is partial.
 // V is transposed on its way to LDS in items of KPI keys x 8 dims (one item per thread
 // for 256- and 512-thread workgroups).
-template <int D, int NT, bool PAGED>
+// Eight values of an INT4 row chunk (4 bytes, element 2j in the low nibble of byte j)
+// times the row's scale, each float32 product rounded to bfloat16, packed in pairs.
+__device__ inline u32x4 dequant8(uint32_t w, float s) {
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int lo = ((int)(w << (28 - 8 * p))) >> 28;
+    const int hi = ((int)(w << (24 - 8 * p))) >> 28;
+    const __bf16 a = (__bf16)(s * (float)lo), b = (__bf16)(s * (float)hi);
+    out[p] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  return out;
+}
+
+template <int D, int NT, bool PAGED, bool Q4 = false>
 struct TileStage {
-  static constexpr int DC = D / 8;                     // 16-byte chunks per key row
+  static constexpr int DC = D / 8;                     // 8-value chunks per key row
   static constexpr int KCHUNKS = kKT * DC;             // K chunks per tile
   static constexpr int KPI = NT >= 512 ? 2 : 4;        // keys per V item
   static constexpr int VITEMS = (kKT / KPI) * DC;      // V items per tile
@@ -267,16 +283,25 @@ struct TileStage {
   u32x4 kr[KPT];
   u32x4 vr[VPT][KPI];
 
-  // Element offset of logical slot `slot` (PAGED: -1 for a bad block id).
-  __device__ static inline int64_t slot_off(const KvAddr &kv, int64_t seq_base, const int *stbl,
+  // Row index (slot row of KV head g) of logical slot `slot` (PAGED: -1 for a bad block).
+  __device__ static inline int64_t slot_row(const KvAddr &kv, int64_t seq_row, const int *stbl,
                                             int blk0, int g, int slot) {
-    if (!PAGED) return seq_base + (int64_t)slot * D;
+    if (!PAGED) return seq_row + slot;
     const int blk = stbl[(slot >> kv.block_shift) - blk0];
     if (blk < 0) return -1;
-    return ((((int64_t)blk * kv.hkv + g) << kv.block_shift) | (slot & ((1 << kv.block_shift) - 1))) * D;
+    return (((int64_t)blk * kv.hkv + g) << kv.block_shift) | (slot & ((1 << kv.block_shift) - 1));
   }
 
-  __device__ inline void load(const AttnArgs &a, const __bf16 *K, const __bf16 *V, int64_t seq_base,
+  // Chunk dc (values 8 dc .. 8 dc + 7) of row `row`, as eight bfloat16 values.
+  __device__ static inline u32x4 chunk(const void *X, const float *xs, int64_t row, int dc) {
+    if (Q4) {
+      const uint32_t w = *(const uint32_t *)((const uint8_t *)X + row * (D / 2) + dc * 4);
+      return dequant8(w, xs[row]);
+    }
+    return *(const u32x4 *)((const __bf16 *)X + row * D + dc * 8);
+  }
+
+  __device__ inline void load(const AttnArgs &a, const void *K, const void *V, int64_t seq_row,
                               const int *stbl, int blk0, int g, int key0, int nkeys) {
     const int tid = threadIdx.x;
     const bool full = key0 + kKT <= nkeys;
@@ -286,8 +311,8 @@ struct TileStage {
       const int key = tid / DC + i * KSTEP;
       u32x4 val = {};
       if (key < kKT && (full || key0 + key < nkeys)) {
-        const int64_t off = slot_off(a.kv, seq_base, stbl, blk0, g, key0 + key);
-        if (off >= 0) val = *(const u32x4 *)(K + off + dc * 8);
+        const int64_t row = slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key);
+        if (row >= 0) val = chunk(K, a.k_scale, row, dc);
       }
       kr[i] = val;
     }
@@ -300,8 +325,8 @@ struct TileStage {
         u32x4 val = {};
         const int key = KPI * kq + r;
         if (c < VITEMS && (full || key0 + key < nkeys)) {
-          const int64_t off = slot_off(a.kv, seq_base, stbl, blk0, g, key0 + key);
-          if (off >= 0) val = *(const u32x4 *)(V + off + vdc * 8);
+          const int64_t row = slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key);
+          if (row >= 0) val = chunk(V, a.v_scale, row, vdc);
         }
         vr[i][r] = val;
       }
@@ -343,10 +368,10 @@ struct TileStage {
   }
 };
 
-template <int D, int QT, int NW, bool PAGED>
+template <int D, int QT, int NW, bool PAGED, bool Q4 = false>
 __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
-  using Stage = TileStage<D, NT, PAGED>;
+  using Stage = TileStage<D, NT, PAGED, Q4>;
   constexpr int KS = D / 16;            // k-steps of the score product
   constexpr int DT = D / 32;            // 32-row tiles of O^T
   constexpr int KP = Stage::KP;
@@ -397,9 +422,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
     return;
   }
   const __bf16 *Q = (const __bf16 *)a.q;
-  const __bf16 *K = (const __bf16 *)a.k;
-  const __bf16 *V = (const __bf16 *)a.v;
-  const int64_t seq_base = PAGED ? 0 : (int64_t)(b * a.kv.hkv + g) * a.kv.cap * D;
+  const void *K = a.k;
+  const void *V = a.v;
+  const int64_t seq_row = PAGED ? 0 : (int64_t)(b * a.kv.hkv + g) * a.kv.cap;
 
   int blk0 = 0;
   if (PAGED) {
@@ -417,7 +442,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
   }
 
   Stage s0;
-  s0.load(a, K, V, seq_base, stbl, blk0, g, t_begin * kKT, nkeys);
+  s0.load(a, K, V, seq_row, stbl, blk0, g, t_begin * kKT, nkeys);
 
   // Q^T fragments (B operand): lane holds query row qn, 8 head-dim elements per k-step.
   bf16x8 qf[QT][KS];
@@ -464,7 +489,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
     tile_exp(sc, pf, mref, l, a.scale_log2);
     tile_pv(o, pf, vfrag);
     if (tile + 1 < t_end) {
-      s0.load(a, K, V, seq_base, stbl, blk0, g, (tile + 1) * kKT, nkeys);
+      s0.load(a, K, V, seq_row, stbl, blk0, g, (tile + 1) * kKT, nkeys);
       __syncthreads();
       s0.store(sK, sV);
       __syncthreads();
@@ -872,6 +897,9 @@ static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq) {
   const int waves_needed = (rows + wave_rows - 1) / wave_rows;
   p.nw = waves_needed >= 8 && p.qt == 1 ? 8
        : waves_needed >= 4 ? 4 : (waves_needed >= 2 ? 2 : 1);
+  // An INT4 tile is dequantised by every thread of the workgroup while staging: at least
+  // four wavefronts share that work even when fewer own query rows.
+  if (dtype == EV_INT4) p.nw = std::max(p.nw, 4);
   p.row_blocks = (waves_needed + p.nw - 1) / p.nw;
   const int max_tiles = (max_slots(kv) + kKT - 1) / kKT;
   const int units = B * kv.hkv * p.row_blocks;
@@ -901,10 +929,10 @@ static size_t workspace_bytes(const Plan &p, int B, int T, int Hq, int D) {
   return align_up(rows * D * sizeof(_Float16), 256) + 2 * align_up(rows * sizeof(float), 256);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool Q4>
 static void launch_main(const Plan &p, const AttnArgs &a, hipStream_t stream) {
   dim3 grid(p.grid);
-  if (D == 128 && p.qt == 1 && p.nw >= 2) {
+  if (!Q4 && D == 128 && p.qt == 1 && p.nw >= 2) {
     if (p.nw == 8)
       hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED>), grid, dim3(512), 0, stream, a);
     else if (p.nw == 4)
@@ -912,24 +940,30 @@ static void launch_main(const Plan &p, const AttnArgs &a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED>), grid, dim3(128), 0, stream, a);
   } else if (p.qt == 2) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 2, 4, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 2, 4, PAGED, Q4>), grid, dim3(256), 0, stream, a);
   } else if (p.nw == 8) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 8, PAGED>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 8, PAGED, Q4>), grid, dim3(512), 0, stream, a);
   } else if (p.nw == 4) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 4, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 4, PAGED, Q4>), grid, dim3(256), 0, stream, a);
   } else if (p.nw == 2) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 2, PAGED>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 2, PAGED, Q4>), grid, dim3(128), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 1, PAGED>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 1, PAGED, Q4>), grid, dim3(64), 0, stream, a);
   }
 }
 
 template <int D>
-static void launch_bf16(const Plan &p, const AttnArgs &a, hipStream_t stream) {
-  if (a.kv.paged)
-    launch_main<D, true>(p, a, stream);
-  else
-    launch_main<D, false>(p, a, stream);
+static void launch_bf16(const Plan &p, const AttnArgs &a, bool q4, hipStream_t stream) {
+  if (q4) {
+    if (a.kv.paged)
+      launch_main<D, true, true>(p, a, stream);
+    else
+      launch_main<D, false, true>(p, a, stream);
+  } else if (a.kv.paged) {
+    launch_main<D, true, false>(p, a, stream);
+  } else {
+    launch_main<D, false, false>(p, a, stream);
+  }
   if (p.n_splits > 1) {
     int64_t nrows = (int64_t)a.B * a.T * a.Hq;
     dim3 mgrid((unsigned)((nrows + 7) / 8));
@@ -968,6 +1002,8 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   a.q = q;
   a.k = kv->k;
   a.v = kv->v;
+  a.k_scale = kv->k_scale;
+  a.v_scale = kv->v_scale;
   a.kv = addr;
   a.prefix_len = prefix_len;
   a.anc = anc_mask;
@@ -998,10 +1034,11 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
     else
       hipLaunchKernelGGL(ev::tree_attn_f32_kernel<128>, grid, dim3(64), 0, stream, a);
   } else {
+    const bool q4 = kv->dtype == EV_INT4;
     if (kv->head_dim == 64)
-      ev::launch_bf16<64>(p, a, stream);
+      ev::launch_bf16<64>(p, a, q4, stream);
     else
-      ev::launch_bf16<128>(p, a, stream);
+      ev::launch_bf16<128>(p, a, q4, stream);
   }
   return ev::launch_status();
 }
