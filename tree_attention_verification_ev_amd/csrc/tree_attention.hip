@@ -280,8 +280,14 @@ struct TileStage {
   static constexpr int KP = D + 8;                     // LDS pitch of the K tile (elements)
   static constexpr int VP = kKT + 8;                   // LDS pitch of the V^T tile (elements)
   static_assert(NT % DC == 0 && NT % (kKT / KPI) == 0, "thread count must tile the stage");
-  u32x4 kr[KPT];
-  u32x4 vr[VPT][KPI];
+  // Staged tile: bf16 chunks, or for Q4 the packed words and their rows' scales
+  // (dequantised when stored, so a prefetch holds only the raw bytes).
+  u32x4 kr[Q4 ? 1 : KPT];
+  u32x4 vr[Q4 ? 1 : VPT][KPI];
+  uint32_t kw[Q4 ? KPT : 1];
+  float ks[Q4 ? KPT : 1];
+  uint32_t vw[Q4 ? VPT : 1][KPI];
+  float vs[Q4 ? VPT : 1][KPI];
 
   // Row index (slot row of KV head g) of logical slot `slot` (PAGED: -1 for a bad block).
   __device__ static inline int64_t slot_row(const KvAddr &kv, int64_t seq_row, const int *stbl,
@@ -292,45 +298,65 @@ struct TileStage {
     return (((int64_t)blk * kv.hkv + g) << kv.block_shift) | (slot & ((1 << kv.block_shift) - 1));
   }
 
-  // Chunk dc (values 8 dc .. 8 dc + 7) of row `row`, as eight bfloat16 values.
-  __device__ static inline u32x4 chunk(const void *X, const float *xs, int64_t row, int dc) {
-    if (Q4) {
-      const uint32_t w = *(const uint32_t *)((const uint8_t *)X + row * (D / 2) + dc * 4);
-      return dequant8(w, xs[row]);
-    }
-    return *(const u32x4 *)((const __bf16 *)X + row * D + dc * 8);
-  }
-
   __device__ inline void load(const AttnArgs &a, const void *K, const void *V, int64_t seq_row,
                               const int *stbl, int blk0, int g, int key0, int nkeys) {
     const int tid = threadIdx.x;
     const bool full = key0 + kKT <= nkeys;
     const int dc = tid % DC;
+    if constexpr (Q4) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = tid / DC + i * KSTEP;
-      u32x4 val = {};
-      if (key < kKT && (full || key0 + key < nkeys)) {
-        const int64_t row = slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key);
-        if (row >= 0) val = chunk(K, a.k_scale, row, dc);
+      for (int i = 0; i < KPT; ++i) {
+        const int key = tid / DC + i * KSTEP;
+        const bool live = key < kKT && (full || key0 + key < nkeys);
+        const int64_t row = live ? slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key) : -1;
+        kw[i] = row >= 0 ? *(const uint32_t *)((const uint8_t *)K + row * (D / 2) + dc * 4) : 0u;
+        ks[i] = row >= 0 ? a.k_scale[row] : 0.f;
       }
-      kr[i] = val;
-    }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * NT;
-      const int kq = c % (kKT / KPI), vdc = c / (kKT / KPI);
+      for (int i = 0; i < VPT; ++i) {
+        const int c = tid + i * NT;
+        const int kq = c % (kKT / KPI), vdc = c / (kKT / KPI);
 #pragma unroll
-      for (int r = 0; r < KPI; ++r) {
-        u32x4 val = {};
-        const int key = KPI * kq + r;
-        if (c < VITEMS && (full || key0 + key < nkeys)) {
-          const int64_t row = slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key);
-          if (row >= 0) val = chunk(V, a.v_scale, row, vdc);
+        for (int r = 0; r < KPI; ++r) {
+          const int key = KPI * kq + r;
+          const bool live = c < VITEMS && (full || key0 + key < nkeys);
+          const int64_t row = live ? slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key) : -1;
+          vw[i][r] = row >= 0 ? *(const uint32_t *)((const uint8_t *)V + row * (D / 2) + vdc * 4) : 0u;
+          vs[i][r] = row >= 0 ? a.v_scale[row] : 0.f;
         }
-        vr[i][r] = val;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int key = tid / DC + i * KSTEP;
+        u32x4 val = {};
+        if (key < kKT && (full || key0 + key < nkeys)) {
+          const int64_t row = slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key);
+          if (row >= 0) val = *(const u32x4 *)((const __bf16 *)K + row * D + dc * 8);
+        }
+        kr[i] = val;
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = tid + i * NT;
+        const int kq = c % (kKT / KPI), vdc = c / (kKT / KPI);
+#pragma unroll
+        for (int r = 0; r < KPI; ++r) {
+          u32x4 val = {};
+          const int key = KPI * kq + r;
+          if (c < VITEMS && (full || key0 + key < nkeys)) {
+            const int64_t row = slot_row(a.kv, seq_row, stbl, blk0, g, key0 + key);
+            if (row >= 0) val = *(const u32x4 *)((const __bf16 *)V + row * D + vdc * 8);
+          }
+          vr[i][r] = val;
+        }
       }
     }
+  }
+
+  __device__ inline u32x4 kchunk(int i) const { return Q4 ? dequant8(kw[i], ks[i]) : kr[i]; }
+  __device__ inline u32x4 vchunk(int i, int r) const {
+    return Q4 ? dequant8(vw[i][r], vs[i][r]) : vr[i][r];
   }
 
   __device__ inline void store(__bf16 *sK, __bf16 *sV) const {
@@ -338,7 +364,7 @@ struct TileStage {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int key = tid / DC + i * KSTEP;
-      if (key < kKT) *(u32x4 *)(sK + key * KP + (tid % DC) * 8) = kr[i];
+      if (key < kKT) *(u32x4 *)(sK + key * KP + (tid % DC) * 8) = kchunk(i);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -349,7 +375,8 @@ struct TileStage {
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         if (KPI == 4) {
-          const u32x4 &r0 = vr[i][0], &r1 = vr[i][1], &r2 = vr[i][KPI - 2], &r3 = vr[i][KPI - 1];
+          const u32x4 r0 = vchunk(i, 0), r1 = vchunk(i, 1), r2 = vchunk(i, KPI - 2),
+                      r3 = vchunk(i, KPI - 1);
           u32x2 lo = {__builtin_amdgcn_perm(r1[wd], r0[wd], 0x05040100u),
                       __builtin_amdgcn_perm(r3[wd], r2[wd], 0x05040100u)};
           u32x2 hi = {__builtin_amdgcn_perm(r1[wd], r0[wd], 0x07060302u),
@@ -357,7 +384,7 @@ struct TileStage {
           *(u32x2 *)(sV + (vdc * 8 + 2 * wd) * VP + KPI * kq) = lo;
           *(u32x2 *)(sV + (vdc * 8 + 2 * wd + 1) * VP + KPI * kq) = hi;
         } else {
-          const u32x4 &r0 = vr[i][0], &r1 = vr[i][1];
+          const u32x4 r0 = vchunk(i, 0), r1 = vchunk(i, 1);
           *(uint32_t *)(sV + (vdc * 8 + 2 * wd) * VP + KPI * kq) =
               __builtin_amdgcn_perm(r1[wd], r0[wd], 0x05040100u);
           *(uint32_t *)(sV + (vdc * 8 + 2 * wd + 1) * VP + KPI * kq) =
@@ -481,6 +508,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
   s0.store(sK, sV);
   __syncthreads();
   for (int tile = t_begin; tile < t_end; ++tile) {
+    // INT4: the next tile's raw bytes are requested before this tile is computed (they are
+    // small enough to stay in registers meanwhile); bf16 keeps load-after-compute.
+    if (Q4 && tile + 1 < t_end) s0.load(a, K, V, seq_row, stbl, blk0, g, (tile + 1) * kKT, nkeys);
     f32x16 sc[QT][2];
     bf16x8 pf[QT][2][2];
     tile_scores(sc, qf, kfrag);
@@ -489,7 +519,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
     tile_exp(sc, pf, mref, l, a.scale_log2);
     tile_pv(o, pf, vfrag);
     if (tile + 1 < t_end) {
-      s0.load(a, K, V, seq_row, stbl, blk0, g, (tile + 1) * kKT, nkeys);
+      if (!Q4) s0.load(a, K, V, seq_row, stbl, blk0, g, (tile + 1) * kKT, nkeys);
       __syncthreads();
       s0.store(sK, sV);
       __syncthreads();
