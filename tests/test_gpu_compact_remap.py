@@ -86,3 +86,13 @@ def test_remap_reports_bad_path_and_leaves_the_sequence():
     assert e.value.code == 104
     assert np.array_equal(td.cpu().numpy(), table)
     assert np.array_equal(kd.cpu().numpy(), k)
+
+
+def test_remap_with_nothing_accepted():
+    """k = 0 everywhere: no slot moves; the tree's blocks past the root's are freed."""
+    rng = np.random.default_rng(9)
+    L, table, k, v, paths, acc = random_case(rng, 4, 24, 4, layers=1, d=64)
+    paths[:, 1:] = -1
+    acc[:] = 0
+    copied = run_case(L, table, k, v, paths, acc, 4, 24, "bf16")
+    assert copied.sum() == 0

@@ -125,3 +125,9 @@ def test_workspace_reuse_across_trees():
     compare(draft_tree_logits(B, V, depths=6, seed=5), 8, 1.0, 64, ws=ws)
     compare(draft_tree_logits(B, V, depths=3, seed=6), 8, 1.0, 40, ws=ws)
     assert int(ws[:2 * 65536 * 4].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("n_nodes", [1, 2, 9])
+def test_draft_tree_small_node_budgets(n_nodes):
+    dl = draft_tree_logits(3, 2000, depths=3, beam=8)
+    compare(dl, 8, 1.0, n_nodes)

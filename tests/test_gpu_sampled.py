@@ -135,3 +135,15 @@ def test_sampled_gpu_preserves_target_distribution_chi_square():
     pv0 = scipy.stats.chisquare(first, first.sum() * ref0).pvalue
     pv1 = scipy.stats.chisquare(second, second.sum() * ref1).pvalue
     assert pv0 > 1e-3 and pv1 > 1e-3, (pv0, pv1, first, second)
+
+
+def test_sampled_root_only_trees():
+    """T = 1: no child to test, every sequence emits one bonus token drawn from p (no rounds)."""
+    cfg = scaled(C3, B=5, T=1, tree="grow", V=3000, L=8)
+    inp = generate(cfg, with_kv=False)
+    draft, tokens = sampled_drafts(inp, DRAFT_TAU)
+    got = run_sampled(inp, draft, tokens, mc=0)
+    ref = oracle_sampled(inp, draft, tokens)
+    assert (got[0] == 0).all()
+    for a, b in zip(got, ref[:3]):
+        assert np.array_equal(a, b)
