@@ -24,6 +24,8 @@
  *     optional device word *dev_status (may be NULL): the first error code stored there
  *     wins (the caller zeroes it beforehand and reads it after synchronising).  Outputs of
  *     an offending sequence are then unspecified, but no out-of-bounds access is made.
+ *   - Arrays of queries, outputs and cache rows must start on a 16-byte boundary (any
+ *     device allocator's alignment); a misaligned one returns EV_ERR_ARG.
  *   - Tree encoding: parent[B][T] int32, node 0 is the root (the last committed token,
  *     parent -1) and 0 <= parent[i] < i for i >= 1; 1 <= T <= 64.
  *   - Draft tokens: tokens[B][T] int32; tokens[b][i] is the token drafted at node i.
@@ -49,7 +51,7 @@ enum {
   EV_ERR_SHAPE = 2,       /* a size is out of range (T, heads, head_dim, V, layout) */
   EV_ERR_DTYPE = 3,       /* unsupported element type */
   EV_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the *_workspace() query */
-  EV_ERR_ARG = 5,         /* invalid scalar (temperature, softmax scale) */
+  EV_ERR_ARG = 5,         /* invalid scalar (temperature, softmax scale) or misaligned array */
   EV_ERR_LAUNCH = 6,      /* a kernel launch failed */
   /* device-side codes, stored into *dev_status */
   EV_DERR_PARENT = 101,   /* parent[] is not a topological tree rooted at node 0 */

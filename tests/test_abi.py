@@ -76,6 +76,8 @@ def test_host_errors_return_before_launch(lib):
     assert att(d, scale=0.0) == 5
     assert att(d, scale=float("nan")) == 5
     assert att(d, q=None) == 1
+    assert att(d, q=P + 8) == 5                     # rows read in 16-byte pieces
+    assert att(_kv(k=P + 2)) == 5
     assert att(d) == 4                              # split workspace missing
     assert att(_kv(paged=1, block_table=None)) == 1
     assert att(_kv(paged=1, block_table=P, block_size=12, max_blocks_per_seq=4, n_blocks=9)) == 2

@@ -348,11 +348,12 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
   AcceptArgs a{logits, tokens, parent, B, T, V, n_chunks_of(V), inv_tau, uniforms,
                base + w.stats, (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
                (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status};
-  // Chunks per wavefront: as many as keep at least 2048 workgroups in the grid (a few per
-  // CU), so that large batches stream with loads in flight behind the reduction.
+  // Chunks per wavefront: as many as keep at least 1024 workgroups in the grid (four per
+  // CU), so that the streams run with the next chunk's loads in flight behind the reduction
+  // while every workgroup stays resident at once.
   const int64_t rows = (int64_t)B * T;
   int cpw = 4;
-  while (cpw > 1 && rows * ((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw)) < 2048)
+  while (cpw > 1 && rows * ((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw)) < 1024)
     cpw /= 2;
   dim3 grid((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw), (unsigned)rows);
 #define EV_LAUNCH_ACCEPT(R, C) hipLaunchKernelGGL((accept_kernel<R, C>), grid, dim3(256), 0, stream, a)

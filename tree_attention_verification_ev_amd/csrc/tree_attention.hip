@@ -82,16 +82,20 @@ template <int QT, int KS, typename KFrag>
 __device__ __forceinline__ void tile_scores(f32x16 (&s)[QT][2], const bf16x8 (&qf)[QT][KS],
                                             KFrag kfrag) {
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int t = 0; t < QT; ++t) s[t][st] = f32x16{};
+  // The two subtiles alternate, so consecutive products accumulate into different
+  // registers and do not wait on each other; each K fragment is read one product ahead.
+  bf16x8 kf = kfrag(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kf = kfrag(st, ks);
+  for (int i = 0; i < 2 * KS; ++i) {
+    const int st = i & 1, ks = i >> 1;
+    const bf16x8 cur = kf;
+    if (i + 1 < 2 * KS) kf = kfrag((i + 1) & 1, (i + 1) >> 1);
 #pragma unroll
-      for (int t = 0; t < QT; ++t)
-        s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][ks], s[t][st], 0, 0, 0);
-    }
+    for (int t = 0; t < QT; ++t)
+      s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[t][ks], s[t][st], 0, 0, 0);
   }
 }
 
@@ -554,6 +558,17 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposing LDS read of a V fragment.  The restrict-qualified pointer gives the read
+// alias-scope information; without it the compiler treats the read as possibly aliasing
+// every direct-to-LDS load in flight and puts a full vmcnt(0) before it, which would wait
+// out the tiles prefetched three steps ahead.  Ordering against the DMA is the kernel's
+// own: explicit vmcnt waits plus a barrier before any tile is read.
+__device__ __forceinline__ bf16x4 lds_read_tr(lds_bf16x4 *__restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
+}
+
 template <int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int D = 128;
@@ -713,9 +728,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     const __bf16 *vb = lds + decltype(stg)::value * 2 * MAT + MAT;
     tile_pv(o, pf, [&](int st, int kk, int dt) {
       const __bf16 *base = vb + (st * 32 + kk * 16) * D;
-      typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + voff[dt][0]));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + voff[dt][1]));
+      const bf16x4 lo = lds_read_tr((lds_bf16x4 *)(base + voff[dt][0]));
+      const bf16x4 hi = lds_read_tr((lds_bf16x4 *)(base + voff[dt][1]));
       return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     });
   };
@@ -765,17 +779,24 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
 }
 
 // Combine split partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
-// 32 lanes per row (sequence, node, head), D/32 head-dim elements per lane; the partials
-// are read in batches of 8 splits (all loads of a batch in flight together) and combined
+// D/E lanes per row (sequence, node, head), E head-dim elements per lane; the partials are
+// read in batches of BATCH splits (all loads of a batch in flight together) and combined
 // with a running maximum.
-template <int D>
+#ifndef EV_MERGE_E
+#define EV_MERGE_E 4
+#endif
+#ifndef EV_MERGE_BATCH
+#define EV_MERGE_BATCH 8
+#endif
+template <int D, int E, int BATCH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int E = D / 32;
-  constexpr int BATCH = 8;
+  constexpr int LPR = D / E;             // lanes per row
+  constexpr int RPB = 256 / LPR;         // rows per workgroup
   typedef _Float16 hE __attribute__((ext_vector_type(E)));
+  typedef __bf16 bE __attribute__((ext_vector_type(E)));
   const int64_t nrows = (int64_t)a.B * a.T * a.Hq;
-  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int c = threadIdx.x & 31;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
   if (row >= nrows) return;
   // Every split wrote its partial LSE (an empty split -inf), so all n_splits are read
   // without waiting for the sequence length.
@@ -814,9 +835,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     mx = bm;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  __bf16 *dst = (__bf16 *)a.out + row * D + c * E;
+  bE o;
 #pragma unroll
-  for (int e = 0; e < E; ++e) dst[e] = (__bf16)(acc[e] * inv);
+  for (int e = 0; e < E; ++e) o[e] = (__bf16)(acc[e] * inv);
+  *(bE *)((__bf16 *)a.out + row * D + c * E) = o;
   if (c == 0) a.lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
@@ -995,9 +1017,11 @@ static void launch_bf16(const Plan &p, const AttnArgs &a, bool q4, hipStream_t s
     launch_main<D, false, false>(p, a, stream);
   }
   if (p.n_splits > 1) {
-    int64_t nrows = (int64_t)a.B * a.T * a.Hq;
-    dim3 mgrid((unsigned)((nrows + 7) / 8));
-    hipLaunchKernelGGL((attn_merge_kernel<D>), mgrid, dim3(256), 0, stream, a);
+    constexpr int E = EV_MERGE_E * D / 128;
+    const int64_t nrows = (int64_t)a.B * a.T * a.Hq;
+    const int rows_per_wg = 256 / (D / E);
+    dim3 mgrid((unsigned)((nrows + rows_per_wg - 1) / rows_per_wg));
+    hipLaunchKernelGGL((attn_merge_kernel<D, E, EV_MERGE_BATCH>), mgrid, dim3(256), 0, stream, a);
   }
 }
 
@@ -1023,6 +1047,8 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return EV_ERR_ARG;
   if (B == 0) return EV_OK;
   if (!q || !prefix_len || !anc_mask || !out || !lse) return EV_ERR_NULL;
+  // rows of q, out and the cache are read and written in 16-byte pieces
+  if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)kv->k | (uintptr_t)kv->v) & 15) return EV_ERR_ARG;
   if ((int64_t)B * kv->n_kv_heads > (1 << 24)) return EV_ERR_SHAPE;
   ev::Plan p = ev::make_plan(addr, kv->dtype, B, T, Hq);
   size_t need = ev::workspace_bytes(p, B, T, Hq, kv->head_dim);
