@@ -579,7 +579,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int PER = 2 * IPW;                   // per wave per tile
   static_assert(IPW >= 1 && 2 * PER <= 63, "vmcnt range");
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT];
+  // kStages K|V tile pairs, then the sequence's ancestor masks (64 x 8 bytes)
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT + kMaxNodes * 4];
   __shared__ int stbl[PAGED ? kTableCache : 1];
 
   const int per_xcd = gridDim.x / kXcds;
@@ -636,22 +637,37 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  // Q^T fragments first, so the DMA traffic that follows is the only vmem in the loop.
-  bf16x8 qf[QT][KS];
-  uint64_t anc_q[QT];
-  {
-    const int r = row0 + qn;
-    const bool ok = r < rows;
-    const int node = ok ? r / a.G : 0;
-    const int head = g * a.G + (ok ? r % a.G : 0);
-    const __bf16 *src = Q + (((int64_t)b * a.T + node) * a.Hq + head) * D + 8 * hh;
+  bf16x8 qf[QT][KS];                             // filled from LDS in the prologue
+  uint64_t anc_q[QT];                            // likewise
+  // The sequence's ancestor masks, also global -> LDS by DMA (wave 0, 4-byte pieces),
+  // into the same LDS array as the tiles.
+  uint64_t *s_anc = (uint64_t *)(lds + kStages * 2 * MAT);
+  auto issue_anc = [&]() {
+    const uint32_t *src = (const uint32_t *)(a.anc + (int64_t)b * a.T);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 z = {};
-      qf[0][ks] = ok ? *(const bf16x8 *)(src + 16 * ks) : z;
+    for (int i = 0; i < 2; ++i)
+      if (64 * i + lane < 2 * a.T)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(src + 64 * i + lane),
+            (__attribute__((address_space(3))) void *)((uint32_t *)s_anc + 64 * i), 4, 0, 0);
+  };
+  // This wave's 32 query rows travel global -> LDS by DMA, whole rows at a time and
+  // chunk-swizzled like a K tile, into the area of stages 2 and 3 (idle until the third
+  // tile is issued); the Q^T fragments are then read from there.  Fetched as ordinary
+  // loads they would be scattered 16-byte gathers queued ahead of the K/V traffic, and
+  // the compiler would drain every DMA in flight before their first use.  Rows past the
+  // last one repeat it: their results are never written.
+  __bf16 *qlds = lds + 2 * 2 * MAT + wave * 32 * D;
+  auto issue_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < 32 * DCH / 64; ++i) {
+      const int rr = 4 * i + (lane >> 4), pc = lane & 15;
+      const int r = min(row0 + rr, rows - 1);
+      const int node = r / a.G, head = g * a.G + r % a.G;
+      dma16(Q + (((int64_t)b * a.T + node) * a.Hq + head) * D + ((pc ^ (rr & 15)) << 3),
+            qlds + i * 512);
     }
-    anc_q[0] = ok ? a.anc[(int64_t)b * a.T + node] : 0ull;
-  }
+  };
 
   // Lane-constant parts of this wave's DMA: instruction i fills 1 KB block wave*IPW + i of
   // a tile, i.e. key rows 4*(wave*IPW + i) .. +3; lane l takes row key_i, physical chunk
@@ -761,9 +777,24 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     return more;
   };
 
-  // prologue: three tiles in flight, scores of the first
+  // prologue: Q and the first two tiles in flight; once this wave's Q rows have landed
+  // its fragments are read, and after every wave has them the third tile goes into the
+  // area they occupied; then the scores of the first tile.
+  if (wave == 0) issue_anc();
+  issue_q();
   issue(t_begin, 0);
-  if (t_begin + 1 < t_end) issue(t_begin + 1, 1);
+  if (t_begin + 1 < t_end) {
+    issue(t_begin + 1, 1);
+    wait_vm<2 * PER>();                          // masks and Q landed (this wave's own rows)
+  } else {
+    wait_vm<PER>();
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[0][ks] = *(const bf16x8 *)(qlds + qn * D + ((((2 * ks) | hh) ^ (qn & 15)) << 3));
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wg_barrier();                                  // every wave holds its Q: stages 2, 3 free
+  anc_q[0] = row0 + qn < rows ? s_anc[(row0 + qn) / a.G] : 0ull;
   if (t_begin + 2 < t_end) issue(t_begin + 2, 2);
   landed(min(t_end - 1, t_begin + 2) - t_begin);
   wg_barrier();
