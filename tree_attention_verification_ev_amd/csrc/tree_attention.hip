@@ -569,6 +569,80 @@ __device__ __forceinline__ bf16x4 lds_read_tr(lds_bf16x4 *__restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
 }
 
+// write_rows for the DMA kernel (one query tile per wave): the wave's 32 normalised rows
+// go through an idle 8 KB of LDS (chunk-swizzled like a K tile) so that the global stores
+// are whole rows, 16 bytes per lane and four rows per instruction, instead of 8-byte pieces
+// scattered over 32 rows.  Values, rounding and the partial-split format are write_rows'.
+template <int D>
+__device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x16 (&o)[1][D / 32],
+                                                  float mref, float l, int row0, int b, int g,
+                                                  int split, int qn, int hh, uint16_t *stage) {
+  constexpr int DT = D / 32, DCH = D / 8;
+  const int lane = threadIdx.x & 63;
+  const int rows = a.T * a.G;
+  const float ltot = l + __shfl_xor(l, 32);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const float lse = ltot > 0.f ? (mref + __log2f(ltot)) * kLn2 : -INFINITY;
+  const bool part = a.n_splits > 1;
+  float k = inv, scale = 1.f;
+  if (part) {
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[0][dt][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+    scale = fmaxf(1.f, amax);
+    k = inv / scale;
+  }
+  // this lane's values: row qn, head dims dt*32 + 8j + 4hh + 0..3 = half hh of chunk 4dt + j
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x16 &ov = o[0][dt];
+      uint32_t w0, w1;
+      if (part) {
+        const f16x4 h = f16x4{(_Float16)(ov[4 * j] * k), (_Float16)(ov[4 * j + 1] * k),
+                              (_Float16)(ov[4 * j + 2] * k), (_Float16)(ov[4 * j + 3] * k)};
+        w0 = __builtin_bit_cast(u32x2, h)[0];
+        w1 = __builtin_bit_cast(u32x2, h)[1];
+      } else {
+        const bf16x4 h = bf16x4{(__bf16)(ov[4 * j] * k), (__bf16)(ov[4 * j + 1] * k),
+                                (__bf16)(ov[4 * j + 2] * k), (__bf16)(ov[4 * j + 3] * k)};
+        w0 = __builtin_bit_cast(u32x2, h)[0];
+        w1 = __builtin_bit_cast(u32x2, h)[1];
+      }
+      const int pc = (4 * dt + j) ^ (qn & 15);
+      *(u32x2 *)(stage + qn * D + pc * 8 + 4 * hh) = u32x2{w0, w1};
+    }
+  // whole rows back out: lane takes row 4i + lane/16, chunk lane%16
+#pragma unroll
+  for (int i = 0; i < 32 * DCH / 64; ++i) {
+    const int rr = 4 * i + (lane >> 4), cc = lane & 15;
+    const int r = row0 + rr;
+    const u32x4 v = *(const u32x4 *)(stage + rr * D + ((cc ^ (rr & 15)) << 3));
+    if (r < rows) {
+      const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
+      if (part)
+        *(u32x4 *)(a.part_o + ((int64_t)split * a.B * a.T * a.Hq + orow) * D + cc * 8) = v;
+      else
+        *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = v;
+    }
+  }
+  const int r = row0 + qn;
+  if (hh == 0 && r < rows) {
+    const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
+    if (part) {
+      const int64_t prow = (int64_t)split * a.B * a.T * a.Hq + orow;
+      a.part_lse[prow] = lse;
+      a.part_scale[prow] = scale;
+    } else {
+      a.lse[orow] = lse;
+    }
+  }
+}
+
 template <int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int D = 128;
@@ -806,7 +880,13 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     if (!step(j + 2, sa, sb, S2{})) break;
     if (!step(j + 3, sb, sa, S3{})) break;
   }
-  write_rows<D, QT>(a, o, mref, l, row0, b, g, split, qn, hh);
+  // Once a wave has left the loop, the others are at most one step behind: they may still
+  // read the stages of the last two tiles, never the two after them, and no DMA is in
+  // flight.  Those two stages hold the waves' output rows (8 KB each).
+  const int last = (t_end - 1 - t_begin) % kStages;
+  uint16_t *stage = (uint16_t *)(lds + ((last + 1 + (wave >> 2)) % kStages) * 2 * MAT +
+                                 (wave & 3) * 32 * D);
+  write_rows_staged<D>(a, o, mref[0], l[0], row0, b, g, split, qn, hh, stage);
 }
 
 // Combine split partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
