@@ -59,13 +59,19 @@ struct AttnArgs {
   int n_work;              // B * Hkv * row_blocks * n_splits
   void *out;               // final O (n_splits == 1)
   float *lse;              // final LSE (n_splits == 1)
-  _Float16 *part_o;        // [n_splits][B][T][Hq][D], scaled by 1 / part_scale
-  float *part_lse;         // [n_splits][B][T][Hq]
-  float *part_scale;       // [n_splits][B][T][Hq]
+  _Float16 *part_o;        // [B][T][Hq][n_splits][D], scaled by 1 / part_scale
+  float *part_lse;         // [B][T][Hq][n_splits]
+  float *part_scale;       // [B][T][Hq][n_splits]
   int32_t *dev_status;
   const float *k_scale;    // INT4 caches: one scale per (slot, KV head) row
   const float *v_scale;
 };
+
+// Row of split `split`'s partial for output row `orow` ((sequence, node, head) order): the
+// partials of one output row are adjacent, so the merge reads one contiguous block.
+__device__ inline int64_t part_row(const AttnArgs &a, int64_t orow, int split) {
+  return orow * a.n_splits + split;
+}
 
 // Is logical slot `slot` visible to a query whose ancestor row is `anc` (prefix length L)?
 __device__ inline bool visible(int slot, int L, uint64_t anc) {
@@ -230,7 +236,7 @@ __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[
       const float scale = fmaxf(1.f, amax);
       const float k = inv / scale;
       if (!ok) continue;
-      const int64_t prow = (int64_t)split * a.B * a.T * a.Hq + orow;
+      const int64_t prow = part_row(a, orow, split);
       _Float16 *dst = a.part_o + prow * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -447,7 +453,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
         const int r = row0 + t * 32 + qn;
         if (r >= rows) continue;
         const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
-        a.part_lse[(int64_t)split * a.B * a.T * a.Hq + orow] = -INFINITY;
+        a.part_lse[part_row(a, orow, split)] = -INFINITY;
       }
     }
     return;
@@ -625,7 +631,7 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
     if (r < rows) {
       const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
       if (part)
-        *(u32x4 *)(a.part_o + ((int64_t)split * a.B * a.T * a.Hq + orow) * D + cc * 8) = v;
+        *(u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8) = v;
       else
         *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = v;
     }
@@ -634,7 +640,7 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
   if (hh == 0 && r < rows) {
     const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
     if (part) {
-      const int64_t prow = (int64_t)split * a.B * a.T * a.Hq + orow;
+      const int64_t prow = part_row(a, orow, split);
       a.part_lse[prow] = lse;
       a.part_scale[prow] = scale;
     } else {
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     if (a.n_splits > 1 && hh == 0 && row0 + qn < rows) {
       const int r = row0 + qn;
       const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
-      a.part_lse[(int64_t)split * a.B * a.T * a.Hq + orow] = -INFINITY;
+      a.part_lse[part_row(a, orow, split)] = -INFINITY;
     }
     return;
   }
@@ -921,9 +927,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     for (int u = 0; u < BATCH; ++u) {
       const int s = s0 + u;
       const bool ok = s < nvalid;
-      ls[u] = ok ? a.part_lse[s * nrows + row] : -INFINITY;
-      sc[u] = ok ? a.part_scale[s * nrows + row] : 0.f;
-      x[u] = ok ? *(const hE *)(a.part_o + (s * nrows + row) * D + c * E) : hE{};
+      ls[u] = ok ? a.part_lse[row * nvalid + s] : -INFINITY;
+      sc[u] = ok ? a.part_scale[row * nvalid + s] : 0.f;
+      x[u] = ok ? *(const hE *)(a.part_o + (row * nvalid + s) * D + c * E) : hE{};
     }
     float bm = mx;
 #pragma unroll
