@@ -108,6 +108,12 @@ ATTN_SMALL = [
     ("bf16_d64", scaled(C3, d=64, L=333, V=64)),
     ("f32_d128", scaled(C1, d=128, L=190, Hq=8, Hkv=2, V=64)),
     ("gqa4_T26", scaled(C2, Hq=32, Hkv=8, L=515, V=64)),
+    # 64 rows per KV head: the two-wavefront DMA workgroup
+    ("gqa8_T8", scaled(C3, T=8, L=257, V=64)),
+    # 320 rows per KV head: the second eight-wavefront workgroup has six waves with no row
+    ("gqa8_T40", scaled(C3, T=40, L=190, V=64)),
+    # paged, 104 rows per KV head: the four-wavefront DMA workgroup over a block table
+    ("paged_gqa4_T26", scaled(C4, B=2, T=26, Hq=32, Hkv=8, L=(100, 700), V=64)),
 ]
 
 
