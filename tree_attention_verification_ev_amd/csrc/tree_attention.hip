@@ -1069,10 +1069,15 @@ static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq) {
   // An INT4 tile is dequantised by every thread of the workgroup while staging: at least
   // four wavefronts share that work even when fewer own query rows.
   if (dtype == EV_INT4) p.nw = std::max(p.nw, 4);
+  // bf16 with d = 128 always takes the direct-to-LDS kernel, whose smallest workgroup has
+  // two wavefronts (with at most 32 rows per KV head the second owns none and only shares
+  // the DMA issue); its 128 KB of LDS leave room for one workgroup per CU.
+  const bool dma = dtype == EV_BF16 && kv.d == 128 && p.qt == 1;
+  if (dma) p.nw = std::max(p.nw, 2);
   p.row_blocks = (waves_needed + p.nw - 1) / p.nw;
   const int max_tiles = (max_slots(kv) + kKT - 1) / kKT;
   const int units = B * kv.hkv * p.row_blocks;
-  const int slots = p.nw >= 4 ? kCUs : (p.nw == 2 ? 2 * kCUs : 4 * kCUs);
+  const int slots = dma || p.nw >= 4 ? kCUs : (p.nw == 2 ? 2 * kCUs : 4 * kCUs);
   int splits = std::max(1, slots / units);
   splits = std::min(splits, std::min(kMaxSplits, max_tiles));
   int tps = (max_tiles + splits - 1) / splits;
