@@ -158,6 +158,51 @@ def kernel_times(sets, reps):
     return out
 
 
+def box_peaks(reps: int = 3):
+    """What this GPU sustains, for rooflines against the box as well as the published peaks:
+    the bf16 matrix-core rate of a register-operand MFMA loop (four independent
+    32x32x16 products per wavefront, 4 wavefronts per CU-slot) and the bandwidths of a
+    16-byte grid-stride copy and read of 2 GiB; each is the best of `reps` timed launches."""
+    n_wg, iters = 1024, 20000
+    flops = n_wg * 4 * iters * 4 * 32768
+    sink = torch.empty(n_wg, dtype=torch.float32, device="cuda")
+    ev.ev_peak_mfma_bf16(n_wg, 200, sink)
+    mfma = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ev.ev_peak_mfma_bf16(n_wg, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        mfma = max(mfma, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ev.ev_peak_copy(src, dst)
+    copy = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ev.ev_peak_copy(src, dst)
+        e1.record()
+        torch.cuda.synchronize()
+        copy = max(copy, 2 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    sink_r = torch.empty(64 * 256, dtype=torch.int32, device="cuda")
+    read = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ev.ev_peak_read(src, sink_r)
+        e1.record()
+        torch.cuda.synchronize()
+        read = max(read, src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return {"mfma_bf16_tflops": mfma, "copy_gbps": copy, "read_gbps": read,
+            "method": "ev_peak_mfma_bf16 (1024 workgroups x 20000 rounds), ev_peak_copy "
+                      "(2 GiB, read + write counted) and ev_peak_read (2 GiB, 16384 workgroups), "
+                      "best of 3 each"}
+
+
 def _counter_values(csv_path, counter):
     """Per-dispatch values of one counter in a rocprofv3 counter_collection.csv, by kernel."""
     import csv
@@ -650,6 +695,7 @@ def main():
         bound, peak, unit = "alu", PEAK_F32_TFLOPS, "TFLOP/s"
         achieved = work["flops"] / t_attn / 1e12
     kv_gbps = work["bytes"] / t_attn / 1e9
+    box = box_peaks()
     result = {
         "metric": METRIC,
         "value": nodes / (ms_per_step * 1e-3),
@@ -664,9 +710,13 @@ def main():
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic_entry(),
                      "kernel": "ev_tree_attention", "algorithmic_flops": work["flops"],
-                     "algorithmic_bytes": work["bytes"]},
+                     "algorithmic_bytes": work["bytes"],
+                     "frac_of_box_peak": achieved / (box["mfma_bf16_tflops"] if bound == "mfma"
+                                                     else peak)},
         "kv_hbm_gbps": kv_gbps,
         "kv_hbm_frac": kv_gbps / PEAK_HBM_GBPS,
+        "kv_hbm_frac_of_box_read": kv_gbps / box["read_gbps"],
+        "box_peaks": box,
         "attention_nodes_per_s": nodes / t_attn,
         "kernels_us": {k: round(v["mean_us"], 3) for k, v in kt.items()},
         "kernels_us_p10_p90": {k: [round(v["p10_us"], 3), round(v["p90_us"], 3)] for k, v in kt.items()},

@@ -32,6 +32,25 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_exports_calibration_kernels(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ev_peaks.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(ev_[a-z0-9_]+)\s*\(", text)))
+    assert set(names) == set(ev.EXPORTED_PEAKS)
+    for name in names:
+        assert hasattr(lib, name), name
+    P = 0x1000
+    assert lib.ev_peak_mfma_bf16(0, 10, P, None) == 2
+    assert lib.ev_peak_mfma_bf16(4, 0, P, None) == 2
+    assert lib.ev_peak_mfma_bf16(4, 10, None, None) == 1
+    assert lib.ev_peak_copy(None, P, 16, None) == 1
+    assert lib.ev_peak_copy(P + 8, P, 16, None) == 5
+    assert lib.ev_peak_copy(P, P, 24, None) == 5
+    assert lib.ev_peak_copy(P, P, 0, None) == 0
+    assert lib.ev_peak_read(None, 16, P, 4, None) == 1
+    assert lib.ev_peak_read(P, 20, P, 4, None) == 5
+    assert lib.ev_peak_read(P, 16, P, 0, None) == 2
+
+
 def test_status_strings(lib):
     for code in ev.STATUS_NAMES:
         assert ev.ev_status_string(code) not in ("", "unknown status")

@@ -36,6 +36,8 @@ EXPORTED = (
     "ev_draft_tree_workspace", "ev_draft_tree_expand", "ev_draft_tree_finalize",
     "ev_status_string",
 )
+# include/ev_peaks.h: calibration kernels (box-measured peaks), not part of the pass
+EXPORTED_PEAKS = ("ev_peak_mfma_bf16", "ev_peak_copy", "ev_peak_read")
 
 
 class EvError(RuntimeError):
@@ -90,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "ev_draft_tree_finalize": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ,
                                               _P]),
             "ev_status_string": (ctypes.c_char_p, [_I32]),
+            "ev_peak_mfma_bf16": (_I32, [_I32, _I32, _P, _P]),
+            "ev_peak_copy": (_I32, [_P, _P, _SZ, _P]),
+            "ev_peak_read": (_I32, [_P, _SZ, _P, _I32, _P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(handle, name)
@@ -435,4 +440,32 @@ def ev_status_string(code: int) -> str:
     return lib().ev_status_string(code).decode()
 
 
-__all__ = ["KvCache", "EvError", "EvKvDesc", "lib", "LIB_PATH", *EXPORTED]
+def ev_peak_mfma_bf16(n_workgroups: int, iters: int, sink: torch.Tensor) -> None:
+    """Enqueue the bf16 matrix-core loop (n_workgroups * 4 * iters * 4 * 32768 flops)."""
+    _dev(sink, "sink", torch.float32)
+    if sink.numel() < n_workgroups:
+        raise ValueError("sink needs one float per workgroup")
+    _finish(lib().ev_peak_mfma_bf16(n_workgroups, iters, sink.data_ptr(), _stream(sink.device)),
+            "ev_peak_mfma_bf16", None, False)
+
+
+def ev_peak_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Enqueue a copy of src's bytes into dst (16-byte pieces)."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _finish(lib().ev_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src.device)),
+            "ev_peak_copy", None, False)
+
+
+def ev_peak_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Enqueue a read of src's bytes by sink.numel() workgroups (one uint32 each into sink)."""
+    _dev(src, "src")
+    _dev(sink, "sink", torch.int32)
+    _finish(lib().ev_peak_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                               sink.numel(), _stream(src.device)), "ev_peak_read", None, False)
+
+
+__all__ = ["KvCache", "EvError", "EvKvDesc", "lib", "LIB_PATH", *EXPORTED, *EXPORTED_PEAKS]
