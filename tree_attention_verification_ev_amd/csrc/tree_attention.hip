@@ -9,10 +9,15 @@
 //   * Work unit = (sequence, KV head, block of query rows, range of key tiles).  The rows
 //     of a unit are the T*G (node, q-head-in-group) pairs that share one KV head, so a
 //     grouped-query layer reuses each K/V byte G*T times inside one workgroup.
-//   * Workgroups of NW wavefronts stage 64-key tiles of K (row-major) and V (transposed)
-//     in LDS; with NW >= 2 the LDS is double-buffered and the next tile's global loads
-//     are in flight (in registers) while the current tile is computed.  Each wavefront
-//     owns QT tiles of 32 query rows.
+//   * bf16 with d = 128 (tree_attn_dma_kernel): workgroups of 2, 4 or 8 wavefronts of 32
+//     query rows; 64-key K and V tiles go global -> LDS by direct-to-LDS loads through a
+//     4-stage ring (three tiles in flight), XOR-swizzled so the fragment reads are
+//     bank-conflict-free; V fragments come from the LDS transpose read.  The query rows
+//     and ancestor masks also arrive by DMA, and the output rows leave through LDS as whole
+//     rows, so the kernel issues no ordinary global loads.
+//   * d = 64 and the INT4 cache (tree_attn_bf16_kernel): the same products with tiles
+//     staged through registers (the INT4 tile dequantised on its way to LDS), double
+//     buffered, the next tile's loads in flight while the current one is computed.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the
 //     accumulator column is the query, so each lane holds 16 keys of ONE query and the
 //     softmax statistics, the output rescale and the final normalisation are lane-local
@@ -26,9 +31,10 @@
 //   * Only tiles reaching past the prefix apply the ancestor bitmask.
 //   * 1-D grid with an XCD-aware order: the row blocks of one (sequence, head, split) are
 //     dispatched to the same XCD and so share its L2 for the K/V tiles.
-//   * Long prefixes are split across workgroups; each split writes its normalised partial
-//     O in fp16 (pre-divided by max(1, |O|max) of the row, the divisor kept in float32) and
-//     its LSE; a merge kernel combines the splits.
+//   * Long prefixes are split across workgroups (sized for one workgroup per CU in the DMA
+//     kernel); each split writes its normalised partial O in fp16 (pre-divided by
+//     max(1, |O|max) of the row, the divisor kept in float32) and its LSE, adjacent to the
+//     other splits of the same row; a merge kernel combines them.
 // float32 path: a plain VALU kernel (one wavefront per (sequence, head, node)).
 #include "ev_internal.h"
 
