@@ -63,6 +63,8 @@ __device__ inline double shifted(float logit, double inv_tau, double M) {
 }
 
 // Lane's 16 logits of chunk `base`: element (k*64 + lane)*4 + e, k < 4, e < 4 (coalesced).
+// NT: non-temporal 16-byte loads, for a row read once by a launch.
+template <bool NT = false>
 __device__ inline void load_chunk(const float *row, int V, int base, bool vec_ok, float v[16],
                                   int idx[16]) {
   const int lane = threadIdx.x & 63;
@@ -70,7 +72,8 @@ __device__ inline void load_chunk(const float *row, int V, int base, bool vec_ok
   for (int k = 0; k < 4; ++k) {
     int i0 = base + (k * 64 + lane) * 4;
     if (vec_ok && i0 + 3 < V) {
-      f32x4 x = *(const f32x4 *)(row + i0);
+      const f32x4 x = NT ? __builtin_nontemporal_load((const f32x4 *)(row + i0))
+                         : *(const f32x4 *)(row + i0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[4 * k + e] = x[e];

@@ -636,8 +636,8 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
     const u32x4 v = *(const u32x4 *)(stage + rr * D + ((cc ^ (rr & 15)) << 3));
     if (r < rows) {
       const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
-      if (part)
-        *(u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8) = v;
+      if (part)   // read once, by the merge kernel: stored non-temporally
+        __builtin_nontemporal_store(v, (u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8));
       else
         *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = v;
     }
