@@ -27,6 +27,7 @@
 #include "rowstream.h"
 
 #include <limits.h>
+#include <type_traits>
 #include <math.h>
 
 namespace ev {
@@ -242,13 +243,16 @@ __device__ void finish_sequence(const Args &a, int b, int tok) {
   if (lane == 0) a.accept_len[b] = k;
 }
 
-// Statistics of one 1024-logit chunk (already in registers) of row `row`.
+// Statistics of one 1024-logit chunk (already in registers), the same in every lane:
+// greedy, the (max, lowest argmax) word; rejection, float64 (M_c = max s, S_c = sum exp(s - M_c)).
 template <bool REJ>
-__device__ __forceinline__ void chunk_stats(const AcceptArgs &a, int64_t row, int chunk,
-                                            const float (&v)[16], const double *tab) {
+using ChunkStat = typename std::conditional<REJ, RejStat, uint64_t>::type;
+
+template <bool REJ>
+__device__ __forceinline__ ChunkStat<REJ> chunk_stats(const AcceptArgs &a, int chunk,
+                                                      const float (&v)[16], const double *tab) {
   const int lane = threadIdx.x & 63;
-  const int nc = a.n_chunks;
-  if (!REJ) {
+  if constexpr (!REJ) {
     // a lane visits its ids in increasing order, so a strict > keeps the lowest index
     float best = -INFINITY;
     int bi = INT_MAX;
@@ -259,7 +263,7 @@ __device__ __forceinline__ void chunk_stats(const AcceptArgs &a, int64_t row, in
       bi = gt ? chunk * kChunk + ((e >> 2) * 64 + lane) * 4 + (e & 3) : bi;
     }
     wave_argmax(best, bi);
-    if (lane == 0) publish((uint64_t *)a.stats + row * nc + chunk, pack(GreedyStat{best, bi}));
+    return pack(GreedyStat{best, bi});
   } else {
     float best = -INFINITY;
 #pragma unroll
@@ -270,19 +274,23 @@ __device__ __forceinline__ void chunk_stats(const AcceptArgs &a, int64_t row, in
     double sum = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sum += exp_nonpos(shifted(v[e], a.inv_tau, M), tab);
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      RejStat *dst = (RejStat *)a.stats + row * nc + chunk;
-      publish(&dst->M, M);
-      publish(&dst->S, sum);
-    }
+    return RejStat{M, wave_sum(sum)};
   }
+}
+
+__device__ inline void publish_stat(const AcceptArgs &a, int64_t row, int chunk, uint64_t st) {
+  publish((uint64_t *)a.stats + row * a.n_chunks + chunk, st);
+}
+__device__ inline void publish_stat(const AcceptArgs &a, int64_t row, int chunk, RejStat st) {
+  RejStat *dst = (RejStat *)a.stats + row * a.n_chunks + chunk;
+  publish(&dst->M, st.M);
+  publish(&dst->S, st.S);
 }
 
 // grid (chunk groups, rows); a workgroup's four wavefronts stream CPW chunks each, the
 // wavefronts of a workgroup interleaved chunk by chunk, with the next chunk's loads in
 // flight while the current one is reduced.
-template <bool REJ, int CPW>
+template <bool REJ, int CPW, bool VEC>
 __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ double tab[64];
   __shared__ int s_last;
@@ -305,21 +313,35 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
 
   // ---- this wavefront's chunk statistics ----
   const float *lrow = a.logits + row * a.V;
-  const bool vec_ok = (a.V & 3) == 0;
-  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
+  // the wavefront's first chunk, uniform across its lanes (so are the branches below)
+  const int c0 = __builtin_amdgcn_readfirstlane(blockIdx.x * kChunksPerWG * CPW + wave);
   float v[2][16];
   int idx_unused[16];
   // Non-temporal loads with two chunks per wavefront, cached loads otherwise (measured, one
   // sequence of 64 rows x 128256 logits, two chunks: 18.9 -> 18.6 us; 26 rows x 32000, one
   // chunk: 6.9 -> 7.2 us; 256 rows x 128256, four chunks: 43.1 -> 45.3 us).
   constexpr bool kNT = CPW == 2;
-  if (c0 < nc) load_chunk<kNT>(lrow, a.V, c0 * kChunk, vec_ok, v[0], idx_unused);
+  // Every wavefront issues all CPW chunk loads, each while the chunk before it is being
+  // reduced, and publishes its statistics only at the end: a load or store under a branch,
+  // or a store between the loads, made the compiler wait for the chunk still in flight.
+  // A chunk past the row's end (last workgroup of a row) loads the row's last chunk and is
+  // not reduced.
+  ChunkStat<REJ> st[CPW];
+  load_chunk_raw<kNT, VEC>(lrow, a.V, min(c0, nc - 1) * kChunk, v[0]);
 #pragma unroll
   for (int m = 0; m < CPW; ++m) {
     const int c = c0 + kChunksPerWG * m;
-    if (m + 1 < CPW && c + kChunksPerWG < nc)
-      load_chunk<kNT>(lrow, a.V, (c + kChunksPerWG) * kChunk, vec_ok, v[(m + 1) & 1], idx_unused);
-    if (c < nc) chunk_stats<REJ>(a, row, c, v[m & 1], tab);
+    if (m + 1 < CPW)
+      load_chunk_raw<kNT, VEC>(lrow, a.V, min(c + kChunksPerWG, nc - 1) * kChunk, v[(m + 1) & 1]);
+    if (c < nc) {
+      mask_chunk(a.V, c * kChunk, v[m & 1], idx_unused);
+      st[m] = chunk_stats<REJ>(a, c, v[m & 1], tab);
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < CPW; ++m)
+      if (c0 + kChunksPerWG * m < nc) publish_stat(a, row, c0 + kChunksPerWG * m, st[m]);
   }
   if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
 
@@ -360,7 +382,12 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
   while (cpw > 1 && rows * ((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw)) < 1024)
     cpw /= 2;
   dim3 grid((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw), (unsigned)rows);
-#define EV_LAUNCH_ACCEPT(R, C) hipLaunchKernelGGL((accept_kernel<R, C>), grid, dim3(256), 0, stream, a)
+  const bool vec = (V & 3) == 0;          // rows start 16-byte aligned
+#define EV_LAUNCH_ACCEPT(R, C)                                                                \
+  do {                                                                                        \
+    if (vec) hipLaunchKernelGGL((accept_kernel<R, C, true>), grid, dim3(256), 0, stream, a);  \
+    else hipLaunchKernelGGL((accept_kernel<R, C, false>), grid, dim3(256), 0, stream, a);     \
+  } while (0)
   if (rej) {
     if (cpw == 4) EV_LAUNCH_ACCEPT(true, 4);
     else if (cpw == 2) EV_LAUNCH_ACCEPT(true, 2);
@@ -588,14 +615,13 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
   const float *lq = a.draft + row * a.V;
   const bool vec_ok = (a.V & 3) == 0;
   int idx_unused[16];
-  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
+  const int c0 = __builtin_amdgcn_readfirstlane(blockIdx.x * kChunksPerWG * CPW + wave);
 #pragma unroll
   for (int m = 0; m < CPW; ++m) {
     const int c = c0 + kChunksPerWG * m;
     if (c >= nc) continue;
     float vp[16], vq[16];
-    load_chunk(lp, a.V, c * kChunk, vec_ok, vp, idx_unused);
-    load_chunk(lq, a.V, c * kChunk, vec_ok, vq, idx_unused);
+    load_pair(lp, lq, a.V, c * kChunk, vec_ok, vp, vq, idx_unused);
     float bp = -INFINITY, bq = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -692,14 +718,13 @@ __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
   const bool vec_ok = (a.V & 3) == 0;
   const double inv_sp = 1.0 / st.Sp, inv_sq = 1.0 / st.Sq;
   int idx_unused[16];
-  const int c0 = blockIdx.x * kChunksPerWG * CPW + wave;
+  const int c0 = __builtin_amdgcn_readfirstlane(blockIdx.x * kChunksPerWG * CPW + wave);
 #pragma unroll
   for (int m = 0; m < CPW; ++m) {
     const int c = c0 + kChunksPerWG * m;
     if (c >= nc) continue;
     float vp[16], vq[16];
-    load_chunk(lp, a.V, c * kChunk, vec_ok, vp, idx_unused);
-    load_chunk(lq, a.V, c * kChunk, vec_ok, vq, idx_unused);
+    load_pair(lp, lq, a.V, c * kChunk, vec_ok, vp, vq, idx_unused);
     double w = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) w += residual_weight(vp[e], vq[e], a, st, inv_sp, inv_sq, tab);

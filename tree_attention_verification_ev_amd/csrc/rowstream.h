@@ -62,32 +62,64 @@ __device__ inline double shifted(float logit, double inv_tau, double M) {
   return fma((double)logit, inv_tau, -M);
 }
 
-// Lane's 16 logits of chunk `base`: element (k*64 + lane)*4 + e, k < 4, e < 4 (coalesced).
-// NT: non-temporal 16-byte loads, for a row read once by a launch.
-template <bool NT = false>
-__device__ inline void load_chunk(const float *row, int V, int base, bool vec_ok, float v[16],
-                                  int idx[16]) {
+// Lane's 16 logits of chunk `base` are elements (k*64 + lane)*4 + e, k < 4, e < 4
+// (coalesced).  load_chunk_raw only issues the loads: an element past the row's end loads
+// an in-bounds address instead, and mask_chunk later turns it into -inf.  No load sits
+// under a lane-dependent branch, and the selects come after the caller has issued its next
+// loads.  (A per-lane branch around each load, with the selects inside it, made the
+// compiler wait for every load in flight, a prefetched chunk's included, before each new
+// load.)  VEC: V is a multiple of 4, so each 16-byte piece lies wholly inside the row or
+// wholly past its end.  NT: non-temporal loads, for a row read once by a launch.
+template <bool NT, bool VEC>
+__device__ inline void load_chunk_raw(const float *row, int V, int base, float v[16]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    int i0 = base + (k * 64 + lane) * 4;
-    if (vec_ok && i0 + 3 < V) {
-      const f32x4 x = NT ? __builtin_nontemporal_load((const f32x4 *)(row + i0))
-                         : *(const f32x4 *)(row + i0);
+    const int i0 = base + (k * 64 + lane) * 4;
+    if constexpr (VEC) {
+      const f32x4 *p = (const f32x4 *)(row + min(i0, V - 4));
+      const f32x4 x = NT ? __builtin_nontemporal_load(p) : *p;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[4 * k + e] = x[e];
-        idx[4 * k + e] = i0 + e;
-      }
+      for (int e = 0; e < 4; ++e) v[4 * k + e] = x[e];
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int i = i0 + e;
-        v[4 * k + e] = i < V ? row[i] : -INFINITY;
-        idx[4 * k + e] = i < V ? i : INT_MAX;
-      }
+      for (int e = 0; e < 4; ++e) v[4 * k + e] = row[min(i0 + e, V - 1)];
     }
   }
+}
+
+__device__ inline void mask_chunk(int V, int base, float v[16], int idx[16]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = base + (k * 64 + lane) * 4 + e;
+      v[4 * k + e] = i < V ? v[4 * k + e] : -INFINITY;
+      idx[4 * k + e] = i < V ? i : INT_MAX;
+    }
+}
+
+// The same chunk of two rows: both rows' loads are in flight before either is masked.
+__device__ inline void load_pair(const float *ra, const float *rb, int V, int base, bool vec_ok,
+                                 float va[16], float vb[16], int idx[16]) {
+  if (vec_ok) {
+    load_chunk_raw<false, true>(ra, V, base, va);
+    load_chunk_raw<false, true>(rb, V, base, vb);
+  } else {
+    load_chunk_raw<false, false>(ra, V, base, va);
+    load_chunk_raw<false, false>(rb, V, base, vb);
+  }
+  mask_chunk(V, base, va, idx);
+  mask_chunk(V, base, vb, idx);
+}
+
+// Both steps at once; vec_ok (V a multiple of 4) is the same for every lane.
+__device__ inline void load_chunk(const float *row, int V, int base, bool vec_ok, float v[16],
+                                  int idx[16]) {
+  if (vec_ok) load_chunk_raw<false, true>(row, V, base, v);
+  else load_chunk_raw<false, false>(row, V, base, v);
+  mask_chunk(V, base, v, idx);
 }
 
 // (value, index) pairs: larger value wins, equal values keep the lower index (selects,
