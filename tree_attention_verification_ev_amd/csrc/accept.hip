@@ -317,10 +317,11 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   const int c0 = __builtin_amdgcn_readfirstlane(blockIdx.x * kChunksPerWG * CPW + wave);
   float v[2][16];
   int idx_unused[16];
-  // Non-temporal loads with two chunks per wavefront, cached loads otherwise (measured, one
-  // sequence of 64 rows x 128256 logits, two chunks: 18.9 -> 18.6 us; 26 rows x 32000, one
-  // chunk: 6.9 -> 7.2 us; 256 rows x 128256, four chunks: 43.1 -> 45.3 us).
-  constexpr bool kNT = CPW == 2;
+  // Non-temporal loads with one or two chunks per wavefront, cached loads with four
+  // (measured against cached loads: 64 rows x 128256 logits, two chunks, 18.4 -> 17.5 us;
+  // 26 rows x 32000, one chunk, 6.47 -> 6.28 us; 256 rows x 128256, four chunks, 39.5 ->
+  // 41.0 us).
+  constexpr bool kNT = CPW <= 2;
   // Every wavefront issues all CPW chunk loads, each while the chunk before it is being
   // reduced, and publishes its statistics only at the end: a load or store under a branch,
   // or a store between the loads, made the compiler wait for the chunk still in flight.
