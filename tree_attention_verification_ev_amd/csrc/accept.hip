@@ -599,7 +599,7 @@ __device__ bool sampled_decide(const SampledArgs &a, int64_t row, const SampledR
 
 // Statistics launch: per-chunk (M, S) of both rows; the row's last workgroup validates
 // the tree and sets up the row state.
-template <int CPW>
+template <int CPW, bool VEC>
 __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
   __shared__ double tab[64];
   __shared__ int s_last;
@@ -614,36 +614,57 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
   __syncthreads();
   const float *lp = a.logits + row * a.V;
   const float *lq = a.draft + row * a.V;
-  const bool vec_ok = (a.V & 3) == 0;
   int idx_unused[16];
   const int c0 = __builtin_amdgcn_readfirstlane(blockIdx.x * kChunksPerWG * CPW + wave);
+  // As in the acceptance stream: the next chunk's loads of both rows are issued before the
+  // current chunk is reduced, unconditionally (a chunk past the row's end reloads the last
+  // one and is not reduced), and the statistics are stored once at the end.
+  float vp[2][16], vq[2][16];
+  RejStat stp[CPW], stq[CPW];
+  load_chunk_raw<false, VEC>(lp, a.V, min(c0, nc - 1) * kChunk, vp[0]);
+  load_chunk_raw<false, VEC>(lq, a.V, min(c0, nc - 1) * kChunk, vq[0]);
+  __builtin_amdgcn_sched_barrier(0);     // keep the first chunk's loads ahead of the next's
 #pragma unroll
   for (int m = 0; m < CPW; ++m) {
     const int c = c0 + kChunksPerWG * m;
-    if (c >= nc) continue;
-    float vp[16], vq[16];
-    load_pair(lp, lq, a.V, c * kChunk, vec_ok, vp, vq, idx_unused);
-    float bp = -INFINITY, bq = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      bp = fmaxf(bp, vp[e]);
-      bq = fmaxf(bq, vq[e]);
+    if (m + 1 < CPW) {
+      const int cn = min(c + kChunksPerWG, nc - 1) * kChunk;
+      load_chunk_raw<false, VEC>(lp, a.V, cn, vp[(m + 1) & 1]);
+      load_chunk_raw<false, VEC>(lq, a.V, cn, vq[(m + 1) & 1]);
     }
-    const double Mp = (double)wave_max_f(bp) * a.inv_tau;
-    const double Mq = (double)wave_max_f(bq) * a.inv_tau_q;
-    double sp = 0.0, sq = 0.0;
+    if (c < nc) {
+      float (&xp)[16] = vp[m & 1];
+      float (&xq)[16] = vq[m & 1];
+      mask_chunk(a.V, c * kChunk, xp, idx_unused);
+      mask_chunk(a.V, c * kChunk, xq, idx_unused);
+      float bp = -INFINITY, bq = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sp += exp_nonpos(shifted(vp[e], a.inv_tau, Mp), tab);
-      sq += exp_nonpos(shifted(vq[e], a.inv_tau_q, Mq), tab);
+      for (int e = 0; e < 16; ++e) {
+        bp = fmaxf(bp, xp[e]);
+        bq = fmaxf(bq, xq[e]);
+      }
+      const double Mp = (double)wave_max_f(bp) * a.inv_tau;
+      const double Mq = (double)wave_max_f(bq) * a.inv_tau_q;
+      double sp = 0.0, sq = 0.0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sp += exp_nonpos(shifted(xp[e], a.inv_tau, Mp), tab);
+        sq += exp_nonpos(shifted(xq[e], a.inv_tau_q, Mq), tab);
+      }
+      stp[m] = RejStat{Mp, wave_sum(sp)};
+      stq[m] = RejStat{Mq, wave_sum(sq)};
     }
-    sp = wave_sum(sp);
-    sq = wave_sum(sq);
-    if (lane == 0) {
-      publish(&a.pstat[row * nc + c].M, Mp);
-      publish(&a.pstat[row * nc + c].S, sp);
-      publish(&a.qstat[row * nc + c].M, Mq);
-      publish(&a.qstat[row * nc + c].S, sq);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      const int c = c0 + kChunksPerWG * m;
+      if (c < nc) {
+        publish(&a.pstat[row * nc + c].M, stp[m].M);
+        publish(&a.pstat[row * nc + c].S, stp[m].S);
+        publish(&a.qstat[row * nc + c].M, stq[m].M);
+        publish(&a.qstat[row * nc + c].S, stq[m].S);
+      }
     }
   }
   if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
@@ -768,9 +789,15 @@ static ev_status launch_sampled(const float *logits, const float *draft, const i
     cpw /= 2;
   dim3 grid((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw), (unsigned)rows);
 #define EV_LAUNCH_SAMPLED(K, C) hipLaunchKernelGGL((K<C>), grid, dim3(256), 0, stream, a)
-  if (cpw == 4) EV_LAUNCH_SAMPLED(sampled_stats_kernel, 4);
-  else if (cpw == 2) EV_LAUNCH_SAMPLED(sampled_stats_kernel, 2);
-  else EV_LAUNCH_SAMPLED(sampled_stats_kernel, 1);
+#define EV_LAUNCH_STATS(C)                                                                    \
+  do {                                                                                        \
+    if ((V & 3) == 0) hipLaunchKernelGGL((sampled_stats_kernel<C, true>), grid, dim3(256), 0, stream, a); \
+    else hipLaunchKernelGGL((sampled_stats_kernel<C, false>), grid, dim3(256), 0, stream, a); \
+  } while (0)
+  if (cpw == 4) EV_LAUNCH_STATS(4);
+  else if (cpw == 2) EV_LAUNCH_STATS(2);
+  else EV_LAUNCH_STATS(1);
+#undef EV_LAUNCH_STATS
   for (int r = 0; r < max_children; ++r) {
     if (cpw == 4) EV_LAUNCH_SAMPLED(sampled_round_kernel, 4);
     else if (cpw == 2) EV_LAUNCH_SAMPLED(sampled_round_kernel, 2);
