@@ -222,13 +222,26 @@ def test_rejection_bit_exact(name, cfg, mode):
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("cfg", [C3, C4], ids=["C3_full", "C4_full"])
+FULL_ACC = [C3, C4, scaled(C3, V=128255)]
+FULL_ACC_IDS = ["C3_full", "C4_full", "C3_full_V128255_unaligned_rows"]
+
+
+@pytest.mark.parametrize("cfg", FULL_ACC, ids=FULL_ACC_IDS)
 def test_rejection_full_size(cfg):
     inp = generate(cfg, with_kv=False)
     r = run_rejection(inp, to_device(inp))
     o = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
     assert min(min(m) for m in o[3]) > 1e-12
     for a, b in zip(r, o[:3]):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", FULL_ACC, ids=FULL_ACC_IDS)
+def test_greedy_full_size(cfg):
+    inp = generate(cfg, tokens="raw", with_kv=False)
+    g = run_greedy(inp, to_device(inp))
+    o = oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
+    for a, b in zip(g, o):
         assert np.array_equal(a, b)
 
 
