@@ -614,7 +614,7 @@ def main():
         write_traffic(*args.traffic_from, args.traffic_command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the per-GPU share of a sharded verification is the single-GPU workload).",
               file=sys.stderr)
         sys.exit(2)

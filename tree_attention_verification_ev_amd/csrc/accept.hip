@@ -436,7 +436,7 @@ struct SampledArgs {
   const double *uniforms;
   RejStat *pstat;                        // [B*T][n_chunks]
   RejStat *qstat;                        // [B*T][n_chunks]
-  double *wpart;                         // [B*T][n_chunks] residual mass per chunk, this round
+  double *wpart;                         // [B*T][n_chunks] residual mass per chunk, current pass
   SampledRow *state;                     // [B*T]
   int32_t *row_cnt;
   int32_t *seq_cnt;
