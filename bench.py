@@ -80,6 +80,7 @@ class BufferSet:
         self.status = z(1)
         self.ws_attn, self.ws_acc = ws_attn, ws_acc
         self.scale = float(np.float32(1.0 / math.sqrt(cfg.d)))
+        self.max_prefix = int(inp.prefix_len.max())
         self.mode = "rejection" if "rejection" in cfg.accept else "greedy"
 
     def mask(self):
@@ -87,7 +88,7 @@ class BufferSet:
 
     def attention(self):
         ev.ev_tree_attention(self.d.q, self.kv, self.d.prefix_len, self.anc, self.scale, self.out,
-                             self.lse, self.ws_attn, self.status)
+                             self.lse, self.ws_attn, self.status, max_prefix_len=self.max_prefix)
 
     def accept(self):
         if self.mode == "rejection":
@@ -550,14 +551,15 @@ def bench_int4(args, cfg):
     out = torch.empty_like(q)
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws = torch.empty(max(1, ev.ev_tree_attention_workspace(caches[0], B, T, Hq)), dtype=torch.uint8,
-                     device="cuda")
-    wsb = torch.empty(max(1, ev.ev_tree_attention_workspace(bf[0], B, T, Hq)), dtype=torch.uint8,
-                      device="cuda")
-    f4 = [lambda kv=kv: ev.ev_tree_attention(q, kv, dev.prefix_len, anc, scale, out, lse, ws, st)
-          for kv in caches]
-    fb = [lambda kv=kv: ev.ev_tree_attention(q, kv, dev.prefix_len, anc, scale, out, lse, wsb, st)
-          for kv in bf]
+    mpl = int(inp.prefix_len.max())
+    ws = torch.zeros(max(1, ev.ev_tree_attention_workspace(caches[0], B, T, Hq, mpl)),
+                     dtype=torch.uint8, device="cuda")
+    wsb = torch.zeros(max(1, ev.ev_tree_attention_workspace(bf[0], B, T, Hq, mpl)),
+                      dtype=torch.uint8, device="cuda")
+    f4 = [lambda kv=kv: ev.ev_tree_attention(q, kv, dev.prefix_len, anc, scale, out, lse, ws, st,
+                                             max_prefix_len=mpl) for kv in caches]
+    fb = [lambda kv=kv: ev.ev_tree_attention(q, kv, dev.prefix_len, anc, scale, out, lse, wsb, st,
+                                             max_prefix_len=mpl) for kv in bf]
     f4[0]()
     torch.cuda.synchronize()
     if int(st.item()) != 0:
@@ -636,7 +638,8 @@ def main():
     per_set = sum(t.numel() * t.element_size() for t in (dev0.q, dev0.k, dev0.v, dev0.logits))
     n_sets = max(1, math.ceil(FOOTPRINT_BYTES / per_set))
     kv_tmp = ev.KvCache(dev0.k, dev0.v, dev0.block_table)
-    ws_attn = torch.empty(max(1, ev.ev_tree_attention_workspace(kv_tmp, cfg.B, cfg.T, cfg.Hq)),
+    ws_attn = torch.zeros(max(1, ev.ev_tree_attention_workspace(kv_tmp, cfg.B, cfg.T, cfg.Hq,
+                                                                int(inp.prefix_len.max()))),
                           dtype=torch.uint8, device="cuda")
     ws_acc = torch.zeros(max(1, ev.ev_accept_workspace(cfg.B, cfg.T, cfg.V)), dtype=torch.uint8,
                          device="cuda")

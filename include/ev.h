@@ -106,8 +106,16 @@ ev_status ev_tree_mask_build(const int32_t *parent, int32_t B, int32_t T,
                              uint64_t *anc_mask, int32_t *depth,
                              int32_t *dev_status, hipStream_t stream);
 
-/* Bytes of workspace ev_tree_attention needs for these shapes (0 when none). */
-size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, int32_t Hq);
+/* Bytes of workspace ev_tree_attention needs for these shapes (0 when none, and 0 for
+ * invalid arguments).  max_prefix_len (host) is the largest prefix_len[b] the call will
+ * see; the key range [0, max_prefix_len + T) is what the work is split over, so pass the
+ * batch's real longest prefix, not the cache capacity.  The same value must be passed to
+ * ev_tree_attention.  The workspace holds arrival counters: zero-fill it (for example
+ * with hipMemset) before its first use; every call leaves the counters at zero again, so
+ * one zeroed workspace of the largest size serves calls of every smaller shape.  Calls
+ * that overlap in time must not share a workspace. */
+size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, int32_t Hq,
+                                   int64_t max_prefix_len);
 
 /* ev_tree_attention — tree-masked attention of the T node queries of each sequence
  * ([TR] sec. 2: every node attends to the whole committed prefix and, among the tree
@@ -115,15 +123,20 @@ size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, i
  *   q    [B][T][Hq][head_dim], dtype kv->dtype;  query head h reads KV head h / (Hq / Hkv)
  *   kv   layer 0 of the cache (slots L_b .. L_b+T-1 already hold the tree's own K/V)
  *   prefix_len [B] int32, anc_mask [B][T] from ev_tree_mask_build
+ *   max_prefix_len (host) an upper bound of every prefix_len[b], as given to
+ *        ev_tree_attention_workspace (>= 0, else EV_ERR_SHAPE)
  *   sm_scale   score scale (pass 1/sqrt(head_dim) for the usual attention)
  *   out  [B][T][Hq][head_dim], dtype kv->dtype;  lse [B][T][Hq] float, natural log of the
  *        softmax normaliser of the scaled scores.
+ *   ws, ws_bytes: workspace of at least ev_tree_attention_workspace() bytes, zero-filled
+ *        before its first use (see there).
  *   bf16 is computed with bf16 matrix-core products and float32 softmax/accumulation;
- *   f32 in float32 throughout.  EV_DERR_BOUNDS when L_b + T exceeds the cache. */
+ *   f32 in float32 throughout.  EV_DERR_BOUNDS when L_b + T exceeds the cache or L_b
+ *   exceeds max_prefix_len. */
 ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
                             const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
-                            float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes,
-                            int32_t *dev_status, hipStream_t stream);
+                            int64_t max_prefix_len, float sm_scale, void *out, float *lse,
+                            void *ws, size_t ws_bytes, int32_t *dev_status, hipStream_t stream);
 
 /* Bytes of workspace the acceptance calls need (B * T <= 65535, V <= 262144).
  * The acceptance workspace holds arrival counters: zero-fill it (for example with

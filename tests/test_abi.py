@@ -69,10 +69,18 @@ def _kv(**kw):
 
 def test_workspace_queries(lib):
     d = _kv()
-    ws = lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 64, 64)
+    ws = lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 64, 64, 4096)
     assert ws % 256 == 0
-    assert lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 65, 64) == 0
-    assert lib.ev_tree_attention_workspace(ctypes.byref(_kv(head_dim=96)), 1, 64, 64) == 0
+    assert lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 65, 64, 4096) == 0
+    assert lib.ev_tree_attention_workspace(ctypes.byref(_kv(head_dim=96)), 1, 64, 64, 4096) == 0
+    assert lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 64, 64, -1) == 0
+    # the split plan follows the longest prefix, not the capacity: a cache eight times as
+    # large as the prefix needs the same workspace
+    big = _kv(cap=8 * 4176)
+    assert lib.ev_tree_attention_workspace(ctypes.byref(big), 1, 64, 64, 4096) == ws
+    # a bound beyond the cache is clamped to what the cache holds (4176 slots)
+    assert (lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 64, 64, 10**12)
+            == lib.ev_tree_attention_workspace(ctypes.byref(d), 1, 64, 64, 4176 - 64))
     counters = 2 * 65536 * 4                       # fixed row and sequence counter areas
     stats = 64 * 126 * 16                          # (max, sum) per 1024-logit chunk per row
     assert lib.ev_accept_workspace(1, 64, 128256) == counters + stats + 64 * 8
@@ -87,9 +95,11 @@ def test_host_errors_return_before_launch(lib):
     assert lib.ev_tree_mask_build(P, 1, 65, P, P, None, None) == 2
     assert lib.ev_tree_mask_build(None, 1, 8, P, P, None, None) == 1
     assert lib.ev_tree_mask_build(None, 0, 8, None, None, None, None) == 0   # empty batch
-    att = lambda desc, T=64, Hq=64, scale=0.088, ws=None, nbytes=0, q=P: lib.ev_tree_attention(
-        q, ctypes.byref(desc), P, P, 1, T, Hq, scale, P, P, ws, nbytes, None, None)
+    att = lambda desc, T=64, Hq=64, scale=0.088, ws=None, nbytes=0, q=P, mpl=4096: \
+        lib.ev_tree_attention(q, ctypes.byref(desc), P, P, 1, T, Hq, mpl, scale, P, P, ws, nbytes,
+                              None, None)
     assert att(d, Hq=60) == 2                       # Hq not a multiple of Hkv
+    assert att(d, mpl=-5) == 2                      # negative prefix bound
     assert att(_kv(head_dim=96)) == 2
     assert att(_kv(dtype=7)) == 3
     assert att(d, scale=0.0) == 5

@@ -60,6 +60,7 @@ CASES = [
     ("B2_V12_tiny", 2, 12, 4, 8, 8, 64),
     ("B1_V128256", 1, 128256, 6, 8, 8, 64),
     ("B4_V128256", 4, 128256, 6, 8, 8, 64),
+    ("B16_V128256", 16, 128256, 6, 8, 8, 64),        # the batched layer's batch and vocabulary
     ("B2_V3000_depth10", 2, 3000, 10, 8, 8, 64),     # 640 candidates: 1024-key sort
     ("B3_V3000_depth16", 3, 3000, 16, 8, 8, 64),     # deepest tree the workspace holds
 ]

@@ -18,7 +18,7 @@ C1, C2, C3, C4, C5 = CONFIGS
 c = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def int4_attention(inp):
+def int4_attention(inp, seqs=None, heads=None, one_split=None):
     cfg = inp.cfg
     kq, ks = quantize_int4(inp.k)
     vq, vs = quantize_int4(inp.v)
@@ -26,12 +26,15 @@ def int4_attention(inp):
     kv = ev.KvCache(c(kq), c(vq), bt, k_scale=c(ks), v_scale=c(vs))
     scale = float(np.float32(1.0 / math.sqrt(cfg.d)))
     anc, _ = ev.ev_tree_mask_build(c(inp.parent), check=True)
+    mpl = int(inp.prefix_len.max())
+    if one_split is not None:     # the plan's split count shows in its workspace size
+        assert (ev.ev_tree_attention_workspace(kv, cfg.B, cfg.T, cfg.Hq, mpl) == 0) == one_split
     out, lse = ev.ev_tree_attention(c(inp.q).to(torch.bfloat16), kv, c(inp.prefix_len), anc, scale,
-                                    check=True)
+                                    check=True, max_prefix_len=mpl)
     ao, _ = oracle.tree_mask_batch(inp.parent)
     Oo, Lo = oracle.tree_attention_batch(inp.q, oracle.dequant_int4(kq, ks), oracle.dequant_int4(vq, vs),
                                          inp.prefix_len, ao, inp.layout, inp.block_table,
-                                         cfg.block_size, scale)
+                                         cfg.block_size, scale, seqs=seqs, heads=heads)
     O, L = out.float().cpu().numpy(), lse.cpu().numpy()
     sel = np.isfinite(Lo)
     ratio, err = o_error(O, Oo, sel, "bf16")
@@ -55,6 +58,17 @@ CASES = [
 @pytest.mark.parametrize("name,cfg", CASES, ids=[n for n, _ in CASES])
 def test_int4_attention(name, cfg):
     int4_attention(generate(cfg, with_logits=False))
+
+
+def test_int4_attention_full_batched_paged_one_split():
+    """Full batched paged layer (B = 16): 256 work units, so one split and the unsplit
+    output path (bf16 O and LSE written directly); three sequences compared, all heads."""
+    int4_attention(generate(C4, with_logits=False), seqs=[0, 7, 15], one_split=True)
+
+
+def test_int4_attention_full_long_context_sampled_heads():
+    inp = generate(C5, with_logits=False)
+    int4_attention(inp, heads=[0, 9, 18, 27, 36, 45, 54, 63], one_split=False)
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "paged"])

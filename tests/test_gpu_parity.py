@@ -42,10 +42,16 @@ def scale_of(cfg):
     return float(np.float32(1.0 / math.sqrt(cfg.d)))
 
 
+def max_prefix(inp):
+    """The batch's longest prefix: the bound the split plan is sized from."""
+    return int(inp.prefix_len.max())
+
+
 def gpu_attention(inp, dev):
     kv = ev.KvCache(dev.k, dev.v, dev.block_table)
     anc, depth = ev.ev_tree_mask_build(dev.parent, check=True)
-    out, lse = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), check=True)
+    out, lse = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), check=True,
+                                    max_prefix_len=max_prefix(inp))
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), anc, depth
 
@@ -106,6 +112,8 @@ ATTN_SMALL = [
     ("star64_gqa", scaled(C3, tree="star", L=77, V=64)),
     ("root_only", scaled(C3, T=1, tree="grow", L=200, V=64)),
     ("bf16_d64", scaled(C3, d=64, L=333, V=64)),
+    # 16 x 8 x 2 = 256 work units: one split, the register-staged kernel's unsplit output
+    ("bf16_d64_one_split", scaled(C4, d=64, L=(100, 900), V=64)),
     ("f32_d128", scaled(C1, d=128, L=190, Hq=8, Hkv=2, V=64)),
     ("gqa4_T26", scaled(C2, Hq=32, Hkv=8, L=515, V=64)),
     # 64 rows per KV head: the two-wavefront DMA workgroup
@@ -136,6 +144,50 @@ def test_attention_full_long_context_sampled_heads():
     check_attention(inp, heads=[0, 9, 18, 27, 36, 45, 54, 63])
 
 
+def check_attention_dev(inp, kv, dev, seqs=None, heads=None):
+    """Attention on an already-built device cache (same logical contents as inp) against
+    the oracle on inp."""
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    out, lse = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), check=True,
+                                    max_prefix_len=max_prefix(inp))
+    O, LSE = out.float().cpu().numpy(), lse.cpu().numpy()
+    Oo, Lo = oracle_attention(inp, seqs, heads)
+    sel = np.isfinite(Lo)
+    assert sel.any() and np.isfinite(O).all() and np.isfinite(LSE).all()
+    o_ratio, o_err = o_error(O, Oo, sel, "bf16")
+    l_err = np.abs(LSE - Lo)[sel].max()
+    assert o_err <= O_TOL_BF16 and l_err <= LSE_TOL_BF16, (o_err, l_err)
+
+
+def test_attention_serving_capacity_contiguous():
+    """The Llama-3-70B-shaped layer over a cache sized for 32k tokens per sequence: the
+    split plan follows the prefix (max_prefix_len), not the capacity, and the result is
+    the tight cache's."""
+    inp = generate(C3, with_logits=False)
+    dev = to_device(inp)
+    cap = 32848
+    k = torch.full((1, C3.Hkv, cap, C3.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v = torch.full_like(k, float("nan"))
+    k[:, :, :inp.cap] = dev.k
+    v[:, :, :inp.cap] = dev.v
+    kv_big, kv_tight = ev.KvCache(k, v), ev.KvCache(dev.k, dev.v)
+    mpl = max_prefix(inp)
+    assert (ev.ev_tree_attention_workspace(kv_big, 1, C3.T, C3.Hq, mpl)
+            == ev.ev_tree_attention_workspace(kv_tight, 1, C3.T, C3.Hq, mpl))
+    check_attention_dev(inp, kv_big, dev)
+
+
+def test_attention_serving_capacity_paged():
+    """The batched paged layer with a block table 2048 blocks wide (32k slots per sequence)
+    and a pool with spare blocks: same result as the tight table, every head compared."""
+    inp = generate(C4, with_logits=False)
+    dev = to_device(inp)
+    B, wide = C4.B, 2048
+    table = torch.full((B, wide), -1, dtype=torch.int32, device="cuda")
+    table[:, :inp.block_table.shape[1]] = dev.block_table
+    check_attention_dev(inp, ev.KvCache(dev.k, dev.v, table), dev, seqs=[0, 5, 11])
+
+
 def test_paged_equals_contiguous_on_the_same_data():
     cfg = scaled(C4, B=3, L=(100, 900), V=64)
     a = generate(cfg, layout="contiguous", with_logits=False)
@@ -151,10 +203,15 @@ def test_attention_is_deterministic():
     dev = to_device(inp)
     kv = ev.KvCache(dev.k, dev.v, dev.block_table)
     anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
-    O1, L1 = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), check=True)
+    mpl = max_prefix(inp)
+    O1, L1 = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), check=True,
+                                  max_prefix_len=mpl)
     O2, L2 = torch.empty_like(O1), torch.empty_like(L1)
+    ws = torch.zeros(max(1, ev.ev_tree_attention_workspace(kv, 1, inp.cfg.T, inp.cfg.Hq, mpl)),
+                     dtype=torch.uint8, device="cuda")
     for _ in range(100):
-        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), O2, L2)
+        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(inp.cfg), O2, L2, ws,
+                             max_prefix_len=mpl)
         assert torch.equal(O1, O2) and torch.equal(L1, L2)
 
 
@@ -166,6 +223,21 @@ def test_attention_reports_prefix_beyond_cache():
     anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
     with pytest.raises(ev.EvError) as e:
         ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, check=True)
+    assert e.value.code == 102
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_attention_reports_prefix_beyond_bound(paged):
+    """A prefix longer than the max_prefix_len the call was planned for is a device error
+    (the splits do not cover it), even where the cache could hold it."""
+    cfg = scaled(C4, B=3, L=(200, 900), V=64) if paged else scaled(C3, B=2, L=(300, 900), V=64)
+    inp = generate(cfg, with_logits=False)
+    dev = to_device(inp)
+    kv = ev.KvCache(dev.k, dev.v, dev.block_table)
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    with pytest.raises(ev.EvError) as e:
+        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, check=True,
+                             max_prefix_len=max_prefix(inp) - 1)
     assert e.value.code == 102
 
 
@@ -313,6 +385,23 @@ def test_accept_workspace_reuse_across_shapes():
         assert int(ws[:counters].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("V", [3001, 128256])
+def test_greedy_rows_of_negative_infinity(V):
+    """Rows whose logits are all -inf have argmax 0 (the lowest index of the maximum), on
+    the GPU as in the oracle: never an id outside [0, V)."""
+    cfg = scaled(C3, B=3, V=V, L=8)
+    inp = generate(cfg, tokens="raw", with_kv=False)
+    inp.logits[0, 0, :] = -np.inf                       # root row: bonus or first step
+    inp.logits[1, :, :] = -np.inf                       # every row of a sequence
+    kids = np.nonzero(inp.parent[1] == 0)[0]
+    inp.tokens[1, kids[0]] = 0                          # a child drafting 0 is accepted
+    g = run_greedy(inp, to_device(inp))
+    o = oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
+    for a, b in zip(g, o):
+        assert np.array_equal(a, b)
+    assert g[2].max() < V and g[2][0, 0] >= 0 and o[0][1] >= 1
+
+
 def test_accept_reports_bad_token():
     inp = generate(scaled(C3, V=500, L=8), with_kv=False)
     dev = to_device(inp)
@@ -450,13 +539,15 @@ def test_graph_replays_match_eager():
     path = torch.zeros((B, T), dtype=torch.int32, device="cuda")
     tok = torch.zeros((B, T), dtype=torch.int32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws_a = torch.empty(max(1, ev.ev_tree_attention_workspace(kv, B, T, cfg.Hq)), dtype=torch.uint8,
-                       device="cuda")
+    mpl = max_prefix(inp)
+    ws_a = torch.zeros(max(1, ev.ev_tree_attention_workspace(kv, B, T, cfg.Hq, mpl)),
+                       dtype=torch.uint8, device="cuda")
     ws_r = torch.zeros(ev.ev_accept_workspace(B, T, cfg.V), dtype=torch.uint8, device="cuda")
 
     def step():
         ev.ev_tree_mask_build(dev.parent, anc, depth, status)
-        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(cfg), out, lse, ws_a, status)
+        ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(cfg), out, lse, ws_a, status,
+                             max_prefix_len=mpl)
         ev.ev_accept_rejection(dev.logits, dev.tokens, dev.parent, dev.tau, dev.uniforms, acc, path,
                                tok, ws_r, status)
 

@@ -58,7 +58,7 @@ def test_sampled_bit_exact(name, cfg):
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("cfg", [C3, scaled(C4, B=4)], ids=["C3_full", "C4_B4_fullV"])
+@pytest.mark.parametrize("cfg", [C3, scaled(C4, B=4), C4], ids=["C3_full", "C4_B4_fullV", "C4_full"])
 def test_sampled_full_vocabulary(cfg):
     inp = generate(cfg, with_kv=False)
     draft, tokens = sampled_drafts(inp, DRAFT_TAU)

@@ -72,9 +72,9 @@ def lib() -> ctypes.CDLL:
         kv = ctypes.POINTER(EvKvDesc)
         sigs = {
             "ev_tree_mask_build": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
-            "ev_tree_attention_workspace": (_SZ, [kv, _I32, _I32, _I32]),
-            "ev_tree_attention": (_I32, [_P, kv, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ,
-                                         _P, _P]),
+            "ev_tree_attention_workspace": (_SZ, [kv, _I32, _I32, _I32, _I64]),
+            "ev_tree_attention": (_I32, [_P, kv, _P, _P, _I32, _I32, _I32, _I64, _F32, _P, _P, _P,
+                                         _SZ, _P, _P]),
             "ev_accept_workspace": (_SZ, [_I32, _I32, _I32]),
             "ev_accept_greedy": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_rejection": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _P,
@@ -199,6 +199,8 @@ class KvCache:
             desc.block_table = None
             desc.block_size = desc.max_blocks_per_seq = desc.n_blocks = 0
         self.desc = desc
+        # logical slots one sequence can hold
+        self.capacity = (desc.max_blocks_per_seq * desc.block_size) if self.paged else desc.cap
         self.dtype = k.dtype
         self.n_kv_heads = hkv
         self.head_dim = d
@@ -223,15 +225,24 @@ def ev_tree_mask_build(parent: torch.Tensor, anc_mask: Optional[torch.Tensor] = 
     return anc_mask, depth
 
 
-def ev_tree_attention_workspace(kv: KvCache, B: int, T: int, Hq: int) -> int:
-    return int(lib().ev_tree_attention_workspace(kv.ref(), B, T, Hq))
+def ev_tree_attention_workspace(kv: KvCache, B: int, T: int, Hq: int,
+                                max_prefix_len: Optional[int] = None) -> int:
+    """Workspace bytes of ev_tree_attention; max_prefix_len defaults to what the cache holds."""
+    mpl = kv.capacity - T if max_prefix_len is None else max_prefix_len
+    return int(lib().ev_tree_attention_workspace(kv.ref(), B, T, Hq, max(0, int(mpl))))
 
 
 def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, anc_mask: torch.Tensor,
                       sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                       lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                      dev_status: Optional[torch.Tensor] = None, check: bool = False):
-    """Tree-masked attention; returns (out [B][T][Hq][d], lse [B][T][Hq] float32)."""
+                      dev_status: Optional[torch.Tensor] = None, check: bool = False,
+                      max_prefix_len: Optional[int] = None):
+    """Tree-masked attention; returns (out [B][T][Hq][d], lse [B][T][Hq] float32).
+
+    max_prefix_len: an upper bound of prefix_len (host int); the work is split over its
+    key range, so pass the batch's longest prefix.  When omitted, the cache's capacity
+    less T is used: always valid, but the split then spans the whole cache.  ws must be
+    zero-filled before its first use (it is allocated zeroed here when not passed)."""
     _dev(q, "q", torch.bfloat16 if kv.dtype == torch.uint8 else kv.dtype)
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(anc_mask, "anc_mask", torch.int64)
@@ -239,15 +250,16 @@ def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, an
     dev = q.device
     if sm_scale is None:
         sm_scale = d ** -0.5
+    mpl = max(0, kv.capacity - T) if max_prefix_len is None else int(max_prefix_len)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
-    need = ev_tree_attention_workspace(kv, B, T, Hq)
+    need = ev_tree_attention_workspace(kv, B, T, Hq, mpl)
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     status = _status_word(dev, dev_status)
     code = lib().ev_tree_attention(_ptr(q), kv.ref(), _ptr(prefix_len), _ptr(anc_mask), B, T, Hq,
-                                   float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                   mpl, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                    _ptr(status), _stream(dev))
     _finish(code, "ev_tree_attention", status, check)
     return out, lse

@@ -253,9 +253,12 @@ __device__ __forceinline__ ChunkStat<REJ> chunk_stats(const AcceptArgs &a, int c
                                                       const float (&v)[16], const double *tab) {
   const int lane = threadIdx.x & 63;
   if constexpr (!REJ) {
-    // a lane visits its ids in increasing order, so a strict > keeps the lowest index
+    // a lane visits its ids in increasing order, so a strict > keeps the lowest index; it
+    // starts from its first id when that lies in the row, so a row of -inf logits still
+    // yields its lowest id (0), as the argmax definition does
     float best = -INFINITY;
-    int bi = INT_MAX;
+    const int first = chunk * kChunk + lane * 4;
+    int bi = first < a.V ? first : INT_MAX;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const bool gt = v[e] > best;

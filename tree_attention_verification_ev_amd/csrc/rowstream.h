@@ -239,6 +239,16 @@ __device__ inline float wave_max_f(float x) {
   return lane_f(x, 63);
 }
 
+__device__ inline float wave_sum_f(float x) {
+  x += dpp_f<kDppQuadSwap1>(x);
+  x += dpp_f<kDppQuadSwap2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  x += dpp_f<kDppMirror>(x);
+  x += bcast_f<kDppRowBcast15, kRows13>(0.f, x);
+  x += bcast_f<kDppRowBcast31, kRows23>(0.f, x);
+  return lane_f(x, 63);
+}
+
 __device__ inline double wave_max(double x) {
   x = fmax(x, dpp_d<kDppQuadSwap1>(x));
   x = fmax(x, dpp_d<kDppQuadSwap2>(x));

@@ -35,8 +35,10 @@
 //     kernel); each split writes its normalised partial O in fp16 (pre-divided by
 //     max(1, |O|max) of the row, the divisor kept in float32) and its LSE, adjacent to the
 //     other splits of the same row; a merge kernel combines them.
-// float32 path: a plain VALU kernel (one wavefront per (sequence, head, node)).
+// float32 path: a VALU kernel, one workgroup per (sequence, KV head, block of query rows),
+// K and V tiles staged in LDS.
 #include "ev_internal.h"
+#include "rowstream.h"
 
 #include <algorithm>
 #include <math.h>
@@ -58,6 +60,7 @@ struct AttnArgs {
   const int32_t *prefix_len;
   const uint64_t *anc;
   int B, T, Hq, G;
+  int max_prefix;          // host bound of every prefix_len[b]; splits cover its key range
   float scale_log2;        // sm_scale * log2(e)
   int row_blocks;
   int tiles_per_split;
@@ -443,7 +446,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
 
   const int L = a.prefix_len[b];
   const int nkeys = L + a.T;
-  if (L < 0 || !a.kv.fits(nkeys)) {
+  if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
     if (threadIdx.x == 0) report(a.dev_status, EV_DERR_BOUNDS);
     return;
   }
@@ -686,7 +689,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
 
   const int L = a.prefix_len[b];
   const int nkeys = L + a.T;
-  if (L < 0 || !a.kv.fits(nkeys)) {
+  if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
     if (threadIdx.x == 0) report(a.dev_status, EV_DERR_BOUNDS);
     return;
   }
@@ -905,12 +908,6 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
 // D/E lanes per row (sequence, node, head), E head-dim elements per lane; the partials are
 // read in batches of BATCH splits (all loads of a batch in flight together) and combined
 // with a running maximum.
-#ifndef EV_MERGE_E
-#define EV_MERGE_E 4
-#endif
-#ifndef EV_MERGE_BATCH
-#define EV_MERGE_BATCH 8
-#endif
 template <int D, int E, int BATCH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int LPR = D / E;             // lanes per row
@@ -965,72 +962,170 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (c == 0) a.lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
-// float32 path: one wavefront per (sequence, q-head, node); lane j scores key j of each
-// 64-key tile, the tile's probabilities go through LDS, lane d accumulates O[d].
-template <int D>
-__global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
-  __shared__ float sq[D];
-  __shared__ float sp[64];
-  const int lane = threadIdx.x;
-  const int node = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / a.G;
+// float32 path: one 256-thread workgroup per (sequence, KV head, block of R query rows).
+// 64-key K and V tiles reach LDS through coalesced 16-byte loads, the next tile's loads in
+// flight in registers while the current one is computed.  Scores: lane k of wavefront w
+// scores key k against rows w, w + 4, ... (query rows are broadcast reads), so a row's 64
+// scores lie across one wavefront and its max and sum are wavefront (DPP) reductions.  P V:
+// thread t owns head dimension t % D of rows t / D, t / D + 256 / D, ...
+template <int D, int R>
+__global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
+  constexpr int NT = 256;
+  constexpr int C4 = D / 4;                 // 16-byte pieces per row
+  constexpr int LPT = kKT * C4 / NT;        // pieces per thread per K or V tile
+  constexpr int KP = D + 1;                 // K tile pitch: lane k reads row k, distinct banks
+  constexpr int RW = R / 4;                 // score rows per wavefront
+  constexpr int RSTEP = NT / D;             // row stride of a thread's P V rows
+  constexpr int RPT = R / RSTEP;            // P V rows per thread
+  static_assert(R % 4 == 0 && R % RSTEP == 0, "row block must tile the workgroup");
+  __shared__ __attribute__((aligned(16))) float sQ[R * D];
+  __shared__ float sK[kKT * KP];
+  __shared__ float sV[kKT * D];
+  __shared__ __attribute__((aligned(16))) float sP[R * kKT];
+  __shared__ float sA[R], sM[R], sL[R];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = blockIdx.x % a.row_blocks;
+  const int bg = blockIdx.x / a.row_blocks;
+  const int b = bg / a.kv.hkv, g = bg % a.kv.hkv;
   const int L = a.prefix_len[b];
   const int nkeys = L + a.T;
-  if (L < 0 || !a.kv.fits(nkeys)) {
-    if (lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
+  if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
+    if (tid == 0) report(a.dev_status, EV_DERR_BOUNDS);
     return;
   }
+  const int rows = a.T * a.G;
+  const int row0 = rb * R;
+  const int nrow = min(R, rows - row0);
   const float *Q = (const float *)a.q;
   const float *K = (const float *)a.k;
   const float *V = (const float *)a.v;
-  const int64_t orow = ((int64_t)b * a.T + node) * a.Hq + h;
-  for (int d = lane; d < D; d += 64) sq[d] = Q[orow * D + d];
-  const uint64_t anc = a.anc[(int64_t)b * a.T + node];
-  __syncthreads();
-  float m = -INFINITY, l = 0.f;
-  float o[D / 64] = {};
-  for (int key0 = 0; key0 < nkeys; key0 += 64) {
-    int slot = key0 + lane;
-    float sc = -INFINITY;
-    if (slot < nkeys && visible(slot, L, anc)) {
-      int64_t off = a.kv.slot_offset(b, g, slot);
-      if (off >= 0) {
-        float acc = 0.f;
-        for (int d = 0; d < D; ++d) acc = fmaf(sq[d], K[off + d], acc);
-        sc = acc * a.scale_log2;
-      } else {
-        report(a.dev_status, EV_DERR_BOUNDS);
+  auto orow_of = [&](int r) {               // output row of block row r (r < nrow)
+    const int rr = row0 + r;
+    return ((int64_t)b * a.T + rr / a.G) * a.Hq + g * a.G + rr % a.G;
+  };
+
+  // query rows of the block (zero past the last row)
+  for (int i = tid; i < R * C4; i += NT) {
+    const int r = i / C4, c = i % C4;
+    f32x4 x = {};
+    if (r < nrow) x = *(const f32x4 *)(Q + orow_of(r) * D + 4 * c);
+    *(f32x4 *)(sQ + r * D + 4 * c) = x;
+  }
+  uint64_t anc[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = wave + 4 * i;
+    anc[i] = r < nrow ? a.anc[(int64_t)b * a.T + (row0 + r) / a.G] : 0ull;
+  }
+
+  f32x4 kr[LPT], vr[LPT];
+  bool bad = false;
+  auto load = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int piece = tid + i * NT, key = piece / C4, c = piece % C4;
+      const int slot = key0 + key;
+      f32x4 xk = {}, xv = {};
+      if (slot < nkeys) {
+        const int64_t off = a.kv.slot_offset(b, g, slot);
+        if (off >= 0) {
+          xk = *(const f32x4 *)(K + off + 4 * c);
+          xv = *(const f32x4 *)(V + off + 4 * c);
+        } else {
+          bad = true;
+        }
+      }
+      kr[i] = xk;
+      vr[i] = xv;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int piece = tid + i * NT, key = piece / C4, c = piece % C4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sK[key * KP + 4 * c + e] = kr[i][e];
+      *(f32x4 *)(sV + key * D + 4 * c) = vr[i];
+    }
+  };
+
+  float m[RW], l[RW], o[RPT];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) m[i] = -INFINITY, l[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) o[j] = 0.f;
+  const int dim = tid % D, prow = tid / D;
+
+  const int ntiles = (nkeys + kKT - 1) / kKT;
+  load(0);
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();                        // the previous tile's P V is done with sK/sV/sP
+    store();
+    __syncthreads();
+    if (t + 1 < ntiles) load((t + 1) * kKT);
+    const int slot = t * kKT + lane;
+    float s[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) s[i] = 0.f;
+    for (int d = 0; d < D; d += 4) {
+      const float k0 = sK[lane * KP + d], k1 = sK[lane * KP + d + 1];
+      const float k2 = sK[lane * KP + d + 2], k3 = sK[lane * KP + d + 3];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        if (wave + 4 * i >= nrow) continue;
+        const f32x4 qv = *(const f32x4 *)(sQ + (wave + 4 * i) * D + d);
+        s[i] = fmaf(qv[0], k0, fmaf(qv[1], k1, fmaf(qv[2], k2, fmaf(qv[3], k3, s[i]))));
       }
     }
-    float mx = sc;
-    for (int w = 32; w >= 1; w >>= 1) mx = fmaxf(mx, __shfl_xor(mx, w));
-    float m_new = fmaxf(m, mx);
-    float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float alpha = exp2f(m - m_use);
-    float p = exp2f(sc - m_use);
-    float ps = p;
-    for (int w = 32; w >= 1; w >>= 1) ps += __shfl_xor(ps, w);
-    l = l * alpha + ps;
-    m = m_new;
-    __syncthreads();
-    sp[lane] = p;
-    __syncthreads();
-    int cnt = min(64, nkeys - key0);
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) o[k] *= alpha;
-    for (int j = 0; j < cnt; ++j) {
-      float pj = sp[j];
-      if (pj == 0.f) continue;
-      int64_t off = a.kv.slot_offset(b, g, key0 + j);
+    for (int i = 0; i < RW; ++i) {
+      const int r = wave + 4 * i;
+      if (r >= nrow) continue;             // uniform across the wavefront
+      const bool ok = slot < nkeys && visible(slot, L, anc[i]);
+      const float x = ok ? s[i] * a.scale_log2 : -INFINITY;
+      const float mnew = fmaxf(m[i], wave_max_f(x));
+      const float alpha = mnew == -INFINITY ? 1.f : exp2f(m[i] - mnew);
+      const float p = ok ? exp2f(x - mnew) : 0.f;
+      l[i] = l[i] * alpha + wave_sum_f(p);
+      m[i] = mnew;
+      sP[r * kKT + lane] = p;
+      if (lane == 0) sA[r] = alpha;
+    }
+    __syncthreads();
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k) o[k] = fmaf(pj, V[off + lane + 64 * k], o[k]);
+    for (int j = 0; j < RPT; ++j) {
+      const int r = prow + RSTEP * j;
+      if (r >= nrow) continue;
+      float acc = o[j] * sA[r];
+      for (int k = 0; k < kKT; k += 4) {
+        const f32x4 pv = *(const f32x4 *)(sP + r * kKT + k);
+        acc = fmaf(pv[0], sV[k * D + dim], acc);
+        acc = fmaf(pv[1], sV[(k + 1) * D + dim], acc);
+        acc = fmaf(pv[2], sV[(k + 2) * D + dim], acc);
+        acc = fmaf(pv[3], sV[(k + 3) * D + dim], acc);
+      }
+      o[j] = acc;
     }
   }
-  float inv = l > 0.f ? 1.f / l : 0.f;
-  float lse = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  if (__any(bad) && lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) ((float *)a.out)[orow * D + lane + 64 * k] = o[k] * inv;
-  if (lane == 0) a.lse[orow] = lse;
+  for (int i = 0; i < RW; ++i) {
+    const int r = wave + 4 * i;
+    if (r < nrow && lane == 0) {
+      sM[r] = m[i];
+      sL[r] = l[i];
+      a.lse[orow_of(r)] = l[i] > 0.f ? (m[i] + log2f(l[i])) * kLn2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = prow + RSTEP * j;
+    if (r >= nrow) continue;
+    const float lt = sL[r];
+    ((float *)a.out)[orow_of(r) * D + dim] = lt > 0.f ? o[j] / lt : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1039,49 +1134,59 @@ constexpr int kMaxSplits = 32;
 constexpr int kCUs = 256;
 
 struct Plan {
-  int qt, nw;            // query tiles per wave, waves per workgroup
+  int nw;                // waves per workgroup
   int row_blocks;
   int tiles_per_split, n_splits;
   int n_work, grid;
 };
 
-static int max_slots(const KvAddr &kv) {
-  if (!kv.paged) return (int)std::min<int64_t>(kv.cap, 1 << 30);
-  return kv.max_blocks << kv.block_shift;
+// Query rows per float32 workgroup: 8 for small groups (the fp32 configuration has 8 rows
+// per KV head), else 32.
+static int f32_rows(int rows) { return rows <= 8 ? 8 : 32; }
+
+static int64_t max_slots(const KvAddr &kv) {
+  if (!kv.paged) return kv.cap;
+  return (int64_t)kv.max_blocks << kv.block_shift;
+}
+
+// Key slots the plan covers: the longest prefix the call may see plus the tree, never more
+// than the cache holds (a longer sequence cannot fit and is reported by the kernel).
+static int plan_slots(const KvAddr &kv, int T, int64_t max_prefix_len) {
+  const int64_t want = std::min<int64_t>(max_prefix_len, 1 << 30) + T;
+  return (int)std::min<int64_t>(std::min<int64_t>(want, max_slots(kv)), 1 << 30);
 }
 
 // Splits are sized so that one round of workgroups fills the chip (GQA: one 8-wave
-// workgroup per CU; MHA: four 1-wave workgroups per CU), at most kMaxSplits of them, and
-// a paged split's block ids must fit the LDS cache.
-static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq) {
+// workgroup per CU; MHA: four 1-wave workgroups per CU), at most kMaxSplits of them, over
+// the key range of the longest prefix the call may see; a paged split's block ids must
+// fit the LDS cache.
+static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq, int64_t max_prefix_len) {
   Plan p{};
-  if (dtype == EV_F32) {
-    p.qt = p.nw = p.row_blocks = p.n_splits = 1;
-    p.tiles_per_split = 1 << 30;
-    return p;
-  }
   const int G = Hq / kv.hkv;
   const int rows = T * G;
-#ifndef EV_ATTN_WIDE_WAVES
-#define EV_ATTN_WIDE_WAVES 0
-#endif
-  // Many rows per KV head: 8 waves of 32 rows (two waves per SIMD, no accumulator
-  // spill to AGPRs); EV_ATTN_WIDE_WAVES selects 4 waves of 64 rows instead.
-  p.qt = (EV_ATTN_WIDE_WAVES && rows >= 256) ? 2 : 1;
-  const int wave_rows = 32 * p.qt;
-  const int waves_needed = (rows + wave_rows - 1) / wave_rows;
-  p.nw = waves_needed >= 8 && p.qt == 1 ? 8
-       : waves_needed >= 4 ? 4 : (waves_needed >= 2 ? 2 : 1);
+  if (dtype == EV_F32) {
+    p.nw = 4;
+    p.row_blocks = (rows + f32_rows(rows) - 1) / f32_rows(rows);
+    p.n_splits = 1;
+    p.tiles_per_split = 1 << 30;
+    p.n_work = B * kv.hkv * p.row_blocks;
+    p.grid = p.n_work;
+    return p;
+  }
+  // Waves of 32 query rows, up to 8 per workgroup (two waves per SIMD, no accumulator
+  // spill to AGPRs).
+  const int waves_needed = (rows + 31) / 32;
+  p.nw = waves_needed >= 8 ? 8 : waves_needed >= 4 ? 4 : (waves_needed >= 2 ? 2 : 1);
   // An INT4 tile is dequantised by every thread of the workgroup while staging: at least
   // four wavefronts share that work even when fewer own query rows.
   if (dtype == EV_INT4) p.nw = std::max(p.nw, 4);
   // bf16 with d = 128 always takes the direct-to-LDS kernel, whose smallest workgroup has
   // two wavefronts (with at most 32 rows per KV head the second owns none and only shares
   // the DMA issue); its 128 KB of LDS leave room for one workgroup per CU.
-  const bool dma = dtype == EV_BF16 && kv.d == 128 && p.qt == 1;
+  const bool dma = dtype == EV_BF16 && kv.d == 128;
   if (dma) p.nw = std::max(p.nw, 2);
   p.row_blocks = (waves_needed + p.nw - 1) / p.nw;
-  const int max_tiles = (max_slots(kv) + kKT - 1) / kKT;
+  const int max_tiles = (plan_slots(kv, T, max_prefix_len) + kKT - 1) / kKT;
   const int units = B * kv.hkv * p.row_blocks;
   const int slots = dma || p.nw >= 4 ? kCUs : (p.nw == 2 ? 2 * kCUs : 4 * kCUs);
   int splits = std::max(1, slots / units);
@@ -1112,23 +1217,24 @@ static size_t workspace_bytes(const Plan &p, int B, int T, int Hq, int D) {
 template <int D, bool PAGED, bool Q4>
 static void launch_main(const Plan &p, const AttnArgs &a, hipStream_t stream) {
   dim3 grid(p.grid);
-  if (!Q4 && D == 128 && p.qt == 1 && p.nw >= 2) {
+  if constexpr (!Q4 && D == 128) {
+    // bf16 with d = 128: the direct-to-LDS kernel (the plan gives it at least 2 waves)
     if (p.nw == 8)
       hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED>), grid, dim3(512), 0, stream, a);
     else if (p.nw == 4)
       hipLaunchKernelGGL((tree_attn_dma_kernel<4, PAGED>), grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED>), grid, dim3(128), 0, stream, a);
-  } else if (p.qt == 2) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 2, 4, PAGED, Q4>), grid, dim3(256), 0, stream, a);
   } else if (p.nw == 8) {
     hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 8, PAGED, Q4>), grid, dim3(512), 0, stream, a);
   } else if (p.nw == 4) {
     hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 4, PAGED, Q4>), grid, dim3(256), 0, stream, a);
-  } else if (p.nw == 2) {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 2, PAGED, Q4>), grid, dim3(128), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 1, PAGED, Q4>), grid, dim3(64), 0, stream, a);
+  } else if constexpr (!Q4) {
+    // d = 64 bf16 only: INT4 plans have at least four waves
+    if (p.nw == 2)
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 2, PAGED, Q4>), grid, dim3(128), 0, stream, a);
+    else
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 1, PAGED, Q4>), grid, dim3(64), 0, stream, a);
   }
 }
 
@@ -1145,40 +1251,43 @@ static void launch_bf16(const Plan &p, const AttnArgs &a, bool q4, hipStream_t s
     launch_main<D, false, false>(p, a, stream);
   }
   if (p.n_splits > 1) {
-    constexpr int E = EV_MERGE_E * D / 128;
+    constexpr int E = 4 * D / 128;
     const int64_t nrows = (int64_t)a.B * a.T * a.Hq;
     const int rows_per_wg = 256 / (D / E);
     dim3 mgrid((unsigned)((nrows + rows_per_wg - 1) / rows_per_wg));
-    hipLaunchKernelGGL((attn_merge_kernel<D, E, EV_MERGE_BATCH>), mgrid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_merge_kernel<D, E, 8>), mgrid, dim3(256), 0, stream, a);
   }
 }
 
 }  // namespace ev
 
-EV_API size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, int32_t Hq) {
+EV_API size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, int32_t Hq,
+                                          int64_t max_prefix_len) {
   ev::KvAddr addr;
   if (ev::make_kv_addr(kv, &addr) != EV_OK || B < 1 || T < 1 || T > ev::kMaxNodes || Hq < 1 ||
-      Hq % kv->n_kv_heads)
+      Hq % kv->n_kv_heads || max_prefix_len < 0)
     return 0;
-  ev::Plan p = ev::make_plan(addr, kv->dtype, B, T, Hq);
+  ev::Plan p = ev::make_plan(addr, kv->dtype, B, T, Hq, max_prefix_len);
   return ev::workspace_bytes(p, B, T, Hq, kv->head_dim);
 }
 
 EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
                                    const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
-                                   float sm_scale, void *out, float *lse, void *ws,
-                                   size_t ws_bytes, int32_t *dev_status, hipStream_t stream) {
+                                   int64_t max_prefix_len, float sm_scale, void *out, float *lse,
+                                   void *ws, size_t ws_bytes, int32_t *dev_status,
+                                   hipStream_t stream) {
   ev::KvAddr addr;
   ev_status st = ev::make_kv_addr(kv, &addr);
   if (st != EV_OK) return st;
-  if (B < 0 || T < 1 || T > ev::kMaxNodes || Hq < 1 || Hq % kv->n_kv_heads) return EV_ERR_SHAPE;
+  if (B < 0 || T < 1 || T > ev::kMaxNodes || Hq < 1 || Hq % kv->n_kv_heads || max_prefix_len < 0)
+    return EV_ERR_SHAPE;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return EV_ERR_ARG;
   if (B == 0) return EV_OK;
   if (!q || !prefix_len || !anc_mask || !out || !lse) return EV_ERR_NULL;
   // rows of q, out and the cache are read and written in 16-byte pieces
   if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)kv->k | (uintptr_t)kv->v) & 15) return EV_ERR_ARG;
   if ((int64_t)B * kv->n_kv_heads > (1 << 24)) return EV_ERR_SHAPE;
-  ev::Plan p = ev::make_plan(addr, kv->dtype, B, T, Hq);
+  ev::Plan p = ev::make_plan(addr, kv->dtype, B, T, Hq, max_prefix_len);
   size_t need = ev::workspace_bytes(p, B, T, Hq, kv->head_dim);
   if (ws_bytes < need || (need && !ws)) return EV_ERR_WORKSPACE;
 
@@ -1195,6 +1304,7 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   a.T = T;
   a.Hq = Hq;
   a.G = Hq / kv->n_kv_heads;
+  a.max_prefix = (int)std::min<int64_t>(max_prefix_len, 1 << 30);
   a.scale_log2 = sm_scale * ev::kLog2e;
   a.row_blocks = p.row_blocks;
   a.tiles_per_split = p.tiles_per_split;
@@ -1212,11 +1322,16 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
     a.part_scale = (float *)(base + o_bytes + ev::align_up(rows * sizeof(float), 256));
   }
   if (kv->dtype == EV_F32) {
-    dim3 grid(T, Hq, B);
-    if (kv->head_dim == 64)
-      hipLaunchKernelGGL(ev::tree_attn_f32_kernel<64>, grid, dim3(64), 0, stream, a);
+    const bool small = ev::f32_rows(T * a.G) == 8;
+    dim3 grid(p.grid);
+    if (kv->head_dim == 64 && small)
+      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<64, 8>), grid, dim3(256), 0, stream, a);
+    else if (kv->head_dim == 64)
+      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<64, 32>), grid, dim3(256), 0, stream, a);
+    else if (small)
+      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<128, 8>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(ev::tree_attn_f32_kernel<128>, grid, dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<128, 32>), grid, dim3(256), 0, stream, a);
   } else {
     const bool q4 = kv->dtype == EV_INT4;
     if (kv->head_dim == 64)
