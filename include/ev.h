@@ -107,13 +107,12 @@ ev_status ev_tree_mask_build(const int32_t *parent, int32_t B, int32_t T,
                              int32_t *dev_status, hipStream_t stream);
 
 /* Bytes of workspace ev_tree_attention needs for these shapes (0 when none, and 0 for
- * invalid arguments).  max_prefix_len (host) is the largest prefix_len[b] the call will
- * see; the key range [0, max_prefix_len + T) is what the work is split over, so pass the
- * batch's real longest prefix, not the cache capacity.  The same value must be passed to
- * ev_tree_attention.  The workspace holds arrival counters: zero-fill it (for example
- * with hipMemset) before its first use; every call leaves the counters at zero again, so
- * one zeroed workspace of the largest size serves calls of every smaller shape.  Calls
- * that overlap in time must not share a workspace. */
+ * invalid arguments): the split-L partial results when the key range is split across
+ * workgroups.  max_prefix_len (host) is the largest prefix_len[b] the call will see; the
+ * key range [0, max_prefix_len + T) is what the work is split over, so pass the batch's
+ * real longest prefix, not the cache capacity (a bound beyond the cache counts as the
+ * cache's capacity).  The same value must be passed to ev_tree_attention.  The workspace
+ * needs no initialisation; calls that overlap in time must not share one. */
 size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, int32_t Hq,
                                    int64_t max_prefix_len);
 
@@ -128,8 +127,7 @@ size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, i
  *   sm_scale   score scale (pass 1/sqrt(head_dim) for the usual attention)
  *   out  [B][T][Hq][head_dim], dtype kv->dtype;  lse [B][T][Hq] float, natural log of the
  *        softmax normaliser of the scaled scores.
- *   ws, ws_bytes: workspace of at least ev_tree_attention_workspace() bytes, zero-filled
- *        before its first use (see there).
+ *   ws, ws_bytes: workspace of at least ev_tree_attention_workspace() bytes.
  *   bf16 is computed with bf16 matrix-core products and float32 softmax/accumulation;
  *   f32 in float32 throughout.  EV_DERR_BOUNDS when L_b + T exceeds the cache or L_b
  *   exceeds max_prefix_len. */

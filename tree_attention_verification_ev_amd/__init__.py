@@ -241,8 +241,7 @@ def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, an
 
     max_prefix_len: an upper bound of prefix_len (host int); the work is split over its
     key range, so pass the batch's longest prefix.  When omitted, the cache's capacity
-    less T is used: always valid, but the split then spans the whole cache.  ws must be
-    zero-filled before its first use (it is allocated zeroed here when not passed)."""
+    less T is used: always valid, but the split then spans the whole cache."""
     _dev(q, "q", torch.bfloat16 if kv.dtype == torch.uint8 else kv.dtype)
     _dev(prefix_len, "prefix_len", torch.int32)
     _dev(anc_mask, "anc_mask", torch.int64)
@@ -255,7 +254,7 @@ def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, an
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
     need = ev_tree_attention_workspace(kv, B, T, Hq, mpl)
     if ws is None and need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     status = _status_word(dev, dev_status)
     code = lib().ev_tree_attention(_ptr(q), kv.ref(), _ptr(prefix_len), _ptr(anc_mask), B, T, Hq,

@@ -51,6 +51,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the reference max is raised
 constexpr int kXcds = 8;
+constexpr int kMaxSplits = 32;          // split-L partials per output row, at most
 
 struct AttnArgs {
   const void *q;
@@ -68,9 +69,8 @@ struct AttnArgs {
   int n_work;              // B * Hkv * row_blocks * n_splits
   void *out;               // final O (n_splits == 1)
   float *lse;              // final LSE (n_splits == 1)
-  _Float16 *part_o;        // [B][T][Hq][n_splits][D], scaled by 1 / part_scale
-  float *part_lse;         // [B][T][Hq][n_splits]
-  float *part_scale;       // [B][T][Hq][n_splits]
+  _Float16 *part_o;        // [B][T][Hq][n_splits][D], scaled by 1 / its scale
+  uint64_t *part_ls;       // [B][T][Hq][n_splits]: partial LSE bits | scale bits << 32
   int32_t *dev_status;
   const float *k_scale;    // INT4 caches: one scale per (slot, KV head) row
   const float *v_scale;
@@ -82,6 +82,13 @@ __device__ inline int64_t part_row(const AttnArgs &a, int64_t orow, int split) {
   return orow * a.n_splits + split;
 }
 
+// A split's partial LSE and the divisor its fp16 row was stored with, as one 64-bit word.
+__device__ inline uint64_t pack_ls(float lse, float scale) {
+  return (uint64_t)__float_as_uint(lse) | ((uint64_t)__float_as_uint(scale) << 32);
+}
+__device__ inline float ls_lse(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ inline float ls_scale(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+
 // Is logical slot `slot` visible to a query whose ancestor row is `anc` (prefix length L)?
 __device__ inline bool visible(int slot, int L, uint64_t anc) {
   int j = slot - L;
@@ -91,23 +98,24 @@ __device__ inline bool visible(int slot, int L, uint64_t anc) {
 // MFMA row index -> key within a 32-key subtile: swap bits 2 and 3.
 __device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// S^T = K Q^T of one 64-key tile as two 32-key subtiles; kfrag(st, ks) returns the K
-// fragment (A operand) of subtile st, head-dim step ks for this lane.
-template <int QT, int KS, typename KFrag>
-__device__ __forceinline__ void tile_scores(f32x16 (&s)[QT][2], const bf16x8 (&qf)[QT][KS],
+// S^T = K Q^T of NST 32-key subtiles of a 64-key tile (both, or the one a wavefront of a
+// key-split workgroup owns); kfrag(st, ks) returns the K fragment (A operand) of local
+// subtile st, head-dim step ks for this lane.
+template <int QT, int KS, int NST, typename KFrag>
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[QT][NST], const bf16x8 (&qf)[QT][KS],
                                             KFrag kfrag) {
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < NST; ++st)
 #pragma unroll
     for (int t = 0; t < QT; ++t) s[t][st] = f32x16{};
-  // The two subtiles alternate, so consecutive products accumulate into different
+  // With two subtiles they alternate, so consecutive products accumulate into different
   // registers and do not wait on each other; each K fragment is read one product ahead.
   bf16x8 kf = kfrag(0, 0);
 #pragma unroll
-  for (int i = 0; i < 2 * KS; ++i) {
-    const int st = i & 1, ks = i >> 1;
+  for (int i = 0; i < NST * KS; ++i) {
+    const int st = i % NST, ks = i / NST;
     const bf16x8 cur = kf;
-    if (i + 1 < 2 * KS) kf = kfrag((i + 1) & 1, (i + 1) >> 1);
+    if (i + 1 < NST * KS) kf = kfrag((i + 1) % NST, (i + 1) / NST);
 #pragma unroll
     for (int t = 0; t < QT; ++t)
       s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[t][ks], s[t][st], 0, 0, 0);
@@ -116,15 +124,15 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[QT][2], const bf16x8 (&q
 
 // Ancestor mask of a tile reaching past the prefix, applied in place to the scores: a key
 // that is neither a prefix slot nor an ancestor-or-self tree slot of the lane's query gets
-// -inf.  Register r of subtile st holds key st*32 + 16*(r>>3) + 8*hh + 4*((r>>2)&1) + (r&3)
-// (the K rows were fed with bits 2 and 3 of the row index swapped).
-template <int QT>
-__device__ __forceinline__ void tile_mask(f32x16 (&s)[QT][2], const uint64_t (&anc_q)[QT],
+// -inf.  Register r of local subtile st holds key key0 + st*32 + 16*(r>>3) + 8*hh +
+// 4*((r>>2)&1) + (r&3) (the K rows were fed with bits 2 and 3 of the row index swapped).
+template <int QT, int NST>
+__device__ __forceinline__ void tile_mask(f32x16 (&s)[QT][NST], const uint64_t (&anc_q)[QT],
                                           int key0, int L, int hh) {
 #pragma unroll
   for (int t = 0; t < QT; ++t)
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < NST; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = st * 32 + (r >> 3) * 16 + hh * 8 + ((r >> 2) & 1) * 4 + (r & 3);
@@ -138,14 +146,14 @@ __device__ __forceinline__ void tile_mask(f32x16 (&s)[QT][2], const uint64_t (&a
 // only when the tile could overflow 2^8 of headroom; tile_exp forms the probabilities,
 // their sum and the bf16 P fragments.  Each 8-register group of a subtile is 8 consecutive
 // keys, so the fragments are directly the B operand of O^T += V^T P^T.
-template <int QT, int DT>
-__device__ __forceinline__ void tile_rescale(const f32x16 (&s)[QT][2], f32x16 (&o)[QT][DT],
+template <int QT, int DT, int NST>
+__device__ __forceinline__ void tile_rescale(const f32x16 (&s)[QT][NST], f32x16 (&o)[QT][DT],
                                              float (&mref)[QT], float (&l)[QT], float scale_log2) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < NST; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][st][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
@@ -160,15 +168,15 @@ __device__ __forceinline__ void tile_rescale(const f32x16 (&s)[QT][2], f32x16 (&
   }
 }
 
-template <int QT>
-__device__ __forceinline__ void tile_exp(const f32x16 (&s)[QT][2], bf16x8 (&pf)[QT][2][2],
+template <int QT, int NST>
+__device__ __forceinline__ void tile_exp(const f32x16 (&s)[QT][NST], bf16x8 (&pf)[QT][NST][2],
                                          const float (&mref)[QT], float (&l)[QT], float scale_log2) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const float nb = mref[t] == -INFINITY ? 0.f : -mref[t];
     float sum = 0.f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < NST; ++st) {
       f32x16 p;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -185,13 +193,13 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[QT][2], bf16x8 (&pf)[
   }
 }
 
-// O^T += V^T P^T over one tile; vfrag(st, kk, dt) returns the V^T fragment (A operand): head
-// dims dt*32 + qn, keys st*32 + kk*16 + 8*hh + 0..7.
-template <int QT, int DT, typename VFrag>
-__device__ __forceinline__ void tile_pv(f32x16 (&o)[QT][DT], const bf16x8 (&pf)[QT][2][2],
+// O^T += V^T P^T over NST subtiles; vfrag(st, kk, dt) returns the V^T fragment (A operand)
+// of local subtile st: head dims dt*32 + qn, keys st*32 + kk*16 + 8*hh + 0..7.
+template <int QT, int DT, int NST, typename VFrag>
+__device__ __forceinline__ void tile_pv(f32x16 (&o)[QT][DT], const bf16x8 (&pf)[QT][NST][2],
                                         VFrag vfrag) {
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < NST; ++st)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -256,10 +264,7 @@ __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[
               f16x4{(_Float16)(ov[4 * j] * k), (_Float16)(ov[4 * j + 1] * k),
                     (_Float16)(ov[4 * j + 2] * k), (_Float16)(ov[4 * j + 3] * k)};
         }
-      if (hh == 0) {
-        a.part_lse[prow] = lse;
-        a.part_scale[prow] = scale;
-      }
+      if (hh == 0) a.part_ls[prow] = pack_ls(lse, scale);
     }
   }
 }
@@ -462,7 +467,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
         const int r = row0 + t * 32 + qn;
         if (r >= rows) continue;
         const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
-        a.part_lse[part_row(a, orow, split)] = -INFINITY;
+        a.part_ls[part_row(a, orow, split)] = pack_ls(-INFINITY, 1.f);
       }
     }
     return;
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnArgs a) {
     if (Q4 && tile + 1 < t_end) s0.load(a, K, V, seq_row, stbl, blk0, g, (tile + 1) * kKT, nkeys);
     f32x16 sc[QT][2];
     bf16x8 pf[QT][2][2];
-    tile_scores(sc, qf, kfrag);
+    tile_scores<QT, KS, 2>(sc, qf, kfrag);
     if (tile * kKT + kKT > L) tile_mask(sc, anc_q, tile * kKT, L, hh);
     tile_rescale(sc, o, mref, l, a.scale_log2);
     tile_exp(sc, pf, mref, l, a.scale_log2);
@@ -584,10 +589,17 @@ __device__ __forceinline__ bf16x4 lds_read_tr(lds_bf16x4 *__restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
 }
 
+// Output row (sequence, node, head order) of query row r of KV head g.
+__device__ inline int64_t out_row(const AttnArgs &a, int b, int g, int r) {
+  return ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
+}
+
 // write_rows for the DMA kernel (one query tile per wave): the wave's 32 normalised rows
 // go through an idle 8 KB of LDS (chunk-swizzled like a K tile) so that the global stores
 // are whole rows, 16 bytes per lane and four rows per instruction, instead of 8-byte pieces
-// scattered over 32 rows.  Values, rounding and the partial-split format are write_rows'.
+// scattered over 32 rows.  A split partial (fp16, pre-divided by max(1, |O|max) of its
+// row, with its LSE and divisor as one word) is stored non-temporally: the merge kernel
+// reads it once.
 template <int D>
 __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x16 (&o)[1][D / 32],
                                                   float mref, float l, int row0, int b, int g,
@@ -638,35 +650,39 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
     const int r = row0 + rr;
     const u32x4 v = *(const u32x4 *)(stage + rr * D + ((cc ^ (rr & 15)) << 3));
     if (r < rows) {
-      const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
-      if (part)   // read once, by the merge kernel: stored non-temporally
+      const int64_t orow = out_row(a, b, g, r);
+      if (part) {
         __builtin_nontemporal_store(v, (u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8));
-      else
+      } else {
         *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = v;
+      }
     }
   }
   const int r = row0 + qn;
   if (hh == 0 && r < rows) {
-    const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
-    if (part) {
-      const int64_t prow = part_row(a, orow, split);
-      a.part_lse[prow] = lse;
-      a.part_scale[prow] = scale;
-    } else {
+    const int64_t orow = out_row(a, b, g, r);
+    if (part)
+      a.part_ls[part_row(a, orow, split)] = pack_ls(lse, scale);
+    else
       a.lse[orow] = lse;
-    }
   }
 }
 
-template <int NW, bool PAGED>
+// Direct-to-LDS tree attention kernel, head_dim 128.  NW wavefronts of 32 query rows each;
+// KSPLIT (at most 32 rows per KV head, NW = 2): both wavefronts take the same 32 rows and
+// each scores and accumulates one 32-key half of every tile, the halves combined through
+// LDS at the end.
+template <int NW, bool PAGED, bool KSPLIT>
 __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int D = 128;
   constexpr int QT = 1;
+  constexpr int NST = KSPLIT ? 1 : 2;            // 32-key subtiles this wave computes
   constexpr int KS = D / 16, DT = D / 32, DCH = D / 8;
   constexpr int MAT = kKT * D;                   // bf16 elements of one K or V tile
   constexpr int IPW = kKT * DCH / 64 / NW;       // DMA instructions per wave per matrix
   constexpr int PER = 2 * IPW;                   // per wave per tile
   static_assert(IPW >= 1 && 2 * PER <= 63, "vmcnt range");
+  static_assert(!KSPLIT || NW == 2, "key-split workgroups have two wavefronts");
   constexpr int NT = NW * 64;
   // kStages K|V tile pairs, then the sequence's ancestor masks (64 x 8 bytes)
   __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT + kMaxNodes * 4];
@@ -685,7 +701,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int qn = lane & 31;
   const int hh = lane >> 5;
   const int rows = a.T * a.G;
-  const int row0 = (rb * NW + wave) * 32;
+  const int row0 = KSPLIT ? rb * 32 : (rb * NW + wave) * 32;
+  const int st0 = KSPLIT ? wave : 0;             // first 32-key subtile of this wave
 
   const int L = a.prefix_len[b];
   const int nkeys = L + a.T;
@@ -698,11 +715,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int t_end = min(t_begin + a.tiles_per_split, ntiles);
   if (t_begin >= t_end) {
     // an empty split (a shorter sequence of the batch): its partial carries no weight
-    if (a.n_splits > 1 && hh == 0 && row0 + qn < rows) {
-      const int r = row0 + qn;
-      const int64_t orow = ((int64_t)b * a.T + r / a.G) * a.Hq + g * a.G + r % a.G;
-      a.part_lse[part_row(a, orow, split)] = -INFINITY;
-    }
+    if (a.n_splits > 1 && hh == 0 && row0 + qn < rows && (!KSPLIT || wave == 0))
+      a.part_ls[part_row(a, out_row(a, b, g, row0 + qn), split)] = pack_ls(-INFINITY, 1.f);
     return;
   }
 
@@ -805,14 +819,14 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   int koff[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koff[ks] = krow * D + ((((2 * ks) | hh) ^ (qn & 15)) << 3);
-  const int r16 = lane & 15, grp = lane >> 4;
+  const int r16 = lane & 15, grp16 = lane >> 4;
   int voff[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int hr = 0; hr < 2; ++hr) {
       const int rr = (r16 >> 2) + 4 * hr;        // key within the 8-key group
-      const int d = dt * 32 + 16 * (grp & 1) + 4 * (r16 & 3);
+      const int d = dt * 32 + 16 * (grp16 & 1) + 4 * (r16 & 3);
       voff[dt][hr] = (8 * hh + rr) * D + (((d >> 3) ^ ((5 * (rr & 3)) & 15)) << 3) + (d & 7);
     }
 
@@ -822,16 +836,17 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt) o[0][dt] = f32x16{};
 
   // Stage index is a compile-time constant in every call below, so all LDS addresses are
-  // a lane-constant register plus an immediate offset.
-  auto scores_of = [&](f32x16 (&sc)[QT][2], auto stg) {
-    const __bf16 *kb = lds + decltype(stg)::value * 2 * MAT;
-    tile_scores(sc, qf, [&](int st, int ks) {
+  // a lane-constant register plus an immediate offset (plus the subtile of a key-split
+  // wave).
+  auto scores_of = [&](f32x16 (&sc)[QT][NST], auto stg) {
+    const __bf16 *kb = lds + decltype(stg)::value * 2 * MAT + st0 * 32 * D;
+    tile_scores<QT, KS, NST>(sc, qf, [&](int st, int ks) {
       return *(const bf16x8 *)(kb + st * 32 * D + koff[ks]);
     });
   };
-  auto pv_of = [&](const bf16x8 (&pf)[QT][2][2], auto stg) {
-    const __bf16 *vb = lds + decltype(stg)::value * 2 * MAT + MAT;
-    tile_pv(o, pf, [&](int st, int kk, int dt) {
+  auto pv_of = [&](const bf16x8 (&pf)[QT][NST][2], auto stg) {
+    const __bf16 *vb = lds + decltype(stg)::value * 2 * MAT + MAT + st0 * 32 * D;
+    tile_pv<QT, DT, NST>(o, pf, [&](int st, int kk, int dt) {
       const __bf16 *base = vb + (st * 32 + kk * 16) * D;
       const bf16x4 lo = lds_read_tr((lds_bf16x4 *)(base + voff[dt][0]));
       const bf16x4 hi = lds_read_tr((lds_bf16x4 *)(base + voff[dt][1]));
@@ -847,7 +862,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // j-1 with tile j+3, and compute the scores of j+1 (into sn; the matrix cores run them
   // while the wave continues) before the softmax and P V of j.  Returns false when j was
   // the last tile.
-  auto step = [&](int j, f32x16 (&sc)[QT][2], f32x16 (&sn)[QT][2], auto stg) -> bool {
+  auto step = [&](int j, f32x16 (&sc)[QT][NST], f32x16 (&sn)[QT][NST], auto stg) -> bool {
     constexpr int STG = decltype(stg)::value;
     using NEXT = std::integral_constant<int, (STG + 1) % kStages>;
     using REFILL = std::integral_constant<int, (STG + 3) % kStages>;
@@ -858,9 +873,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
       if (j + 3 < t_end) issue(j + 3, REFILL::value);
       scores_of(sn, NEXT{});
     }
-    if (j * kKT + kKT > L) tile_mask(sc, anc_q, j * kKT, L, hh);
+    if (j * kKT + kKT > L) tile_mask(sc, anc_q, j * kKT + st0 * 32, L, hh);
     tile_rescale(sc, o, mref, l, a.scale_log2);
-    bf16x8 pf[QT][2][2];
+    bf16x8 pf[QT][NST][2];
     tile_exp(sc, pf, mref, l, a.scale_log2);
     pv_of(pf, stg);
     return more;
@@ -887,7 +902,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   if (t_begin + 2 < t_end) issue(t_begin + 2, 2);
   landed(min(t_end - 1, t_begin + 2) - t_begin);
   wg_barrier();
-  f32x16 sa[QT][2], sb[QT][2];
+  f32x16 sa[QT][NST], sb[QT][NST];
   scores_of(sa, S0{});
   for (int j = t_begin;; j += 4) {
     if (!step(j, sa, sb, S0{})) break;
@@ -899,6 +914,31 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // read the stages of the last two tiles, never the two after them, and no DMA is in
   // flight.  Those two stages hold the waves' output rows (8 KB each).
   const int last = (t_end - 1 - t_begin) % kStages;
+  if constexpr (KSPLIT) {
+    // wave 1 hands its half (reference max, partial sum, accumulators) to wave 0 through
+    // the second free stage, element-major so the accesses are conflict-free
+    float *xch = (float *)(lds + ((last + 2) % kStages) * 2 * MAT);
+    if (wave == 1) {
+      xch[lane] = mref[0];
+      xch[64 + lane] = l[0];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(2 + dt * 16 + i) * 64 + lane] = o[0][dt][i];
+    }
+    __syncthreads();
+    if (wave == 1) return;
+    const float m1 = xch[lane], l1 = xch[64 + lane];
+    const float mnew = fmaxf(mref[0], m1);
+    const float a0 = mref[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[0] - mnew);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mnew);
+    l[0] = l[0] * a0 + l1 * a1;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[0][dt][i] = o[0][dt][i] * a0 + xch[(2 + dt * 16 + i) * 64 + lane] * a1;
+    mref[0] = mnew;
+  }
   uint16_t *stage = (uint16_t *)(lds + ((last + 1 + (wave >> 2)) % kStages) * 2 * MAT +
                                  (wave & 3) * 32 * D);
   write_rows_staged<D>(a, o, mref[0], l[0], row0, b, g, split, qn, hh, stage);
@@ -930,8 +970,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     for (int u = 0; u < BATCH; ++u) {
       const int s = s0 + u;
       const bool ok = s < nvalid;
-      ls[u] = ok ? a.part_lse[row * nvalid + s] : -INFINITY;
-      sc[u] = ok ? a.part_scale[row * nvalid + s] : 0.f;
+      const uint64_t w = ok ? a.part_ls[row * nvalid + s] : pack_ls(-INFINITY, 0.f);
+      ls[u] = ls_lse(w);
+      sc[u] = ls_scale(w);
       x[u] = ok ? *(const hE *)(a.part_o + (row * nvalid + s) * D + c * E) : hE{};
     }
     float bm = mx;
@@ -1130,11 +1171,12 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // Launch policy.
-constexpr int kMaxSplits = 32;
 constexpr int kCUs = 256;
 
 struct Plan {
   int nw;                // waves per workgroup
+  bool dma;              // bf16 d = 128: the direct-to-LDS kernel
+  bool ksplit;           // DMA kernel with <= 32 rows per KV head: waves split each tile's keys
   int row_blocks;
   int tiles_per_split, n_splits;
   int n_work, grid;
@@ -1185,6 +1227,8 @@ static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq, int64_t
   // the DMA issue); its 128 KB of LDS leave room for one workgroup per CU.
   const bool dma = dtype == EV_BF16 && kv.d == 128;
   if (dma) p.nw = std::max(p.nw, 2);
+  p.dma = dma;
+  p.ksplit = dma && waves_needed == 1;
   p.row_blocks = (waves_needed + p.nw - 1) / p.nw;
   const int max_tiles = (plan_slots(kv, T, max_prefix_len) + kKT - 1) / kKT;
   const int units = B * kv.hkv * p.row_blocks;
@@ -1208,10 +1252,11 @@ static size_t part_rows(const Plan &p, int B, int T, int Hq) {
   return (size_t)p.n_splits * B * T * Hq;
 }
 
+// Workspace of a split plan: the fp16 partial rows, then their (LSE, divisor) words.
 static size_t workspace_bytes(const Plan &p, int B, int T, int Hq, int D) {
   if (p.n_splits <= 1) return 0;
   size_t rows = part_rows(p, B, T, Hq);
-  return align_up(rows * D * sizeof(_Float16), 256) + 2 * align_up(rows * sizeof(float), 256);
+  return align_up(rows * D * sizeof(_Float16), 256) + align_up(rows * sizeof(uint64_t), 256);
 }
 
 template <int D, bool PAGED, bool Q4>
@@ -1220,11 +1265,13 @@ static void launch_main(const Plan &p, const AttnArgs &a, hipStream_t stream) {
   if constexpr (!Q4 && D == 128) {
     // bf16 with d = 128: the direct-to-LDS kernel (the plan gives it at least 2 waves)
     if (p.nw == 8)
-      hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED>), grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED, false>), grid, dim3(512), 0, stream, a);
     else if (p.nw == 4)
-      hipLaunchKernelGGL((tree_attn_dma_kernel<4, PAGED>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_dma_kernel<4, PAGED, false>), grid, dim3(256), 0, stream, a);
+    else if (p.ksplit)
+      hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED, true>), grid, dim3(128), 0, stream, a);
     else
-      hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED>), grid, dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED, false>), grid, dim3(128), 0, stream, a);
   } else if (p.nw == 8) {
     hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 8, PAGED, Q4>), grid, dim3(512), 0, stream, a);
   } else if (p.nw == 4) {
@@ -1316,10 +1363,9 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   if (need) {
     size_t rows = ev::part_rows(p, B, T, Hq);
     char *base = (char *)ws;
-    size_t o_bytes = ev::align_up(rows * kv->head_dim * sizeof(_Float16), 256);
+    const size_t o_bytes = ev::align_up(rows * kv->head_dim * sizeof(_Float16), 256);
     a.part_o = (_Float16 *)base;
-    a.part_lse = (float *)(base + o_bytes);
-    a.part_scale = (float *)(base + o_bytes + ev::align_up(rows * sizeof(float), 256));
+    a.part_ls = (uint64_t *)(base + o_bytes);
   }
   if (kv->dtype == EV_F32) {
     const bool small = ev::f32_rows(T * a.G) == 8;
