@@ -31,7 +31,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import tree_attention_verification_ev_amd as ev  # noqa: E402
-from synth import config_by_name, draft_tree_logits, generate, sampled_drafts  # noqa: E402
+from synth import CONFIGS, config_by_name, draft_tree_logits, generate, sampled_drafts  # noqa: E402
 from synth.device import to_device  # noqa: E402
 
 METRIC = "verified tree-nodes/s + KV HBM GB/s (% roofline), GQA 64/8 d128 L=4096 T=64"
@@ -266,34 +266,91 @@ def traffic_entry():
         return None
 
 
-def cpu_baseline(inp, budget_s: float):
-    import oracle
+def cpu_description():
+    """CPU model and the BLAS library numpy runs on (as threadpoolctl reports them)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     from threadpoolctl import threadpool_info
+    blas = [{"api": p.get("internal_api"), "version": p.get("version"),
+             "threads": p.get("num_threads"), "library": os.path.basename(p.get("filepath", ""))}
+            for p in threadpool_info() if p.get("user_api") == "blas"]
+    return model, blas
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The oracle, untouched, on the host: whole verification steps for about budget_s
+    seconds (the reported value), then the median of 3 timings of each part, attention
+    also with one BLAS thread."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     cfg = inp.cfg
     scale = float(np.float32(1.0 / math.sqrt(cfg.d)))
+    rej = "rejection" in cfg.accept
+
+    def mask():
+        return oracle.tree_mask_batch(inp.parent)[0]
+
+    def attention(anc):
+        return oracle.tree_attention_batch(inp.q, inp.k, inp.v, inp.prefix_len, anc, inp.layout,
+                                           inp.block_table, cfg.block_size, scale)
+
+    def accept():
+        if rej:
+            return oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
+        return oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
+
+    def compact(r):
+        return oracle.kv_compact(inp.k, inp.v, inp.prefix_len, r[1], r[0], inp.layout,
+                                 inp.block_table, cfg.block_size)
+
     steps = 0
     t0 = time.perf_counter()
     while True:
-        anc, _ = oracle.tree_mask_batch(inp.parent)
-        oracle.tree_attention_batch(inp.q, inp.k, inp.v, inp.prefix_len, anc, inp.layout,
-                                    inp.block_table, cfg.block_size, scale)
-        if "rejection" in cfg.accept:
-            r = oracle.rejection_batch(inp.logits, inp.tokens, inp.parent, inp.tau, inp.uniforms)
-        else:
-            r = oracle.greedy_batch(inp.logits, inp.tokens, inp.parent)
-        oracle.kv_compact(inp.k, inp.v, inp.prefix_len, r[1], r[0], inp.layout, inp.block_table,
-                          cfg.block_size)
+        anc = mask()
+        attention(anc)
+        r = accept()
+        compact(r)
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+
+    def med(fn, *a):
+        ts = []
+        for _ in range(3):
+            t = time.perf_counter()
+            out = fn(*a)
+            ts.append(time.perf_counter() - t)
+        return statistics.median(ts), out
+
+    t_mask, anc = med(mask)
+    t_attn, _ = med(attention, anc)
+    with threadpool_limits(limits=1):
+        t_attn1, _ = med(attention, anc)
+    t_acc, r = med(accept)
+    t_cmp, _ = med(compact, r)
+    work = algorithmic_work(inp)
+    model, blas = cpu_description()
     return {"value": cfg.B * cfg.T * steps / el, "unit": "tree-nodes/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{steps} full verification step(s) of the {cfg.name} workload (B={cfg.B}, "
                       f"T={cfg.T}): float64 mask + explicit-mask attention + "
-                      f"{'rejection' if 'rejection' in cfg.accept else 'greedy'} walk + compaction, "
-                      f"{el:.1f} s on the host"}
+                      f"{'rejection' if rej else 'greedy'} walk + compaction, "
+                      f"{el:.1f} s on the host; then 3 timings of each part",
+            "cpu_model": model, "blas": blas,
+            "parts_s": {"mask": t_mask, "attention": t_attn, "attention_1_thread": t_attn1,
+                        "accept": t_acc, "compact": t_cmp},
+            "attention_nodes_per_s": cfg.B * cfg.T / t_attn,
+            "attention_bytes_per_s": work["bytes"] / t_attn,
+            "attention_bytes_per_s_1_thread": work["bytes"] / t_attn1}
 
 
 def timed_rotation(step_fns, steps, warmup):
@@ -591,6 +648,99 @@ def bench_int4(args, cfg):
     print(json.dumps(result), flush=True)
 
 
+MAX_SETS = 64                      # buffer sets of a tiny workload (launch-bound anyway)
+ROOF_RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)   # flop per byte
+
+
+def build_sets(inp):
+    """Buffer sets of one workload: enough copies that the rotation touches >= 512 MB."""
+    cfg = inp.cfg
+    dev0 = to_device(inp)
+    per_set = sum(t.numel() * t.element_size() for t in (dev0.q, dev0.k, dev0.v, dev0.logits))
+    n_sets = min(MAX_SETS, max(1, math.ceil(FOOTPRINT_BYTES / per_set)))
+    kv_tmp = ev.KvCache(dev0.k, dev0.v, dev0.block_table)
+    mpl = int(inp.prefix_len.max())
+    ws_attn = torch.empty(max(1, ev.ev_tree_attention_workspace(kv_tmp, cfg.B, cfg.T, cfg.Hq, mpl)),
+                          dtype=torch.uint8, device="cuda")
+    ws_acc = torch.zeros(max(1, ev.ev_accept_workspace(cfg.B, cfg.T, cfg.V)), dtype=torch.uint8,
+                         device="cuda")
+    return [BufferSet(inp, dev0 if i == 0 else to_device(inp), ws_attn, ws_acc)
+            for i in range(n_sets)]
+
+
+def rooflines(inp, kt):
+    """Rates and roofline fractions of one workload's attention call and step."""
+    cfg = inp.cfg
+    work = algorithmic_work(inp)
+    t_attn = kt["attention"]["mean_us"] * 1e-6
+    t_acc = kt["accept"]["mean_us"] * 1e-6
+    tflops = work["flops"] / t_attn / 1e12
+    gbps = work["bytes"] / t_attn / 1e9
+    if cfg.dtype == "f32":
+        bound, frac = "latency", None
+    elif work["flops"] / work["bytes"] > ROOF_RIDGE:
+        bound, frac = "mfma", tflops / PEAK_BF16_TFLOPS
+    else:
+        bound, frac = "hbm", gbps / PEAK_HBM_GBPS
+    return {"workload": cfg.workload, "kv_layout": inp.layout,
+            "acceptance": "rejection" if "rejection" in cfg.accept else "greedy",
+            "kernels_us": {k: round(v["mean_us"], 3) for k, v in kt.items()},
+            "step_us": round(sum(v["mean_us"] for v in kt.values()), 3),
+            "tree_nodes_per_s_step": cfg.B * cfg.T / (sum(v["mean_us"] for v in kt.values()) * 1e-6),
+            "attention_tree_nodes_per_s": cfg.B * cfg.T / t_attn,
+            "attention_tflops": tflops, "attention_mfma_frac": tflops / PEAK_BF16_TFLOPS,
+            "attention_gbps": gbps, "attention_hbm_frac": gbps / PEAK_HBM_GBPS,
+            "attention_bound": bound, "attention_frac_of_bound": frac,
+            "algorithmic_flops": work["flops"], "algorithmic_bytes": work["bytes"],
+            "accept_logit_gbps": work["logit_bytes"] / t_acc / 1e9,
+            "accept_hbm_frac": work["logit_bytes"] / t_acc / 1e9 / PEAK_HBM_GBPS}
+
+
+def config_entry(cfg, reps):
+    """Per-call times of every part of the step for one workload (parity configs)."""
+    inp = generate(cfg)
+    sets = build_sets(inp)
+    sets[0].step()
+    torch.cuda.synchronize()
+    if int(sets[0].status.item()) != 0:
+        raise ev.EvError(int(sets[0].status.item()), f"bench eager step ({cfg.name})")
+    e = rooflines(inp, kernel_times(sets, reps))
+    e["buffer_sets"] = len(sets)
+    del sets
+    torch.cuda.empty_cache()
+    return e
+
+
+def capacity_entry(inp, sets, caps):
+    """Attention per call over caches sized for longer contexts (same contents, NaN beyond),
+    split plan from the real longest prefix: the time should not depend on the capacity."""
+    cfg = inp.cfg
+    out = {}
+    for cap in caps:
+        kvs = []
+        for st in sets:
+            k = torch.full((cfg.B, cfg.Hkv, cap, cfg.d), float("nan"), dtype=torch.bfloat16,
+                           device="cuda")
+            v = torch.full_like(k, float("nan"))
+            k[:, :, :inp.cap] = st.d.k
+            v[:, :, :inp.cap] = st.d.v
+            kvs.append(ev.KvCache(k, v))
+        mpl = int(inp.prefix_len.max())
+        ws = torch.empty(max(1, ev.ev_tree_attention_workspace(kvs[0], cfg.B, cfg.T, cfg.Hq, mpl)),
+                         dtype=torch.uint8, device="cuda")
+
+        def call(i, kv):
+            st = sets[i]
+            ev.ev_tree_attention(st.d.q, kv, st.d.prefix_len, st.anc, st.scale, st.out, st.lse, ws,
+                                 st.status, max_prefix_len=mpl)
+
+        fns = [lambda i=i, kv=kv: call(i, kv) for i, kv in enumerate(kvs)]
+        out[str(cap)] = round(call_time_us(fns), 3)
+        del kvs, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -605,6 +755,8 @@ def main():
                          "attention over an INT4 cache against the bf16 cache")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-call timings of the other workloads and cache capacities")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -634,16 +786,11 @@ def main():
     if args.path == "int4":
         return bench_int4(args, cfg)
     inp = generate(cfg)
-    dev0 = to_device(inp)
-    per_set = sum(t.numel() * t.element_size() for t in (dev0.q, dev0.k, dev0.v, dev0.logits))
-    n_sets = max(1, math.ceil(FOOTPRINT_BYTES / per_set))
-    kv_tmp = ev.KvCache(dev0.k, dev0.v, dev0.block_table)
-    ws_attn = torch.zeros(max(1, ev.ev_tree_attention_workspace(kv_tmp, cfg.B, cfg.T, cfg.Hq,
-                                                                int(inp.prefix_len.max()))),
-                          dtype=torch.uint8, device="cuda")
-    ws_acc = torch.zeros(max(1, ev.ev_accept_workspace(cfg.B, cfg.T, cfg.V)), dtype=torch.uint8,
-                         device="cuda")
-    sets = [BufferSet(inp, dev0 if i == 0 else to_device(inp), ws_attn, ws_acc) for i in range(n_sets)]
+    sets = build_sets(inp)
+    n_sets = len(sets)
+    mode = sets[0].mode
+    if args.calibrate:          # counter runs profile the main workload's kernels only
+        args.no_configs = True
 
     # eager reference of the acceptance result, then capture
     sets[0].step()
@@ -698,6 +845,16 @@ def main():
         bound, peak, unit = "alu", PEAK_F32_TFLOPS, "TFLOP/s"
         achieved = work["flops"] / t_attn / 1e12
     kv_gbps = work["bytes"] / t_attn / 1e9
+    this = rooflines(inp, kt)
+    this["buffer_sets"] = n_sets
+    capacity = (capacity_entry(inp, sets, (32848, 131152))
+                if not inp.cfg.paged and cfg.B == 1 and not args.no_configs else None)
+    del sets, graphs, rotation
+    torch.cuda.empty_cache()
+    configs = {}
+    if not args.no_configs:
+        for c in CONFIGS:
+            configs[c.name] = this if c.name == cfg.name else config_entry(c, 5)
     box = box_peaks()
     result = {
         "metric": METRIC,
@@ -709,7 +866,7 @@ def main():
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.workload, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "L": cfg.L, "T": cfg.T, "V": cfg.V, "kv_layout": inp.layout,
-                   "acceptance": sets[0].mode, "tau": cfg.tau, "buffer_sets": n_sets},
+                   "acceptance": mode, "tau": cfg.tau, "buffer_sets": n_sets},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic_entry(),
                      "kernel": "ev_tree_attention", "algorithmic_flops": work["flops"],
@@ -725,6 +882,9 @@ def main():
         "kernels_us_p10_p90": {k: [round(v["p10_us"], 3), round(v["p90_us"], 3)] for k, v in kt.items()},
         "accept_len": int(ref[0].float().mean().item()),
         "tokens_per_step": float(ref[0].float().mean().item()) + 1.0,
+        "attention_us_by_cache_capacity": (dict({str(inp.cap): round(kt["attention"]["mean_us"], 3)},
+                                                **capacity) if capacity else None),
+        "configs": configs or None,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

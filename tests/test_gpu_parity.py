@@ -115,6 +115,8 @@ ATTN_SMALL = [
     # 16 x 8 x 2 = 256 work units: one split, the register-staged kernel's unsplit output
     ("bf16_d64_one_split", scaled(C4, d=64, L=(100, 900), V=64)),
     ("f32_d128", scaled(C1, d=128, L=190, Hq=8, Hkv=2, V=64)),
+    # float32 over a shuffled block table, 64 rows per KV head (two row blocks of 32)
+    ("f32_paged_gqa", scaled(C4, dtype="f32", B=2, T=16, Hq=32, Hkv=8, L=(60, 300), V=64)),
     ("gqa4_T26", scaled(C2, Hq=32, Hkv=8, L=515, V=64)),
     # 64 rows per KV head: the two-wavefront DMA workgroup
     ("gqa8_T8", scaled(C3, T=8, L=257, V=64)),
@@ -186,6 +188,44 @@ def test_attention_serving_capacity_paged():
     table = torch.full((B, wide), -1, dtype=torch.int32, device="cuda")
     table[:, :inp.block_table.shape[1]] = dev.block_table
     check_attention_dev(inp, ev.KvCache(dev.k, dev.v, table), dev, seqs=[0, 5, 11])
+
+
+@pytest.mark.parametrize("L", [300, 350, 410, 4000])
+def test_attention_planned_beyond_the_prefix(L):
+    """Splits planned for a 4096-token prefix over a shorter one: the contiguous kernel
+    fetches each split's first two tiles before it knows the length, so with L = 300 or
+    350 the sequence's partial last tile is such an early tile (its stale rows past the
+    sequence must not reach the output) and later splits are empty."""
+    inp = generate(scaled(C3, L=L, V=64), with_logits=False)
+    dev = to_device(inp)
+    cap = 4096 + C3.T + 16
+    k = torch.full((1, C3.Hkv, cap, C3.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v = torch.full_like(k, float("nan"))
+    k[:, :, :inp.cap] = dev.k
+    v[:, :, :inp.cap] = dev.v
+    kv = ev.KvCache(k, v)
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    out, lse = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(C3), check=True,
+                                    max_prefix_len=4096)
+    O, LSE = out.float().cpu().numpy(), lse.cpu().numpy()
+    Oo, Lo = oracle_attention(inp)
+    assert np.isfinite(O).all() and np.isfinite(LSE).all()
+    assert np.abs(O - Oo).max() <= O_TOL_BF16 and np.abs(LSE - Lo).max() <= LSE_TOL_BF16
+
+
+def test_attention_paged_planned_beyond_the_prefix():
+    inp = generate(scaled(C4, B=3, L=(100, 700), V=64), with_logits=False)
+    dev = to_device(inp)
+    table = torch.full((3, 260), -1, dtype=torch.int32, device="cuda")
+    table[:, :inp.block_table.shape[1]] = dev.block_table
+    kv = ev.KvCache(dev.k, dev.v, table)
+    anc, _ = ev.ev_tree_mask_build(dev.parent, check=True)
+    out, lse = ev.ev_tree_attention(dev.q, kv, dev.prefix_len, anc, scale_of(C4), check=True,
+                                    max_prefix_len=4000)
+    Oo, Lo = oracle_attention(inp)
+    O, LSE = out.float().cpu().numpy(), lse.cpu().numpy()
+    ratio, _ = o_error(O, Oo, np.isfinite(Lo), "bf16")
+    assert ratio <= 1.0 and np.abs(LSE - Lo).max() <= LSE_TOL_BF16
 
 
 def test_paged_equals_contiguous_on_the_same_data():

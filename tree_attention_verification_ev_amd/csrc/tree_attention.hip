@@ -62,6 +62,7 @@ struct AttnArgs {
   const uint64_t *anc;
   int B, T, Hq, G;
   int max_prefix;          // host bound of every prefix_len[b]; splits cover its key range
+  int max_tiles;           // 64-key tiles of that range (the plan's)
   float scale_log2;        // sm_scale * log2(e)
   int row_blocks;
   int tiles_per_split;
@@ -704,41 +705,11 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int row0 = KSPLIT ? rb * 32 : (rb * NW + wave) * 32;
   const int st0 = KSPLIT ? wave : 0;             // first 32-key subtile of this wave
 
-  const int L = a.prefix_len[b];
-  const int nkeys = L + a.T;
-  if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
-    if (threadIdx.x == 0) report(a.dev_status, EV_DERR_BOUNDS);
-    return;
-  }
-  const int ntiles = (nkeys + kKT - 1) / kKT;
-  const int t_begin = split * a.tiles_per_split;
-  const int t_end = min(t_begin + a.tiles_per_split, ntiles);
-  if (t_begin >= t_end) {
-    // an empty split (a shorter sequence of the batch): its partial carries no weight
-    if (a.n_splits > 1 && hh == 0 && row0 + qn < rows && (!KSPLIT || wave == 0))
-      a.part_ls[part_row(a, out_row(a, b, g, row0 + qn), split)] = pack_ls(-INFINITY, 1.f);
-    return;
-  }
-
   const __bf16 *Q = (const __bf16 *)a.q;
   const __bf16 *K = (const __bf16 *)a.k;
   const __bf16 *V = (const __bf16 *)a.v;
   const int64_t seq_base = PAGED ? 0 : (int64_t)(b * a.kv.hkv + g) * a.kv.cap * D;
-
-  int blk0 = 0;
-  if (PAGED) {
-    blk0 = (t_begin * kKT) >> a.kv.block_shift;
-    const int nblk = ((min(t_end * kKT, nkeys) - 1) >> a.kv.block_shift) - blk0 + 1;
-    bool bad = false;
-    for (int i = threadIdx.x; i < nblk; i += NT) {
-      const int blk = a.kv.table[(int64_t)b * a.kv.max_blocks + blk0 + i];
-      const bool ok = blk >= 0 && blk < a.kv.n_blocks;
-      bad |= !ok;
-      stbl[i] = ok ? blk : -1;
-    }
-    if (__any(bad) && lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
-    __syncthreads();
-  }
+  const int t_begin = split * a.tiles_per_split;
 
   bf16x8 qf[QT][KS];                             // filled from LDS in the prologue
   uint64_t anc_q[QT];                            // likewise
@@ -784,6 +755,70 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     doffK[i] = ((pc ^ swap23(key & 15)) << 3);
     doffV[i] = ((pc ^ ((5 * (key & 3)) & 15)) << 3);
   }
+  // DMA of one tile's K and V rows into stage stg, from element offsets row_of(slot).
+  auto issue_rows = [&](int tile, int stg, auto row_of) {
+    __bf16 *kd = lds + stg * 2 * MAT;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int64_t off = row_of(tile * kKT + dkey[i]);
+      const int blk = wave * IPW + i;
+      dma16(K + off + doffK[i], kd + blk * 512);
+      dma16(V + off + doffV[i], kd + MAT + blk * 512);
+    }
+  };
+
+  // Prologue, first part: the masks, the query rows and, for a contiguous cache, the
+  // split's first two tiles go out before the prefix length is known (its load is a
+  // dependent round trip).  The speculative tiles read slots up to the end of the planned
+  // key range, clamped into the cache; slots past the sequence are dealt with once the
+  // length is known (V rows zeroed, scores masked).
+  if (wave == 0) issue_anc();
+  issue_q();
+  int n_early = 0;                               // tiles issued before the length is known
+  if constexpr (!PAGED) {
+    auto spec_row = [&](int slot) {
+      return seq_base + (int64_t)min<int64_t>(slot, a.kv.cap - 1) * D;
+    };
+    issue_rows(t_begin, 0, spec_row);
+    n_early = 1;
+    if (t_begin + 1 < a.max_tiles) {
+      issue_rows(t_begin + 1, 1, spec_row);
+      n_early = 2;
+    }
+  }
+
+  const int L = a.prefix_len[b];
+  const int nkeys = L + a.T;
+  if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
+    if (threadIdx.x == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    wait_vm<0>();                                // no DMA into LDS outlives the wave
+    return;
+  }
+  const int ntiles = (nkeys + kKT - 1) / kKT;
+  const int t_end = min(t_begin + a.tiles_per_split, ntiles);
+  if (t_begin >= t_end) {
+    // an empty split (a shorter sequence of the batch): its partial carries no weight
+    if (a.n_splits > 1 && hh == 0 && row0 + qn < rows && (!KSPLIT || wave == 0))
+      a.part_ls[part_row(a, out_row(a, b, g, row0 + qn), split)] = pack_ls(-INFINITY, 1.f);
+    wait_vm<0>();
+    return;
+  }
+
+  int blk0 = 0;
+  if (PAGED) {
+    blk0 = (t_begin * kKT) >> a.kv.block_shift;
+    const int nblk = ((min(t_end * kKT, nkeys) - 1) >> a.kv.block_shift) - blk0 + 1;
+    bool bad = false;
+    for (int i = threadIdx.x; i < nblk; i += NT) {
+      const int blk = a.kv.table[(int64_t)b * a.kv.max_blocks + blk0 + i];
+      const bool ok = blk >= 0 && blk < a.kv.n_blocks;
+      bad |= !ok;
+      stbl[i] = ok ? blk : -1;
+    }
+    if (__any(bad) && lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    __syncthreads();
+  }
+
   // Element offset of a slot's row (PAGED: from the LDS block-id cache; bad ids read row 0,
   // already reported).
   auto row_off = [&](int slot) -> int64_t {
@@ -796,16 +831,22 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   auto issue = [&](int tile, int stg) {
     const int key0 = tile * kKT;
     const bool full = key0 + kKT <= nkeys;
-    __bf16 *kd = lds + stg * 2 * MAT;
+    issue_rows(tile, stg, [&](int slot) {
+      // past the sequence: finite data, masked out
+      return row_off(!full && slot >= nkeys ? key0 : slot);
+    });
+  };
+  // A speculatively issued tile that reaches past the sequence: once it has landed, each
+  // wave zeroes the V rows past the sequence among those it fetched (a zero probability
+  // times a stale value must not make NaN); the scores of those keys are masked anyway.
+  auto fix_tail = [&](int tile, int stg) {
+    const int key0 = tile * kKT;
+    if (key0 + kKT <= nkeys) return;
+    __bf16 *vd = lds + stg * 2 * MAT + MAT;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      int slot = key0 + dkey[i];
-      if (!full && slot >= nkeys) slot = key0;   // past the sequence: finite data, masked out
-      const int64_t off = row_off(slot);
-      const int blk = wave * IPW + i;
-      dma16(K + off + doffK[i], kd + blk * 512);
-      dma16(V + off + doffV[i], kd + MAT + blk * 512);
-    }
+    for (int i = 0; i < IPW; ++i)
+      if (key0 + dkey[i] >= nkeys) *(u32x4 *)(vd + (wave * IPW + i) * 512 + lane * 8) = u32x4{};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   // Wait until the tile `newer` tiles older than the newest issued one has landed.
   auto landed = [&](int newer) {
@@ -869,6 +910,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     const bool more = j + 1 < t_end;
     if (more) {
       landed(min(t_end - 1, j + 2) - (j + 1));
+      if constexpr (!PAGED)
+        if (j == t_begin) fix_tail(j + 1, NEXT::value);   // the second early tile
       wg_barrier();                              // tile j+1 visible; stage of j-1 free
       if (j + 3 < t_end) issue(j + 3, REFILL::value);
       scores_of(sn, NEXT{});
@@ -881,18 +924,20 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     return more;
   };
 
-  // prologue: Q and the first two tiles in flight; once this wave's Q rows have landed
-  // its fragments are read, and after every wave has them the third tile goes into the
-  // area they occupied; then the scores of the first tile.
-  if (wave == 0) issue_anc();
-  issue_q();
-  issue(t_begin, 0);
-  if (t_begin + 1 < t_end) {
-    issue(t_begin + 1, 1);
-    wait_vm<2 * PER>();                          // masks and Q landed (this wave's own rows)
-  } else {
-    wait_vm<PER>();
+  // Prologue, second part: a paged cache's first two tiles (their block ids are in LDS
+  // now).  Once this wave's Q rows have landed its fragments are read, and after every
+  // wave has them the third tile goes into the area they occupied; then the scores of the
+  // first tile.
+  if constexpr (PAGED) {
+    issue(t_begin, 0);
+    n_early = 1;
+    if (t_begin + 1 < t_end) {
+      issue(t_begin + 1, 1);
+      n_early = 2;
+    }
   }
+  if (n_early == 2) wait_vm<2 * PER>();          // masks and Q landed (this wave's own rows)
+  else wait_vm<PER>();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qf[0][ks] = *(const bf16x8 *)(qlds + qn * D + ((((2 * ks) | hh) ^ (qn & 15)) << 3));
@@ -900,7 +945,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   wg_barrier();                                  // every wave holds its Q: stages 2, 3 free
   anc_q[0] = row0 + qn < rows ? s_anc[(row0 + qn) / a.G] : 0ull;
   if (t_begin + 2 < t_end) issue(t_begin + 2, 2);
+  // (with an early second tile beyond t_end this waits for everything in flight)
   landed(min(t_end - 1, t_begin + 2) - t_begin);
+  if constexpr (!PAGED) fix_tail(t_begin, 0);
   wg_barrier();
   f32x16 sa[QT][NST], sb[QT][NST];
   scores_of(sa, S0{});
@@ -1009,7 +1056,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 // scores key k against rows w, w + 4, ... (query rows are broadcast reads), so a row's 64
 // scores lie across one wavefront and its max and sum are wavefront (DPP) reductions.  P V:
 // thread t owns head dimension t % D of rows t / D, t / D + 256 / D, ...
-template <int D, int R>
+// Workgroup barrier for LDS data only: the wave's LDS accesses complete, then s_barrier.
+// Unlike __syncthreads it does not wait for global loads, so a tile prefetched into
+// registers stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, int R, bool PAGED>
 __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
   constexpr int NT = 256;
   constexpr int C4 = D / 4;                 // 16-byte pieces per row
@@ -1069,7 +1123,8 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
       const int slot = key0 + key;
       f32x4 xk = {}, xv = {};
       if (slot < nkeys) {
-        const int64_t off = a.kv.slot_offset(b, g, slot);
+        const int64_t off = PAGED ? a.kv.slot_offset(b, g, slot)
+                                  : ((int64_t)(b * a.kv.hkv + g) * a.kv.cap + slot) * D;
         if (off >= 0) {
           xk = *(const f32x4 *)(K + off + 4 * c);
           xv = *(const f32x4 *)(V + off + 4 * c);
@@ -1101,9 +1156,9 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
   const int ntiles = (nkeys + kKT - 1) / kKT;
   load(0);
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();                        // the previous tile's P V is done with sK/sV/sP
+    lds_barrier();                          // the previous tile's P V is done with sK/sV/sP
     store();
-    __syncthreads();
+    lds_barrier();
     if (t + 1 < ntiles) load((t + 1) * kKT);
     const int slot = t * kKT + lane;
     float s[RW];
@@ -1133,7 +1188,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
       sP[r * kKT + lane] = p;
       if (lane == 0) sA[r] = alpha;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int r = prow + RSTEP * j;
@@ -1159,7 +1214,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
       a.lse[orow_of(r)] = l[i] > 0.f ? (m[i] + log2f(l[i])) * kLn2 : -INFINITY;
     }
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int r = prow + RSTEP * j;
@@ -1179,6 +1234,7 @@ struct Plan {
   bool ksplit;           // DMA kernel with <= 32 rows per KV head: waves split each tile's keys
   int row_blocks;
   int tiles_per_split, n_splits;
+  int max_tiles;         // 64-key tiles of the planned key range
   int n_work, grid;
 };
 
@@ -1242,6 +1298,7 @@ static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq, int64_t
     tps = std::min(tps, (kTableCache - 1) / blocks_per_tile);
   }
   p.tiles_per_split = tps;
+  p.max_tiles = max_tiles;
   p.n_splits = (max_tiles + tps - 1) / tps;
   p.n_work = units * p.n_splits;
   p.grid = (p.n_work + kXcds - 1) / kXcds * kXcds;
@@ -1306,6 +1363,20 @@ static void launch_bf16(const Plan &p, const AttnArgs &a, bool q4, hipStream_t s
   }
 }
 
+template <bool PAGED>
+static void launch_f32(const Plan &p, const AttnArgs &a, int T, hipStream_t stream) {
+  const bool small = f32_rows(T * a.G) == 8;
+  dim3 grid(p.grid);
+  if (a.kv.d == 64 && small)
+    hipLaunchKernelGGL((tree_attn_f32_kernel<64, 8, PAGED>), grid, dim3(256), 0, stream, a);
+  else if (a.kv.d == 64)
+    hipLaunchKernelGGL((tree_attn_f32_kernel<64, 32, PAGED>), grid, dim3(256), 0, stream, a);
+  else if (small)
+    hipLaunchKernelGGL((tree_attn_f32_kernel<128, 8, PAGED>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tree_attn_f32_kernel<128, 32, PAGED>), grid, dim3(256), 0, stream, a);
+}
+
 }  // namespace ev
 
 EV_API size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32_t T, int32_t Hq,
@@ -1352,6 +1423,7 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   a.Hq = Hq;
   a.G = Hq / kv->n_kv_heads;
   a.max_prefix = (int)std::min<int64_t>(max_prefix_len, 1 << 30);
+  a.max_tiles = p.max_tiles;
   a.scale_log2 = sm_scale * ev::kLog2e;
   a.row_blocks = p.row_blocks;
   a.tiles_per_split = p.tiles_per_split;
@@ -1368,16 +1440,10 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
     a.part_ls = (uint64_t *)(base + o_bytes);
   }
   if (kv->dtype == EV_F32) {
-    const bool small = ev::f32_rows(T * a.G) == 8;
-    dim3 grid(p.grid);
-    if (kv->head_dim == 64 && small)
-      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<64, 8>), grid, dim3(256), 0, stream, a);
-    else if (kv->head_dim == 64)
-      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<64, 32>), grid, dim3(256), 0, stream, a);
-    else if (small)
-      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<128, 8>), grid, dim3(256), 0, stream, a);
+    if (kv->paged)
+      ev::launch_f32<true>(p, a, T, stream);
     else
-      hipLaunchKernelGGL((ev::tree_attn_f32_kernel<128, 32>), grid, dim3(256), 0, stream, a);
+      ev::launch_f32<false>(p, a, T, stream);
   } else {
     const bool q4 = kv->dtype == EV_INT4;
     if (kv->head_dim == 64)
