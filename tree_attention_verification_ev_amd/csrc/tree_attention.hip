@@ -1068,14 +1068,18 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
   constexpr int NT = 256;
   constexpr int C4 = D / 4;                 // 16-byte pieces per row
   constexpr int LPT = kKT * C4 / NT;        // pieces per thread per K or V tile
-  constexpr int KP = D + 1;                 // K tile pitch: lane k reads row k, distinct banks
+  constexpr int KP = D + 4;                 // K tile pitch: 16-byte reads of row k by lane k
+                                            // cover all 64 banks across 16 lanes
   constexpr int RW = R / 4;                 // score rows per wavefront
   constexpr int RSTEP = NT / D;             // row stride of a thread's P V rows
   constexpr int RPT = R / RSTEP;            // P V rows per thread
   static_assert(R % 4 == 0 && R % RSTEP == 0, "row block must tile the workgroup");
+  // the 8-row block unrolls its LDS loops fully (all reads in flight together); the
+  // 32-row block would run out of registers doing so
+  constexpr int UNR = R == 8 ? (D == 64 ? 16 : 8) : 2;
   __shared__ __attribute__((aligned(16))) float sQ[R * D];
-  __shared__ float sK[kKT * KP];
-  __shared__ float sV[kKT * D];
+  __shared__ __attribute__((aligned(16))) float sK[kKT * KP];
+  __shared__ __attribute__((aligned(16))) float sV[kKT * D];
   __shared__ __attribute__((aligned(16))) float sP[R * kKT];
   __shared__ float sA[R], sM[R], sL[R];
 
@@ -1140,8 +1144,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int piece = tid + i * NT, key = piece / C4, c = piece % C4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sK[key * KP + 4 * c + e] = kr[i][e];
+      *(f32x4 *)(sK + key * KP + 4 * c) = kr[i];
       *(f32x4 *)(sV + key * D + 4 * c) = vr[i];
     }
   };
@@ -1164,14 +1167,14 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
     float s[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) s[i] = 0.f;
+    // rows past the block's last read row 0's query (broadcast) and are never used
+#pragma unroll UNR
     for (int d = 0; d < D; d += 4) {
-      const float k0 = sK[lane * KP + d], k1 = sK[lane * KP + d + 1];
-      const float k2 = sK[lane * KP + d + 2], k3 = sK[lane * KP + d + 3];
+      const f32x4 kv = *(const f32x4 *)(sK + lane * KP + d);
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
-        if (wave + 4 * i >= nrow) continue;
-        const f32x4 qv = *(const f32x4 *)(sQ + (wave + 4 * i) * D + d);
-        s[i] = fmaf(qv[0], k0, fmaf(qv[1], k1, fmaf(qv[2], k2, fmaf(qv[3], k3, s[i]))));
+        const f32x4 qv = *(const f32x4 *)(sQ + (wave + 4 * i < nrow ? wave + 4 * i : 0) * D + d);
+        s[i] = fmaf(qv[0], kv[0], fmaf(qv[1], kv[1], fmaf(qv[2], kv[2], fmaf(qv[3], kv[3], s[i]))));
       }
     }
 #pragma unroll
@@ -1189,19 +1192,22 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
       if (lane == 0) sA[r] = alpha;
     }
     lds_barrier();
+    // keys in the outer loop: each V element read once feeds all of the thread's rows
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int r = prow + RSTEP * j;
-      if (r >= nrow) continue;
-      float acc = o[j] * sA[r];
-      for (int k = 0; k < kKT; k += 4) {
-        const f32x4 pv = *(const f32x4 *)(sP + r * kKT + k);
-        acc = fmaf(pv[0], sV[k * D + dim], acc);
-        acc = fmaf(pv[1], sV[(k + 1) * D + dim], acc);
-        acc = fmaf(pv[2], sV[(k + 2) * D + dim], acc);
-        acc = fmaf(pv[3], sV[(k + 3) * D + dim], acc);
+      o[j] *= r < nrow ? sA[r] : 1.f;
+    }
+#pragma unroll UNR
+    for (int k = 0; k < kKT; k += 4) {
+      const float v0 = sV[k * D + dim], v1 = sV[(k + 1) * D + dim];
+      const float v2 = sV[(k + 2) * D + dim], v3 = sV[(k + 3) * D + dim];
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        const int r = prow + RSTEP * j;
+        const f32x4 pv = *(const f32x4 *)(sP + (r < nrow ? r : 0) * kKT + k);
+        o[j] = fmaf(pv[0], v0, fmaf(pv[1], v1, fmaf(pv[2], v2, fmaf(pv[3], v3, o[j]))));
       }
-      o[j] = acc;
     }
   }
   if (__any(bad) && lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
