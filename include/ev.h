@@ -53,6 +53,7 @@ enum {
   EV_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the *_workspace() query */
   EV_ERR_ARG = 5,         /* invalid scalar (temperature, softmax scale) or misaligned array */
   EV_ERR_LAUNCH = 6,      /* a kernel launch failed */
+  EV_ERR_SCRATCH = 7,     /* the call does not fit the fixed scratch of a no-allocation entry point */
   /* device-side codes, stored into *dev_status */
   EV_DERR_PARENT = 101,   /* parent[] is not a topological tree rooted at node 0 */
   EV_DERR_BOUNDS = 102,   /* prefix + tree does not fit the cache, or a block id is out of range */
@@ -135,6 +136,25 @@ ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const int32_t *
                             const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
                             int64_t max_prefix_len, float sm_scale, void *out, float *lse,
                             void *ws, size_t ws_bytes, int32_t *dev_status, hipStream_t stream);
+
+/* ev_tree_attention_noalloc — ev_tree_attention for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as ev_tree_attention, without ws and
+ * ws_bytes: the split partials go to a fixed array of ev_tree_attention_noalloc_limit()
+ * bytes (32 MiB) that the library holds on each GPU it runs on until the process ends.
+ * The call allocates nothing; it runs on the current device (pass a stream of that
+ * device).  A call whose plan needs more than the array returns EV_ERR_SCRATCH before
+ * launching (the Llama-3-70B-shaped layer needs 14 MB; a paged batch with one split per
+ * work unit needs none).  Every call on a GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (other streams, other host threads) race and must be serialised by
+ * the caller. */
+ev_status ev_tree_attention_noalloc(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
+                                    const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
+                                    int64_t max_prefix_len, float sm_scale, void *out, float *lse,
+                                    int32_t *dev_status, hipStream_t stream);
+
+/* (host) Bytes of the fixed scratch array ev_tree_attention_noalloc uses. */
+size_t ev_tree_attention_noalloc_limit(void);
 
 /* Bytes of workspace the acceptance calls need (B * T <= 65535, V <= 262144).
  * The acceptance workspace holds arrival counters: zero-fill it (for example with

@@ -25,11 +25,13 @@ EV_OK = 0
 EV_F32, EV_BF16, EV_INT4 = 0, 1, 2
 STATUS_NAMES = {
     0: "EV_OK", 1: "EV_ERR_NULL", 2: "EV_ERR_SHAPE", 3: "EV_ERR_DTYPE", 4: "EV_ERR_WORKSPACE",
-    5: "EV_ERR_ARG", 6: "EV_ERR_LAUNCH", 101: "EV_DERR_PARENT", 102: "EV_DERR_BOUNDS",
+    5: "EV_ERR_ARG", 6: "EV_ERR_LAUNCH", 7: "EV_ERR_SCRATCH", 101: "EV_DERR_PARENT",
+    102: "EV_DERR_BOUNDS",
     103: "EV_DERR_TOKEN", 104: "EV_DERR_PATH", 105: "EV_DERR_WIDTH",
 }
 EXPORTED = (
     "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
+    "ev_tree_attention_noalloc", "ev_tree_attention_noalloc_limit",
     "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection",
     "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact",
     "ev_kv_compact_remap_workspace", "ev_kv_compact_remap",
@@ -75,6 +77,9 @@ def lib() -> ctypes.CDLL:
             "ev_tree_attention_workspace": (_SZ, [kv, _I32, _I32, _I32, _I64]),
             "ev_tree_attention": (_I32, [_P, kv, _P, _P, _I32, _I32, _I32, _I64, _F32, _P, _P, _P,
                                          _SZ, _P, _P]),
+            "ev_tree_attention_noalloc": (_I32, [_P, kv, _P, _P, _I32, _I32, _I32, _I64, _F32, _P,
+                                                 _P, _P, _P]),
+            "ev_tree_attention_noalloc_limit": (_SZ, []),
             "ev_accept_workspace": (_SZ, [_I32, _I32, _I32]),
             "ev_accept_greedy": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_rejection": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _P,
@@ -262,6 +267,36 @@ def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, an
                                    _ptr(status), _stream(dev))
     _finish(code, "ev_tree_attention", status, check)
     return out, lse
+
+
+def ev_tree_attention_noalloc(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor,
+                              anc_mask: torch.Tensor, sm_scale: Optional[float] = None,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                              dev_status: Optional[torch.Tensor] = None, check: bool = False,
+                              max_prefix_len: Optional[int] = None):
+    """ev_tree_attention through the entry point that allocates nothing (its split partials
+    live in the library's fixed per-GPU array).  Pass out, lse and dev_status to make the
+    call itself allocation-free; otherwise they are allocated here."""
+    _dev(q, "q", torch.bfloat16 if kv.dtype == torch.uint8 else kv.dtype)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(anc_mask, "anc_mask", torch.int64)
+    B, T, Hq, d = q.shape
+    dev = q.device
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    mpl = max(0, kv.capacity - T) if max_prefix_len is None else int(max_prefix_len)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    status = _status_word(dev, dev_status)
+    code = lib().ev_tree_attention_noalloc(_ptr(q), kv.ref(), _ptr(prefix_len), _ptr(anc_mask), B, T,
+                                           Hq, mpl, float(sm_scale), _ptr(out), _ptr(lse),
+                                           _ptr(status), _stream(dev))
+    _finish(code, "ev_tree_attention_noalloc", status, check)
+    return out, lse
+
+
+def ev_tree_attention_noalloc_limit() -> int:
+    return int(lib().ev_tree_attention_noalloc_limit())
 
 
 def ev_accept_workspace(B: int, T: int, V: int) -> int:

@@ -42,6 +42,7 @@
 
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <type_traits>
 
 namespace ev {
@@ -1395,11 +1396,15 @@ EV_API size_t ev_tree_attention_workspace(const ev_kv_desc *kv, int32_t B, int32
   return ev::workspace_bytes(p, B, T, Hq, kv->head_dim);
 }
 
-EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
-                                   const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
-                                   int64_t max_prefix_len, float sm_scale, void *out, float *lse,
-                                   void *ws, size_t ws_bytes, int32_t *dev_status,
-                                   hipStream_t stream) {
+namespace ev {
+
+// ev_tree_attention's work with the workspace given; scratch_call: the workspace is the
+// fixed scratch array, so a plan that needs more than ws_bytes is EV_ERR_SCRATCH.
+static ev_status attention_call(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
+                                const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
+                                int64_t max_prefix_len, float sm_scale, void *out, float *lse,
+                                void *ws, size_t ws_bytes, int32_t *dev_status,
+                                hipStream_t stream, bool scratch_call) {
   ev::KvAddr addr;
   ev_status st = ev::make_kv_addr(kv, &addr);
   if (st != EV_OK) return st;
@@ -1413,7 +1418,7 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   if ((int64_t)B * kv->n_kv_heads > (1 << 24)) return EV_ERR_SHAPE;
   ev::Plan p = ev::make_plan(addr, kv->dtype, B, T, Hq, max_prefix_len);
   size_t need = ev::workspace_bytes(p, B, T, Hq, kv->head_dim);
-  if (ws_bytes < need || (need && !ws)) return EV_ERR_WORKSPACE;
+  if (ws_bytes < need || (need && !ws)) return scratch_call ? EV_ERR_SCRATCH : EV_ERR_WORKSPACE;
 
   ev::AttnArgs a{};
   a.q = q;
@@ -1459,3 +1464,56 @@ EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const in
   }
   return ev::launch_status();
 }
+
+// Workspace of the no-allocation entry point: one fixed array per GPU, holding the split
+// partials of the call in progress.  In host code its name stands for no device address;
+// the address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kScratchDevices];
+
+}  // namespace ev
+
+static __device__ __align__(256) unsigned char scratch[ev::kScratchBytes];
+
+namespace ev {
+// Device address of this GPU's scratch array (the current device's), looked up on the
+// first call on that device.
+static ev_status scratch_pointer(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return EV_ERR_SCRATCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return EV_ERR_SCRATCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return EV_OK;
+}
+}  // namespace ev
+
+EV_API ev_status ev_tree_attention(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
+                                   const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
+                                   int64_t max_prefix_len, float sm_scale, void *out, float *lse,
+                                   void *ws, size_t ws_bytes, int32_t *dev_status,
+                                   hipStream_t stream) {
+  return ev::attention_call(q, kv, prefix_len, anc_mask, B, T, Hq, max_prefix_len, sm_scale, out,
+                            lse, ws, ws_bytes, dev_status, stream, false);
+}
+
+EV_API ev_status ev_tree_attention_noalloc(const void *q, const ev_kv_desc *kv,
+                                           const int32_t *prefix_len, const uint64_t *anc_mask,
+                                           int32_t B, int32_t T, int32_t Hq,
+                                           int64_t max_prefix_len, float sm_scale, void *out,
+                                           float *lse, int32_t *dev_status, hipStream_t stream) {
+  void *ws = nullptr;
+  const ev_status st = ev::scratch_pointer(&ws);
+  if (st != EV_OK) return st;
+  return ev::attention_call(q, kv, prefix_len, anc_mask, B, T, Hq, max_prefix_len, sm_scale, out,
+                            lse, ws, ev::kScratchBytes, dev_status, stream, true);
+}
+
+EV_API size_t ev_tree_attention_noalloc_limit(void) { return ev::kScratchBytes; }
+
