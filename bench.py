@@ -39,7 +39,6 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 FOOTPRINT_BYTES = 512 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attention_llama3_70b_layer_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "tree_attention_verification_ev_amd", "csrc", "tree_attention.hip")
 
 
@@ -215,47 +214,66 @@ def _counter_values(csv_path, counter):
     return acc
 
 
-def write_traffic(fetch_csv, write_csv, command):
-    """HBM bytes per attention call (main + split merge kernels) from two rocprofv3 --pmc
-    runs of `bench.py --calibrate`, each counter scaled by what it reads for the 256 MiB
-    device copy of the same run."""
+TRAFFIC_PARTS = {
+    # part: (kernel-name keys, source file, record file stem)
+    "attention": (("tree_attn_", "attn_merge_kernel"), ATTN_SRC, "tree_attention"),
+    "accept": (("accept_kernel",), os.path.join(ROOT, "tree_attention_verification_ev_amd", "csrc",
+                                                "accept.hip"), "accept"),
+}
+
+
+def traffic_path(part, workload):
+    return os.path.join(ROOT, "profiles", f"{TRAFFIC_PARTS[part][2]}_{workload}_traffic.json")
+
+
+def write_traffic(fetch_csv, write_csv, command, part="attention", workload="llama3_70b_layer"):
+    """HBM bytes per call of one part of the step (attention: main + split merge kernels;
+    accept: the acceptance kernel) from two rocprofv3 --pmc runs of `bench.py --calibrate`,
+    each counter scaled by what it reads for the 256 MiB device copy of the same run."""
     fetch, write = _counter_values(fetch_csv, "FETCH_SIZE"), _counter_values(write_csv, "WRITE_SIZE")
     copy_kib = (256 << 20) / 1024
+    keys, src, _ = TRAFFIC_PARTS[part]
 
     def pick(table, key):
         hits = [(k, v) for k, v in table.items() if key in k]
-        if not hits:
-            raise SystemExit(f"no kernel matching {key!r} in the counter file")
-        return max(hits, key=lambda kv: len(kv[1]))
+        return max(hits, key=lambda kv: len(kv[1])) if hits else None
 
     # the calibration copy is the largest device copy of the run
     cal_f = copy_kib / max(max(v) for k, v in fetch.items() if "copyBuffer" in k)
     cal_w = copy_kib / max(max(v) for k, v in write.items() if "copyBuffer" in k)
     kernels = {}
     total = 0.0
-    for key in ("tree_attn_", "attn_merge_kernel"):
-        kf, vf = pick(fetch, key)
-        kw, vw = pick(write, key)
+    for key in keys:
+        pf, pw = pick(fetch, key), pick(write, key)
+        if pf is None or pw is None:
+            continue                     # e.g. no split merge at a one-split plan
+        (kf, vf), (kw, vw) = pf, pw
         f_kib, nf, w_kib, nw = statistics.fmean(vf), len(vf), statistics.fmean(vw), len(vw)
         b = f_kib * 1024 * cal_f + w_kib * 1024 * cal_w
         kernels[kf] = {"fetch_kib": f_kib, "write_kib": w_kib, "dispatches": [nf, nw],
                        "hbm_bytes": b}
         total += b
-    with open(ATTN_SRC, "rb") as f:
+    if not kernels:
+        raise SystemExit(f"no kernel matching {keys} in the counter files")
+    with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    rec = {"workload": "llama3_70b_layer", "hbm_bytes_per_launch": total,
+    inp = generate(config_by_name(workload), with_kv=False, with_logits=False)
+    work = algorithmic_work(inp)
+    algo = work["bytes"] if part == "attention" else work["logit_bytes"]
+    rec = {"workload": workload, "part": part, "hbm_bytes_per_launch": total,
+           "algorithmic_bytes": algo, "ratio_to_algorithmic": total / algo,
            "fetch_calibration": cal_f, "write_calibration": cal_w, "kernels": kernels,
            "source_sha256": sha, "command": command}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_path(part, workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
 
-def traffic_entry():
-    """HBM bytes per attention launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source."""
+def traffic_entry(workload):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs of this
+    workload, if they were taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_path("attention", workload)) as f:
             t = json.load(f)
         with open(ATTN_SRC, "rb") as f:
             h = hashlib.sha256(f.read()).hexdigest()
@@ -763,9 +781,13 @@ def main():
                     help="write the attention traffic record from two rocprofv3 --pmc "
                          "counter files (FETCH_SIZE, WRITE_SIZE) and exit (no GPU needed)")
     ap.add_argument("--traffic-command", default="", help="command recorded with --traffic-from")
+    ap.add_argument("--traffic-part", default="attention", choices=tuple(TRAFFIC_PARTS),
+                    help="which part of the step the --traffic-from record covers")
+    ap.add_argument("--no-box-peaks", action="store_true",
+                    help="skip the calibration kernels (counter runs)")
     args = ap.parse_args()
     if args.traffic_from:
-        write_traffic(*args.traffic_from, args.traffic_command)
+        write_traffic(*args.traffic_from, args.traffic_command, args.traffic_part, args.config)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -855,7 +877,7 @@ def main():
     if not args.no_configs:
         for c in CONFIGS:
             configs[c.name] = this if c.name == cfg.name else config_entry(c, 5)
-    box = box_peaks()
+    box = None if args.no_box_peaks else box_peaks()
     result = {
         "metric": METRIC,
         "value": nodes / (ms_per_step * 1e-3),
@@ -868,14 +890,14 @@ def main():
                    "L": cfg.L, "T": cfg.T, "V": cfg.V, "kv_layout": inp.layout,
                    "acceptance": mode, "tau": cfg.tau, "buffer_sets": n_sets},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": traffic_entry(),
+                     "frac": achieved / peak, "traffic": traffic_entry(cfg.name),
                      "kernel": "ev_tree_attention", "algorithmic_flops": work["flops"],
                      "algorithmic_bytes": work["bytes"],
-                     "frac_of_box_peak": achieved / (box["mfma_bf16_tflops"] if bound == "mfma"
-                                                     else peak)},
+                     "frac_of_box_peak": (achieved / (box["mfma_bf16_tflops"] if bound == "mfma"
+                                                      else peak)) if box else None},
         "kv_hbm_gbps": kv_gbps,
         "kv_hbm_frac": kv_gbps / PEAK_HBM_GBPS,
-        "kv_hbm_frac_of_box_read": kv_gbps / box["read_gbps"],
+        "kv_hbm_frac_of_box_read": kv_gbps / box["read_gbps"] if box else None,
         "box_peaks": box,
         "attention_nodes_per_s": nodes / t_attn,
         "kernels_us": {k: round(v["mean_us"], 3) for k, v in kt.items()},

@@ -11,7 +11,7 @@ SeedSequence(1000 + config index), so that changing one component never shifts a
   stream 5  V                     N(0, 1)
   stream 6  logits                N(0, sigma = 2), float32
   stream 7  draft tokens          uniform ids, distinct among siblings
-  stream 8  planting              per internal node: keep-coin (p = 0.8) and target prob pi ~ U[0.5, 0.95]
+  stream 8  planting              per internal node: keep-coin (p = 0.85) and target prob pi ~ U[0.8, 0.97]
   stream 9  uniforms              float64 U[0, 1), one per node
 
 bf16 workloads round Q/K/V to bf16 (round to nearest even) and keep them as float32
@@ -38,8 +38,8 @@ import numpy as np
 from .configs import Config
 
 N_STREAMS = 10
-_PLANT_ALPHA = 0.8
-_PLANT_PI = (0.5, 0.95)
+_PLANT_ALPHA = 0.85
+_PLANT_PI = (0.8, 0.97)
 _LOGIT_SIGMA = 2.0
 _PLANT_TAU = 0.7
 
