@@ -115,6 +115,9 @@ ATTN_SMALL = [
     # 16 x 8 x 2 = 256 work units: one split, the register-staged kernel's unsplit output
     ("bf16_d64_one_split", scaled(C4, d=64, L=(100, 900), V=64)),
     ("f32_d128", scaled(C1, d=128, L=190, Hq=8, Hkv=2, V=64)),
+    # float32 blocks of 8 rows (eight wavefronts): d = 128, and paged d = 64
+    ("f32_d128_8rows", scaled(C1, d=128, L=150, V=64)),
+    ("f32_paged_8rows", scaled(C1, paged=True, L=(70, 200), B=3, V=64)),
     # float32 over a shuffled block table, 64 rows per KV head (two row blocks of 32)
     ("f32_paged_gqa", scaled(C4, dtype="f32", B=2, T=16, Hq=32, Hkv=8, L=(60, 300), V=64)),
     ("gqa4_T26", scaled(C2, Hq=32, Hkv=8, L=515, V=64)),

@@ -1051,10 +1051,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (c == 0) a.lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
-// float32 path: one 256-thread workgroup per (sequence, KV head, block of R query rows).
+// float32 path: one workgroup per (sequence, KV head, block of R query rows): 8 wavefronts
+// for a block of 8 rows (one row each), 4 for a block of 32.
 // 64-key K and V tiles reach LDS through coalesced 16-byte loads, the next tile's loads in
 // flight in registers while the current one is computed.  Scores: lane k of wavefront w
-// scores key k against rows w, w + 4, ... (query rows are broadcast reads), so a row's 64
+// scores key k against rows w, w + NWV, ... (query rows are broadcast reads), so a row's 64
 // scores lie across one wavefront and its max and sum are wavefront (DPP) reductions.  P V:
 // thread t owns head dimension t % D of rows t / D, t / D + 256 / D, ...
 // Workgroup barrier for LDS data only: the wave's LDS accesses complete, then s_barrier.
@@ -1064,20 +1065,22 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D, int R, bool PAGED>
-__global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
-  constexpr int NT = 256;
+template <int D, int R, bool PAGED, int NT>
+__global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
+  constexpr int NWV = NT / 64;              // wavefronts
   constexpr int C4 = D / 4;                 // 16-byte pieces per row
   constexpr int LPT = kKT * C4 / NT;        // pieces per thread per K or V tile
   constexpr int KP = D + 4;                 // K tile pitch: 16-byte reads of row k by lane k
                                             // cover all 64 banks across 16 lanes
-  constexpr int RW = R / 4;                 // score rows per wavefront
+  constexpr int RW = R / NWV;               // score rows per wavefront
   constexpr int RSTEP = NT / D;             // row stride of a thread's P V rows
   constexpr int RPT = R / RSTEP;            // P V rows per thread
-  static_assert(R % 4 == 0 && R % RSTEP == 0, "row block must tile the workgroup");
-  // the 8-row block unrolls its LDS loops fully (all reads in flight together); the
-  // 32-row block would run out of registers doing so
-  constexpr int UNR = R == 8 ? (D == 64 ? 16 : 8) : 2;
+  static_assert(R % NWV == 0 && R % RSTEP == 0, "row block must tile the workgroup");
+  // the 8-row block unrolls its LDS loops fully (all reads in flight together, and its
+  // register-held query rows indexed by constants); the 32-row block would run out of
+  // registers doing so
+  constexpr bool QREG = RW * D <= 128 && D == 64;   // query rows held in registers
+  constexpr int UNR = QREG ? D / 4 : (R == 8 ? 8 : 2);
   __shared__ __attribute__((aligned(16))) float sQ[R * D];
   __shared__ __attribute__((aligned(16))) float sK[kKT * KP];
   __shared__ __attribute__((aligned(16))) float sV[kKT * D];
@@ -1115,38 +1118,38 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
   uint64_t anc[RW];
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    const int r = wave + 4 * i;
+    const int r = wave + NWV * i;
     anc[i] = r < nrow ? a.anc[(int64_t)b * a.T + (row0 + r) / a.G] : 0ull;
   }
 
+  // Every piece is loaded unconditionally from an in-bounds address (a slot past the
+  // sequence reloads its last slot; a bad block id reads the cache's first row) and
+  // masked only when stored: a load under a per-lane branch made the compiler wait for it
+  // at once.
   f32x4 kr[LPT], vr[LPT];
   bool bad = false;
+  int key0_loaded = 0;
   auto load = [&](int key0) {
+    key0_loaded = key0;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int piece = tid + i * NT, key = piece / C4, c = piece % C4;
-      const int slot = key0 + key;
-      f32x4 xk = {}, xv = {};
-      if (slot < nkeys) {
-        const int64_t off = PAGED ? a.kv.slot_offset(b, g, slot)
-                                  : ((int64_t)(b * a.kv.hkv + g) * a.kv.cap + slot) * D;
-        if (off >= 0) {
-          xk = *(const f32x4 *)(K + off + 4 * c);
-          xv = *(const f32x4 *)(V + off + 4 * c);
-        } else {
-          bad = true;
-        }
-      }
-      kr[i] = xk;
-      vr[i] = xv;
+      const int slot = min(key0 + key, nkeys - 1);
+      int64_t off = PAGED ? a.kv.slot_offset(b, g, slot)
+                          : ((int64_t)(b * a.kv.hkv + g) * a.kv.cap + slot) * D;
+      bad |= off < 0;
+      off = off < 0 ? 0 : off;
+      kr[i] = *(const f32x4 *)(K + off + 4 * c);
+      vr[i] = *(const f32x4 *)(V + off + 4 * c);
     }
   };
   auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int piece = tid + i * NT, key = piece / C4, c = piece % C4;
-      *(f32x4 *)(sK + key * KP + 4 * c) = kr[i];
-      *(f32x4 *)(sV + key * D + 4 * c) = vr[i];
+      const bool live = key0_loaded + key < nkeys;
+      *(f32x4 *)(sK + key * KP + 4 * c) = live ? kr[i] : f32x4{};
+      *(f32x4 *)(sV + key * D + 4 * c) = live ? vr[i] : f32x4{};
     }
   };
 
@@ -1157,8 +1160,20 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
   for (int j = 0; j < RPT; ++j) o[j] = 0.f;
   const int dim = tid % D, prow = tid / D;
 
+  // With at most two rows of 64 dimensions per wavefront the query rows are held in
+  // registers (up to 128 per lane) instead of being re-read from LDS for every key tile:
+  // a broadcast read still moves 1 KB through the LDS per instruction.
+  f32x4 qr[QREG ? RW : 1][QREG ? D / 4 : 1];
   const int ntiles = (nkeys + kKT - 1) / kKT;
   load(0);
+  if constexpr (QREG) {
+    lds_barrier();                          // the query rows are in LDS
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c)
+        qr[i][c] = *(const f32x4 *)(sQ + (wave + NWV * i < nrow ? wave + NWV * i : 0) * D + 4 * c);
+  }
   for (int t = 0; t < ntiles; ++t) {
     lds_barrier();                          // the previous tile's P V is done with sK/sV/sP
     store();
@@ -1174,13 +1189,14 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
       const f32x4 kv = *(const f32x4 *)(sK + lane * KP + d);
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
-        const f32x4 qv = *(const f32x4 *)(sQ + (wave + 4 * i < nrow ? wave + 4 * i : 0) * D + d);
+        const f32x4 qv = QREG ? qr[i][d / 4]
+                              : *(const f32x4 *)(sQ + (wave + NWV * i < nrow ? wave + NWV * i : 0) * D + d);
         s[i] = fmaf(qv[0], kv[0], fmaf(qv[1], kv[1], fmaf(qv[2], kv[2], fmaf(qv[3], kv[3], s[i]))));
       }
     }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const int r = wave + 4 * i;
+      const int r = wave + NWV * i;
       if (r >= nrow) continue;             // uniform across the wavefront
       const bool ok = slot < nkeys && visible(slot, L, anc[i]);
       const float x = ok ? s[i] * a.scale_log2 : -INFINITY;
@@ -1214,7 +1230,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
   if (__any(bad) && lane == 0) report(a.dev_status, EV_DERR_BOUNDS);
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    const int r = wave + 4 * i;
+    const int r = wave + NWV * i;
     if (r < nrow && lane == 0) {
       sM[r] = m[i];
       sL[r] = l[i];
@@ -1375,13 +1391,13 @@ static void launch_f32(const Plan &p, const AttnArgs &a, int T, hipStream_t stre
   const bool small = f32_rows(T * a.G) == 8;
   dim3 grid(p.grid);
   if (a.kv.d == 64 && small)
-    hipLaunchKernelGGL((tree_attn_f32_kernel<64, 8, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_f32_kernel<64, 8, PAGED, 512>), grid, dim3(512), 0, stream, a);
   else if (a.kv.d == 64)
-    hipLaunchKernelGGL((tree_attn_f32_kernel<64, 32, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_f32_kernel<64, 32, PAGED, 256>), grid, dim3(256), 0, stream, a);
   else if (small)
-    hipLaunchKernelGGL((tree_attn_f32_kernel<128, 8, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_f32_kernel<128, 8, PAGED, 512>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((tree_attn_f32_kernel<128, 32, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((tree_attn_f32_kernel<128, 32, PAGED, 256>), grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace ev
