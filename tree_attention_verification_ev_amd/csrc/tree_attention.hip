@@ -670,10 +670,12 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
   }
 }
 
-// Direct-to-LDS tree attention kernel, head_dim 128.  NW wavefronts of 32 query rows each;
-// KSPLIT (at most 32 rows per KV head, NW = 2): both wavefronts take the same 32 rows and
-// each scores and accumulates one 32-key half of every tile, the halves combined through
-// LDS at the end.
+// Direct-to-LDS tree attention kernel, head_dim 128.  Without KSPLIT: NW wavefronts of 32
+// query rows each.  KSPLIT: NW / 2 groups of 32 rows, two wavefronts per group (one per
+// 32-key half of every tile, so each scores and accumulates half the keys), the halves
+// combined through LDS at the end; with NW = 2 it serves heads of at most 32 rows, with
+// NW = 8 it halves the rows per workgroup of short split plans (more row blocks, fewer
+// splits, fewer partial rows).
 template <int NW, bool PAGED, bool KSPLIT>
 __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int D = 128;
@@ -684,7 +686,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int IPW = kKT * DCH / 64 / NW;       // DMA instructions per wave per matrix
   constexpr int PER = 2 * IPW;                   // per wave per tile
   static_assert(IPW >= 1 && 2 * PER <= 63, "vmcnt range");
-  static_assert(!KSPLIT || NW == 2, "key-split workgroups have two wavefronts");
+  static_assert(!KSPLIT || NW == 2 || NW == 8, "key-split workgroups have two or eight wavefronts");
+  constexpr int RG = KSPLIT ? NW / 2 : NW;       // groups of 32 query rows per workgroup
   constexpr int NT = NW * 64;
   // kStages K|V tile pairs, then the sequence's ancestor masks (64 x 8 bytes)
   __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT + kMaxNodes * 4];
@@ -703,8 +706,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int qn = lane & 31;
   const int hh = lane >> 5;
   const int rows = a.T * a.G;
-  const int row0 = KSPLIT ? rb * 32 : (rb * NW + wave) * 32;
-  const int st0 = KSPLIT ? wave : 0;             // first 32-key subtile of this wave
+  const int rg = wave % RG;                      // this wave's row group
+  const int kh = wave / RG;                      // KSPLIT: this wave's half of each tile
+  const int row0 = (rb * RG + rg) * 32;
+  const int st0 = KSPLIT ? kh : 0;               // first 32-key subtile of this wave
 
   const __bf16 *Q = (const __bf16 *)a.q;
   const __bf16 *K = (const __bf16 *)a.k;
@@ -731,11 +736,15 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // tile is issued); the Q^T fragments are then read from there.  Fetched as ordinary
   // loads they would be scattered 16-byte gathers queued ahead of the K/V traffic, and
   // the compiler would drain every DMA in flight before their first use.  Rows past the
-  // last one repeat it: their results are never written.
-  __bf16 *qlds = lds + 2 * 2 * MAT + wave * 32 * D;
+  // last one repeat it: their results are never written.  The two wavefronts of a
+  // key-split group fetch 16 of the group's rows each.
+  __bf16 *qlds = lds + 2 * 2 * MAT + rg * 32 * D;
   auto issue_q = [&]() {
+    constexpr int NQ = 32 * DCH / 64;            // DMA instructions for 32 whole rows
+    constexpr int QI = KSPLIT ? NQ / 2 : NQ;
 #pragma unroll
-    for (int i = 0; i < 32 * DCH / 64; ++i) {
+    for (int ii = 0; ii < QI; ++ii) {
+      const int i = KSPLIT ? kh * QI + ii : ii;
       const int rr = 4 * i + (lane >> 4), pc = lane & 15;
       const int r = min(row0 + rr, rows - 1);
       const int node = r / a.G, head = g * a.G + r % a.G;
@@ -799,7 +808,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int t_end = min(t_begin + a.tiles_per_split, ntiles);
   if (t_begin >= t_end) {
     // an empty split (a shorter sequence of the batch): its partial carries no weight
-    if (a.n_splits > 1 && hh == 0 && row0 + qn < rows && (!KSPLIT || wave == 0))
+    if (a.n_splits > 1 && hh == 0 && row0 + qn < rows && kh == 0)
       a.part_ls[part_row(a, out_row(a, b, g, row0 + qn), split)] = pack_ls(-INFINITY, 1.f);
     wait_vm<0>();
     return;
@@ -939,6 +948,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   }
   if (n_early == 2) wait_vm<2 * PER>();          // masks and Q landed (this wave's own rows)
   else wait_vm<PER>();
+  if constexpr (KSPLIT) wg_barrier();            // and the other half of the group's rows
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qf[0][ks] = *(const bf16x8 *)(qlds + qn * D + ((((2 * ks) | hh) ^ (qn & 15)) << 3));
@@ -963,10 +973,18 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // flight.  Those two stages hold the waves' output rows (8 KB each).
   const int last = (t_end - 1 - t_begin) % kStages;
   if constexpr (KSPLIT) {
-    // wave 1 hands its half (reference max, partial sum, accumulators) to wave 0 through
-    // the second free stage, element-major so the accesses are conflict-free
-    float *xch = (float *)(lds + ((last + 2) % kStages) * 2 * MAT);
-    if (wave == 1) {
+    // the second wave of each group hands its half (reference max, partial sum,
+    // accumulators) to the first, element-major so the accesses are conflict-free: with
+    // one group through the second free stage, with four (66 KB) through stages 0-2 once
+    // every wave is past its last tile
+    float *xch;
+    if constexpr (NW == 2) {
+      xch = (float *)(lds + ((last + 2) % kStages) * 2 * MAT);
+    } else {
+      __syncthreads();
+      xch = (float *)lds + rg * (2 + DT * 16) * 64;
+    }
+    if (kh == 1) {
       xch[lane] = mref[0];
       xch[64 + lane] = l[0];
 #pragma unroll
@@ -975,7 +993,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) xch[(2 + dt * 16 + i) * 64 + lane] = o[0][dt][i];
     }
     __syncthreads();
-    if (wave == 1) return;
+    if (kh == 1) return;
     const float m1 = xch[lane], l1 = xch[64 + lane];
     const float mnew = fmaxf(mref[0], m1);
     const float a0 = mref[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[0] - mnew);
@@ -987,8 +1005,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) o[0][dt][i] = o[0][dt][i] * a0 + xch[(2 + dt * 16 + i) * 64 + lane] * a1;
     mref[0] = mnew;
   }
-  uint16_t *stage = (uint16_t *)(lds + ((last + 1 + (wave >> 2)) % kStages) * 2 * MAT +
-                                 (wave & 3) * 32 * D);
+  uint16_t *stage = KSPLIT && NW == 8
+                        ? (uint16_t *)(lds + 3 * 2 * MAT + rg * 32 * D)   // past the exchange
+                        : (uint16_t *)(lds + ((last + 1 + (wave >> 2)) % kStages) * 2 * MAT +
+                                       (wave & 3) * 32 * D);
   write_rows_staged<D>(a, o, mref[0], l[0], row0, b, g, split, qn, hh, stage);
 }
 
@@ -1250,11 +1270,12 @@ __global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------------------
 // Launch policy.
 constexpr int kCUs = 256;
+constexpr int kShortSplit = 16;   // tiles per split up to which GQA plans halve their row blocks
 
 struct Plan {
   int nw;                // waves per workgroup
   bool dma;              // bf16 d = 128: the direct-to-LDS kernel
-  bool ksplit;           // DMA kernel with <= 32 rows per KV head: waves split each tile's keys
+  bool ksplit;           // DMA kernel whose wave pairs split each tile's keys
   int row_blocks;
   int tiles_per_split, n_splits;
   int max_tiles;         // 64-key tiles of the planned key range
@@ -1308,22 +1329,34 @@ static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq, int64_t
   if (dma) p.nw = std::max(p.nw, 2);
   p.dma = dma;
   p.ksplit = dma && waves_needed == 1;
-  p.row_blocks = (waves_needed + p.nw - 1) / p.nw;
   const int max_tiles = (plan_slots(kv, T, max_prefix_len) + kKT - 1) / kKT;
-  const int units = B * kv.hkv * p.row_blocks;
   const int slots = dma || p.nw >= 4 ? kCUs : (p.nw == 2 ? 2 * kCUs : 4 * kCUs);
-  int splits = std::max(1, slots / units);
-  splits = std::min(splits, std::min(kMaxSplits, max_tiles));
-  int tps = (max_tiles + splits - 1) / splits;
-  if (kv.paged) {
-    // a split's block ids must fit the LDS cache
-    const int blocks_per_tile = std::max(1, kKT >> kv.block_shift);
-    tps = std::min(tps, (kTableCache - 1) / blocks_per_tile);
+  // split the planned key range over enough workgroups to fill `slots`
+  auto split_plan = [&](int groups_per_wg) {
+    p.row_blocks = (waves_needed + groups_per_wg - 1) / groups_per_wg;
+    const int units = B * kv.hkv * p.row_blocks;
+    int splits = std::max(1, slots / units);
+    splits = std::min(splits, std::min(kMaxSplits, max_tiles));
+    int tps = (max_tiles + splits - 1) / splits;
+    if (kv.paged) {
+      // a split's block ids must fit the LDS cache
+      const int blocks_per_tile = std::max(1, kKT >> kv.block_shift);
+      tps = std::min(tps, (kTableCache - 1) / blocks_per_tile);
+    }
+    p.tiles_per_split = tps;
+    p.n_splits = (max_tiles + tps - 1) / tps;
+    p.n_work = units * p.n_splits;
+  };
+  split_plan(p.ksplit ? 1 : p.nw);
+  // Short split loops (a few tiles per workgroup, the partials a large part of the
+  // traffic): eight-wave workgroups take 128 rows instead of 256, their wave pairs
+  // splitting every tile's keys, when that still fits one round of workgroups.
+  if (dma && p.nw == 8 && p.n_splits > 1 && p.tiles_per_split <= kShortSplit &&
+      (int64_t)B * kv.hkv * ((waves_needed + 3) / 4) <= kCUs) {
+    p.ksplit = true;
+    split_plan(4);
   }
-  p.tiles_per_split = tps;
   p.max_tiles = max_tiles;
-  p.n_splits = (max_tiles + tps - 1) / tps;
-  p.n_work = units * p.n_splits;
   p.grid = (p.n_work + kXcds - 1) / kXcds * kXcds;
   return p;
 }
@@ -1344,7 +1377,9 @@ static void launch_main(const Plan &p, const AttnArgs &a, hipStream_t stream) {
   dim3 grid(p.grid);
   if constexpr (!Q4 && D == 128) {
     // bf16 with d = 128: the direct-to-LDS kernel (the plan gives it at least 2 waves)
-    if (p.nw == 8)
+    if (p.nw == 8 && p.ksplit)
+      hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED, true>), grid, dim3(512), 0, stream, a);
+    else if (p.nw == 8)
       hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED, false>), grid, dim3(512), 0, stream, a);
     else if (p.nw == 4)
       hipLaunchKernelGGL((tree_attn_dma_kernel<4, PAGED, false>), grid, dim3(256), 0, stream, a);
