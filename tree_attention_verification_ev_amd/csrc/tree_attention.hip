@@ -599,10 +599,10 @@ __device__ inline int64_t out_row(const AttnArgs &a, int b, int g, int r) {
 // write_rows for the DMA kernel (one query tile per wave): the wave's 32 normalised rows
 // go through an idle 8 KB of LDS (chunk-swizzled like a K tile) so that the global stores
 // are whole rows, 16 bytes per lane and four rows per instruction, instead of 8-byte pieces
-// scattered over 32 rows.  A split partial (fp16, pre-divided by max(1, |O|max) of its
-// row, with its LSE and divisor as one word) is stored non-temporally: the merge kernel
-// reads it once.
-template <int D>
+// scattered over 32 rows.  A split partial is fp16, pre-divided by max(1, |O|max) of its
+// row, with its LSE and divisor as one word; with NT its rows are stored non-temporally (the
+// merge reads each once).
+template <int D, bool NT>
 __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x16 (&o)[1][D / 32],
                                                   float mref, float l, int row0, int b, int g,
                                                   int split, int qn, int hh, uint16_t *stage) {
@@ -654,7 +654,11 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
     if (r < rows) {
       const int64_t orow = out_row(a, b, g, r);
       if (part) {
-        __builtin_nontemporal_store(v, (u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8));
+        u32x4 *dst = (u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8);
+        if constexpr (NT)
+          __builtin_nontemporal_store(v, dst);
+        else
+          *dst = v;
       } else {
         *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = v;
       }
@@ -1009,7 +1013,11 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
                         ? (uint16_t *)(lds + 3 * 2 * MAT + rg * 32 * D)   // past the exchange
                         : (uint16_t *)(lds + ((last + 1 + (wave >> 2)) % kStages) * 2 * MAT +
                                        (wave & 3) * 32 * D);
-  write_rows_staged<D>(a, o, mref[0], l[0], row0, b, g, split, qn, hh, stage);
+  // Partial rows go non-temporally from workgroups of 128 rows or more; a split plan of
+  // smaller workgroups writes at most 256 x 64 partial rows (4 MB), which stay cached
+  // (measured: 8 MB of partials, 8 splits of 4096 rows, 22.3 us per call non-temporal
+  // against 22.9 cached; 1.5 MB, 7 splits of 832 rows, 18.9 against 18.6).
+  write_rows_staged<D, RG * 32 >= 128>(a, o, mref[0], l[0], row0, b, g, split, qn, hh, stage);
 }
 
 // Combine split partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
