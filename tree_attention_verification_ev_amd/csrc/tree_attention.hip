@@ -580,6 +580,28 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Uses each value in scalar registers at this point of the program.  Listing the kernel
+// arguments a prologue needs here makes the compiler fetch them in one batch at entry,
+// where it would otherwise load each where it is first used, a dependent round trip
+// through the scalar cache each time.
+template <typename T>
+__device__ __forceinline__ void in_sgprs(T x) {
+  asm volatile("" ::"s"(x));
+}
+template <typename... Ts>
+__device__ __forceinline__ void args_in_sgprs(const Ts &...xs) {
+  (in_sgprs(xs), ...);
+}
+
+// A uniform load through the scalar cache: from the constant address space the compiler
+// may use a scalar load even after stores or inline assembly earlier in the kernel (read
+// through a global pointer there, it issues a vector load).  Only for data no kernel of
+// the call writes.
+template <typename T>
+__device__ __forceinline__ T scalar_load(const T *p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // Transposing LDS read of a V fragment.  The restrict-qualified pointer gives the read
@@ -697,6 +719,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT + kMaxNodes * 4];
   __shared__ int stbl[PAGED ? kTableCache : 1];
 
+  args_in_sgprs(gridDim.x, a.n_work, a.row_blocks, a.n_splits, a.kv.hkv, a.kv.cap, a.T, a.G, a.Hq,
+                a.q, a.k, a.v, a.anc, a.prefix_len, a.tiles_per_split, a.max_tiles, a.max_prefix);
   const int per_xcd = gridDim.x / kXcds;
   const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (w >= a.n_work) return;
@@ -705,6 +729,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   const int bg = w / (a.row_blocks * a.n_splits);
   const int b = bg / a.kv.hkv;
   const int g = bg % a.kv.hkv;
+  // The prefix length, as a scalar load ahead of every DMA: read after them it became a
+  // vector load that could only be waited for together with all of them.
+  const int L = scalar_load(a.prefix_len, b);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int qn = lane & 31;
@@ -801,7 +828,6 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     }
   }
 
-  const int L = a.prefix_len[b];
   const int nkeys = L + a.T;
   if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
     if (threadIdx.x == 0) report(a.dev_status, EV_DERR_BOUNDS);
@@ -1115,16 +1141,13 @@ __global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sP[R * kKT];
   __shared__ float sA[R], sM[R], sL[R];
 
+  args_in_sgprs(a.row_blocks, a.kv.hkv, a.kv.cap, a.T, a.G, a.Hq, a.q, a.k, a.v, a.anc,
+                a.prefix_len, a.max_prefix);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rb = blockIdx.x % a.row_blocks;
   const int bg = blockIdx.x / a.row_blocks;
   const int b = bg / a.kv.hkv, g = bg % a.kv.hkv;
-  const int L = a.prefix_len[b];
-  const int nkeys = L + a.T;
-  if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
-    if (tid == 0) report(a.dev_status, EV_DERR_BOUNDS);
-    return;
-  }
+  const int L = scalar_load(a.prefix_len, b);   // waited for after the first loads
   const int rows = a.T * a.G;
   const int row0 = rb * R;
   const int nrow = min(R, rows - row0);
@@ -1136,12 +1159,17 @@ __global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
     return ((int64_t)b * a.T + rr / a.G) * a.Hq + g * a.G + rr % a.G;
   };
 
-  // query rows of the block (zero past the last row)
-  for (int i = tid; i < R * C4; i += NT) {
-    const int r = i / C4, c = i % C4;
-    f32x4 x = {};
-    if (r < nrow) x = *(const f32x4 *)(Q + orow_of(r) * D + 4 * c);
-    *(f32x4 *)(sQ + r * D + 4 * c) = x;
+  // Loads that do not need the prefix length go out before it is known: the block's query
+  // rows (zero past the last row), the ancestor masks and, for a contiguous cache, the
+  // first K/V tile (slots clamped into the cache; keys past the sequence are zeroed when
+  // stored and masked when scored).
+  constexpr int QPT = (R * C4 + NT - 1) / NT;
+  f32x4 qx[QPT];
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int i = tid + u * NT, r = i / C4, c = i % C4;
+    qx[u] = f32x4{};
+    if (i < R * C4 && r < nrow) qx[u] = *(const f32x4 *)(Q + orow_of(r) * D + 4 * c);
   }
   uint64_t anc[RW];
 #pragma unroll
@@ -1150,23 +1178,28 @@ __global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
     anc[i] = r < nrow ? a.anc[(int64_t)b * a.T + (row0 + r) / a.G] : 0ull;
   }
 
-  // Every piece is loaded unconditionally from an in-bounds address (a slot past the
-  // sequence reloads its last slot; a bad block id reads the cache's first row) and
-  // masked only when stored: a load under a per-lane branch made the compiler wait for it
-  // at once.
+  // Every piece is loaded unconditionally from an in-bounds address (contiguous: a slot
+  // past the cache reloads its last slot; paged, loaded once the length is known: a slot
+  // past the sequence reloads its last slot, a bad block id reads the cache's first row)
+  // and masked only when stored: a load under a per-lane branch made the compiler wait
+  // for it at once.
   f32x4 kr[LPT], vr[LPT];
   bool bad = false;
   int key0_loaded = 0;
+  int nkeys = 0;
   auto load = [&](int key0) {
     key0_loaded = key0;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int piece = tid + i * NT, key = piece / C4, c = piece % C4;
-      const int slot = min(key0 + key, nkeys - 1);
-      int64_t off = PAGED ? a.kv.slot_offset(b, g, slot)
-                          : ((int64_t)(b * a.kv.hkv + g) * a.kv.cap + slot) * D;
-      bad |= off < 0;
-      off = off < 0 ? 0 : off;
+      int64_t off;
+      if constexpr (PAGED) {
+        off = a.kv.slot_offset(b, g, min(key0 + key, nkeys - 1));
+        bad |= off < 0;
+        off = off < 0 ? 0 : off;
+      } else {
+        off = ((int64_t)(b * a.kv.hkv + g) * a.kv.cap + min<int64_t>(key0 + key, a.kv.cap - 1)) * D;
+      }
       kr[i] = *(const f32x4 *)(K + off + 4 * c);
       vr[i] = *(const f32x4 *)(V + off + 4 * c);
     }
@@ -1180,6 +1213,23 @@ __global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
       *(f32x4 *)(sV + key * D + 4 * c) = live ? vr[i] : f32x4{};
     }
   };
+  if constexpr (!PAGED) load(0);
+
+  nkeys = L + a.T;
+  if (L < 0 || L > a.max_prefix || !a.kv.fits(nkeys)) {
+    if (tid == 0) report(a.dev_status, EV_DERR_BOUNDS);
+    if constexpr (!PAGED)
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) asm volatile("" ::"v"(kr[i]), "v"(vr[i]));   // keeps the
+      // early tile's loads above this branch (the compiler sank them past it otherwise)
+    return;
+  }
+  if constexpr (PAGED) load(0);
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int i = tid + u * NT;
+    if (i < R * C4) *(f32x4 *)(sQ + i * 4) = qx[u];
+  }
 
   float m[RW], l[RW], o[RPT];
 #pragma unroll
@@ -1193,7 +1243,6 @@ __global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
   // a broadcast read still moves 1 KB through the LDS per instruction.
   f32x4 qr[QREG ? RW : 1][QREG ? D / 4 : 1];
   const int ntiles = (nkeys + kKT - 1) / kKT;
-  load(0);
   if constexpr (QREG) {
     lds_barrier();                          // the query rows are in LDS
 #pragma unroll
@@ -1319,6 +1368,7 @@ static Plan make_plan(const KvAddr &kv, int dtype, int B, int T, int Hq, int64_t
     p.row_blocks = (rows + f32_rows(rows) - 1) / f32_rows(rows);
     p.n_splits = 1;
     p.tiles_per_split = 1 << 30;
+    p.max_tiles = (plan_slots(kv, T, max_prefix_len) + kKT - 1) / kKT;
     p.n_work = B * kv.hkv * p.row_blocks;
     p.grid = p.n_work;
     return p;
