@@ -297,6 +297,8 @@ template <bool REJ, int CPW, bool VEC>
 __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ double tab[64];
   __shared__ int s_last;
+  args_in_sgprs(a.n_chunks, a.T, a.V, a.logits, a.parent, a.tokens, a.uniforms, a.inv_tau,
+                a.stats, a.row_cnt);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.y;

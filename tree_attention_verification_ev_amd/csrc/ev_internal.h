@@ -92,4 +92,26 @@ inline ev_status launch_status() {
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Uses each value in scalar registers at this point of the program.  Listing the kernel
+// arguments a prologue needs here makes the compiler fetch them in one batch at entry,
+// where it would otherwise load each where it is first used, a dependent round trip
+// through the scalar cache each time.
+template <typename T>
+__device__ __forceinline__ void in_sgprs(T x) {
+  asm volatile("" ::"s"(x));
+}
+template <typename... Ts>
+__device__ __forceinline__ void args_in_sgprs(const Ts &...xs) {
+  (in_sgprs(xs), ...);
+}
+
+// A uniform load through the scalar cache: from the constant address space the compiler
+// may use a scalar load even after stores or inline assembly earlier in the kernel (read
+// through a global pointer there, it issues a vector load).  Only for data no kernel of
+// the call writes.
+template <typename T>
+__device__ __forceinline__ T scalar_load(const T *p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+
 }  // namespace ev

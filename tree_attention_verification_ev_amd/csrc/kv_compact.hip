@@ -53,11 +53,18 @@ __global__ __launch_bounds__(kCompactThreads) void kv_compact_kernel(CompactArgs
   const int g = (z >> 1) % a.kv.hkv;
   const int group = (z >> 1) / a.kv.hkv;
   const int tid = threadIdx.x;
+  // the arguments in one batch, then the sequence's copy mask, length, accepted count and
+  // path together (loaded where first used they were five dependent round trips)
+  args_in_sgprs(a.copy_mask, a.mask_stride, a.prefix_len, a.accept_len, a.path, a.T, a.kv.hkv,
+                a.kv.d, a.kv.paged, a.kv.cap, a.n_layers, a.layers_per_wg, a.row_bytes,
+                a.layer_stride, a.k, a.v, a.k_scale, a.v_scale);
   const uint64_t mask = a.copy_mask ? a.copy_mask[(int64_t)b * a.mask_stride] : ~0ull;
-  if (mask == 0) return;                 // remap mode: nothing to copy (or an invalid tree)
   const int L = a.prefix_len[b];
   const int k = a.accept_len[b];
-  if (tid < kMaxNodes) s_path[tid] = tid < a.T ? a.path[(int64_t)b * a.T + tid] : -1;
+  const int pth = tid < kMaxNodes && tid < a.T ? a.path[(int64_t)b * a.T + tid] : -1;
+  args_in_sgprs(mask, L, k);
+  if (mask == 0) return;                 // remap mode: nothing to copy (or an invalid tree)
+  if (tid < kMaxNodes) s_path[tid] = pth;
   if (tid == 0) s_bad = 0;
   __syncthreads();
   if (!a.copy_mask) {

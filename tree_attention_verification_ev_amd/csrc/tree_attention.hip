@@ -580,28 +580,6 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Uses each value in scalar registers at this point of the program.  Listing the kernel
-// arguments a prologue needs here makes the compiler fetch them in one batch at entry,
-// where it would otherwise load each where it is first used, a dependent round trip
-// through the scalar cache each time.
-template <typename T>
-__device__ __forceinline__ void in_sgprs(T x) {
-  asm volatile("" ::"s"(x));
-}
-template <typename... Ts>
-__device__ __forceinline__ void args_in_sgprs(const Ts &...xs) {
-  (in_sgprs(xs), ...);
-}
-
-// A uniform load through the scalar cache: from the constant address space the compiler
-// may use a scalar load even after stores or inline assembly earlier in the kernel (read
-// through a global pointer there, it issues a vector load).  Only for data no kernel of
-// the call writes.
-template <typename T>
-__device__ __forceinline__ T scalar_load(const T *p, int64_t i) {
-  return ((const __attribute__((address_space(4))) T *)p)[i];
-}
-
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // Transposing LDS read of a V fragment.  The restrict-qualified pointer gives the read
@@ -1054,6 +1032,7 @@ template <int D, int E, int BATCH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int LPR = D / E;             // lanes per row
   constexpr int RPB = 256 / LPR;         // rows per workgroup
+  args_in_sgprs(a.B, a.T, a.Hq, a.n_splits, a.part_o, a.part_ls, a.out, a.lse);
   typedef _Float16 hE __attribute__((ext_vector_type(E)));
   typedef __bf16 bE __attribute__((ext_vector_type(E)));
   const int64_t nrows = (int64_t)a.B * a.T * a.Hq;

@@ -13,6 +13,7 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t *__restrict
                                                         int32_t T, uint64_t *__restrict__ anc,
                                                         int32_t *__restrict__ depth,
                                                         int32_t *dev_status) {
+  args_in_sgprs(parent, T, anc, depth);
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const bool live = i < T;
