@@ -93,11 +93,24 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
   for (;;) {
     const int y0 = cstar * kChunk + lane * 16;   // lane scans 16 consecutive ids
     double pv[16];
+    float lv[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int y = y0 + e;
-      const double pe = exp_nonpos(shifted(row[min(y, V - 1)], inv_tau, M), tab) * inv_S;
-      pv[e] = y < V ? pe : 0.0;
+    for (int e = 0; e < 16; ++e) lv[e] = row[min(y0 + e, V - 1)];
+    // table reads in batches of 4, each batch issued before any of it is used (a larger
+    // batch raised the kernel's register count and cost the logit stream occupancy)
+#pragma unroll
+    for (int h = 0; h < 16; h += 4) {
+      ExpParts ep[4];
+      double tj[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ep[e] = exp_split(shifted(lv[h + e], inv_tau, M));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tj[e] = tab[ep[e].k & 63];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double pe = exp_join(ep[e], tj[e]) * inv_S;
+        pv[h + e] = y0 + h + e < V ? pe : 0.0;
+      }
     }
     for (uint64_t rr = rej; rr; rr &= rr - 1) {
       const int x = __shfl(tok, __ffsll((unsigned long long)rr) - 1);
@@ -248,7 +261,7 @@ __device__ void finish_sequence(const Args &a, int b, int tok) {
 template <bool REJ>
 using ChunkStat = typename std::conditional<REJ, RejStat, uint64_t>::type;
 
-template <bool REJ>
+template <bool REJ, int XB>
 __device__ __forceinline__ ChunkStat<REJ> chunk_stats(const AcceptArgs &a, int chunk,
                                                       const float (&v)[16], const double *tab) {
   const int lane = threadIdx.x & 63;
@@ -274,9 +287,7 @@ __device__ __forceinline__ ChunkStat<REJ> chunk_stats(const AcceptArgs &a, int c
     const double M = (double)wave_max_f(best) * a.inv_tau;
     // Padding past V holds -inf: its term is clamped to at most 5e-324, which vanishes
     // next to the chunk's own maximum term (1), so no per-element test is needed.
-    double sum = 0.0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sum += exp_nonpos(shifted(v[e], a.inv_tau, M), tab);
+    const double sum = exp_sum<16, XB>([&](int e) { return shifted(v[e], a.inv_tau, M); }, tab);
     return RejStat{M, wave_sum(sum)};
   }
 }
@@ -324,6 +335,9 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   // filled (26 rows x 32000: 6.38 -> 5.98 us); with two or four they go out after the
   // barrier (issued before it, 64 rows x 128256 took 18.3 -> 18.6 us).
   ChunkStat<REJ> st[CPW];
+  // exp table reads issued 8 (four chunks per wavefront: 4) at a time; 8 with four chunks
+  // took the kernel past the register count that keeps six wavefronts per SIMD
+  constexpr int kExpBatch = CPW == 4 ? 4 : 8;
   if constexpr (CPW == 1) load_chunk_raw<kNT, VEC>(lrow, a.V, min(c0, nc - 1) * kChunk, v[0]);
 
   if (REJ) fill_exp_table(tab);
@@ -345,7 +359,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
       load_chunk_raw<kNT, VEC>(lrow, a.V, min(c + kChunksPerWG, nc - 1) * kChunk, v[(m + 1) & 1]);
     if (c < nc) {
       mask_chunk(a.V, c * kChunk, v[m & 1], idx_unused);
-      st[m] = chunk_stats<REJ>(a, c, v[m & 1], tab);
+      st[m] = chunk_stats<REJ, kExpBatch>(a, c, v[m & 1], tab);
     }
   }
   if (lane == 0) {
@@ -610,6 +624,7 @@ __device__ bool sampled_decide(const SampledArgs &a, int64_t row, const SampledR
 // the tree and sets up the row state.
 template <int CPW, bool VEC>
 __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
+  constexpr int XB = 4;                  // exp table reads issued 4 at a time
   __shared__ double tab[64];
   __shared__ int s_last;
   fill_exp_table(tab);
@@ -654,12 +669,8 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
       }
       const double Mp = (double)wave_max_f(bp) * a.inv_tau;
       const double Mq = (double)wave_max_f(bq) * a.inv_tau_q;
-      double sp = 0.0, sq = 0.0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sp += exp_nonpos(shifted(xp[e], a.inv_tau, Mp), tab);
-        sq += exp_nonpos(shifted(xq[e], a.inv_tau_q, Mq), tab);
-      }
+      const double sp = exp_sum<16, XB>([&](int e) { return shifted(xp[e], a.inv_tau, Mp); }, tab);
+      const double sq = exp_sum<16, XB>([&](int e) { return shifted(xq[e], a.inv_tau_q, Mq); }, tab);
       stp[m] = RejStat{Mp, wave_sum(sp)};
       stq[m] = RejStat{Mq, wave_sum(sq)};
     }

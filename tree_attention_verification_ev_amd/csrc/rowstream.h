@@ -37,7 +37,14 @@ __host__ __device__ inline int n_chunks_of(int V) { return (V + kChunk - 1) / kC
 // The nearest integer to 64 x / ln2 comes from adding and removing 1.5 * 2^52, whose low
 // word then holds it as a two's-complement integer.  Arguments below -745 (results below
 // the smallest subnormal) are clamped there, so they return at most 5e-324.
-__device__ inline double exp_nonpos(double x, const double *tab) {
+// The method in two halves, so that a caller can issue the table reads of several
+// arguments before it combines any of them (each read is an LDS round trip):
+// exp_nonpos(x) = exp_join(exp_split(x), tab[k & 63]).
+struct ExpParts {
+  double p;                                                   // exp(r) - 1
+  int k;                                                      // 64 m + j
+};
+__device__ inline ExpParts exp_split(double x) {
   constexpr double kInvLn2x64 = 92.33248261689366;            // 64 / ln 2
   constexpr double kLn2d64Hi = 0.010830424696249145;          // ln2/64 rounded to double
   constexpr double kLn2d64Lo = 3.623510646634843e-19;         // ln2/64 - kLn2d64Hi
@@ -52,9 +59,34 @@ __device__ inline double exp_nonpos(double x, const double *tab) {
   p = fma(r, p, 1.0 / 6.0);
   p = fma(r, p, 0.5);
   p = fma(r, p, 1.0);
-  p *= r;                                                     // exp(r) - 1
-  const double tj = tab[k & 63];
-  return ldexp(fma(tj, p, tj), k >> 6);
+  return ExpParts{p * r, k};
+}
+__device__ inline double exp_join(ExpParts e, double tj) {
+  return ldexp(fma(tj, e.p, tj), e.k >> 6);
+}
+__device__ inline double exp_nonpos(double x, const double *tab) {
+  const ExpParts e = exp_split(x);
+  return exp_join(e, tab[e.k & 63]);
+}
+// sum of exp_nonpos(x(e)), e = 0 .. N-1 in order, the table reads of every XB arguments
+// issued before any of them is used (with XB = 1, one read at a time, each waited for
+// before the next argument begins).  The arithmetic does not depend on XB.
+template <int N, int XB, class F>
+__device__ __forceinline__ double exp_sum(F x, const double *tab) {
+  static_assert(N % XB == 0, "whole batches");
+  double sum = 0.0;
+#pragma unroll
+  for (int h = 0; h < N; h += XB) {
+    ExpParts ep[XB];
+    double tj[XB];
+#pragma unroll
+    for (int e = 0; e < XB; ++e) ep[e] = exp_split(x(h + e));
+#pragma unroll
+    for (int e = 0; e < XB; ++e) tj[e] = tab[ep[e].k & 63];
+#pragma unroll
+    for (int e = 0; e < XB; ++e) sum += exp_join(ep[e], tj[e]);
+  }
+  return sum;
 }
 
 // s - M for a logit at inverse temperature inv_tau (one rounding).
