@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   const int wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.y;
   const int nc = a.n_chunks;
-  const int b = (int)(row / a.T), n = (int)(row % a.T);
+  const int b = (int)row / a.T, n = (int)row % a.T;   // row < 2^31
 
   // ---- this wavefront's chunk statistics ----
   const float *lrow = a.logits + row * a.V;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   // A chunk past the row's end (last workgroup of a row) loads the row's last chunk and is
   // not reduced.  With one chunk per wavefront its loads go out before the exp table is
   // filled (26 rows x 32000: 6.38 -> 5.98 us); with two or four they go out after the
-  // barrier (issued before it, 64 rows x 128256 took 18.3 -> 18.6 us).
+  // barrier (issued before it, 64 rows x 128256 took 16.15 -> 16.48 us, same-box pairs).
   ChunkStat<REJ> st[CPW];
   // exp table reads issued 8 (four chunks per wavefront: 4) at a time; 8 with four chunks
   // took the kernel past the register count that keeps six wavefronts per SIMD
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     tok = a.tokens[(int64_t)b * a.T + lane];
     if (REJ) ul = a.uniforms[(int64_t)b * a.T + lane];
   }
-  __syncthreads();
+  lds_barrier();                          // the exp table
   if constexpr (CPW != 1) load_chunk_raw<kNT, VEC>(lrow, a.V, min(c0, nc - 1) * kChunk, v[0]);
 #pragma unroll
   for (int m = 0; m < CPW; ++m) {

@@ -92,6 +92,12 @@ inline ev_status launch_status() {
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations, not for its
+// global loads in flight (__syncthreads waits for those as well).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Uses each value in scalar registers at this point of the program.  Listing the kernel
 // arguments a prologue needs here makes the compiler fetch them in one batch at entry,
 // where it would otherwise load each where it is first used, a dependent round trip

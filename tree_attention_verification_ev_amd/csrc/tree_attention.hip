@@ -1094,9 +1094,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 // Workgroup barrier for LDS data only: the wave's LDS accesses complete, then s_barrier.
 // Unlike __syncthreads it does not wait for global loads, so a tile prefetched into
 // registers stays in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int D, int R, bool PAGED, int NT>
 __global__ __launch_bounds__(NT) void tree_attn_f32_kernel(AttnArgs a) {
