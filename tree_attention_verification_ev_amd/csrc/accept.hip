@@ -62,10 +62,12 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
                              uint64_t rej, int tok, double prej, double t, const double *tab) {
   const int lane = threadIdx.x & 63;
   const double inv_S = 1.0 / S;
-  double mass[kChunkRegs];
+  double mass[kChunkRegs], xm[kChunkRegs], em[kChunkRegs];
 #pragma unroll
-  for (int r = 0; r < kChunkRegs; ++r)
-    mass[r] = cs[r].S > 0.0 ? cs[r].S * exp_nonpos(cs[r].M - M, tab) * inv_S : 0.0;
+  for (int r = 0; r < kChunkRegs; ++r) xm[r] = cs[r].M - M;
+  exp_nonpos_n(xm, em, tab);
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) mass[r] = cs[r].S > 0.0 ? cs[r].S * em[r] * inv_S : 0.0;
   for (uint64_t rr = rej; rr; rr &= rr - 1) {
     const int src = __ffsll((unsigned long long)rr) - 1;
     const int x = __shfl(tok, src);
@@ -201,6 +203,9 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
       double M, S;
       row_stats_regs(cs, tab, M, S);
       const double inv_S = 1.0 / S;
+      // every child's target probability at once, in its own lane (in the loop below, one
+      // exp per child, each waiting for its table read, made wide nodes the slowest rows)
+      const double pk = exp_nonpos(shifted(lg, a.inv_tau, M), tab) * inv_S;
       double Z = 1.0, myp = 0.0;
       uint64_t rej = 0;
       next = -1;
@@ -208,7 +213,7 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
         const int c = __ffsll((unsigned long long)kk) - 1;
         const int x = __shfl(tok, c);
         if (__ballot(((rej >> lane) & 1) && tok == x)) continue;   // already rejected here
-        const double p = exp_nonpos(shifted(__shfl(lg, c), a.inv_tau, M), tab) * inv_S;
+        const double p = __shfl(pk, c);
         if (__shfl(ul, c) * Z < p) {
           next = c;
           break;
@@ -719,10 +724,12 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
       row_stats_regs(cp, tab, st.Mp, st.Sp);
       row_stats_regs(cq, tab, st.Mq, st.Sq);
       const double inv_sp = 1.0 / st.Sp;
-      double mass[kChunkRegs];
+      double mass[kChunkRegs], xm[kChunkRegs], em[kChunkRegs];
 #pragma unroll
-      for (int r = 0; r < kChunkRegs; ++r)
-        mass[r] = cp[r].S > 0.0 ? cp[r].S * exp_nonpos(cp[r].M - st.Mp, tab) * inv_sp : 0.0;
+      for (int r = 0; r < kChunkRegs; ++r) xm[r] = cp[r].M - st.Mp;
+      exp_nonpos_n(xm, em, tab);
+#pragma unroll
+      for (int r = 0; r < kChunkRegs; ++r) mass[r] = cp[r].S > 0.0 ? cp[r].S * em[r] * inv_sp : 0.0;
       const bool done = sampled_decide(a, row, st, v, mass, tab);
       if (lane == 0) s_last = done ? 1 : 0;
     } else if (lane == 0) {

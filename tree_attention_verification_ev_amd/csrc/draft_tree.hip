@@ -237,11 +237,14 @@ __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, M
       M = fmax(M, cs[r].M);
     }
     M = wave_max(M);
-    double S = 0.0, T = 0.0;
+    double S = 0.0, T = 0.0, xf[kChunkRegs], ef[kChunkRegs];
+#pragma unroll
+    for (int r = 0; r < kChunkRegs; ++r) xf[r] = cs[r].M - M;
+    exp_nonpos_n(xf, ef, tab);
 #pragma unroll
     for (int r = 0; r < kChunkRegs; ++r) {
       if (cs[r].S > 0.0) {
-        const double f = exp_nonpos(cs[r].M - M, tab);
+        const double f = ef[r];
         S += cs[r].S * f;
         T += f * fma(cs[r].M - M, cs[r].S, cs[r].T);
       }

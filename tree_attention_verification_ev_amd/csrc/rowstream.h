@@ -68,6 +68,19 @@ __device__ inline double exp_nonpos(double x, const double *tab) {
   const ExpParts e = exp_split(x);
   return exp_join(e, tab[e.k & 63]);
 }
+// exp_nonpos of N arguments, their table reads issued together.
+template <int N>
+__device__ __forceinline__ void exp_nonpos_n(const double (&x)[N], double (&y)[N],
+                                             const double *tab) {
+  ExpParts ep[N];
+  double tj[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) ep[i] = exp_split(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) tj[i] = tab[ep[i].k & 63];
+#pragma unroll
+  for (int i = 0; i < N; ++i) y[i] = exp_join(ep[i], tj[i]);
+}
 // sum of exp_nonpos(x(e)), e = 0 .. N-1 in order, the table reads of every XB arguments
 // issued before any of them is used (with XB = 1, one read at a time, each waited for
 // before the next argument begins).  The arithmetic does not depend on XB.
@@ -337,10 +350,14 @@ __device__ inline void row_stats_regs(const RejStat (&cs)[kChunkRegs], const dou
 #pragma unroll
   for (int r = 0; r < kChunkRegs; ++r) M = fmax(M, cs[r].M);
   M = wave_max(M);
+  double x[kChunkRegs], e[kChunkRegs];
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) x[r] = cs[r].M - M;
+  exp_nonpos_n(x, e, tab);
   S = 0.0;
 #pragma unroll
   for (int r = 0; r < kChunkRegs; ++r)
-    if (cs[r].S > 0.0) S += cs[r].S * exp_nonpos(cs[r].M - M, tab);
+    if (cs[r].S > 0.0) S += cs[r].S * e[r];
   S = wave_sum(S);
 }
 
