@@ -57,7 +57,7 @@ struct TreeFront {
 };
 
 struct TreeWs {
-  size_t row_cnt, seq_cnt, chunk, top, rows, front, cand, cand_count, n_exp, total;
+  size_t row_cnt, seq_cnt, chunk, top, rows, front, cand, cand_rank, cand_count, n_exp, total;
 };
 
 inline TreeWs tree_ws_layout(int B, int W, int V) {
@@ -70,7 +70,8 @@ inline TreeWs tree_ws_layout(int B, int W, int V) {
   w.rows = w.top + align_up(per_chunk * sizeof(uint64_t), 256);
   w.front = w.rows + align_up(rows * sizeof(TreeRow), 256);
   w.cand = w.front + align_up(2 * (size_t)B * sizeof(TreeFront), 256);
-  w.cand_count = w.cand + align_up((size_t)B * kMaxExpansions * kCandSlots * sizeof(TreeCand), 256);
+  w.cand_rank = w.cand + align_up((size_t)B * kMaxExpansions * kCandSlots * sizeof(TreeCand), 256);
+  w.cand_count = w.cand_rank + align_up((size_t)B * kMaxExpansions * kCandSlots * sizeof(int32_t), 256);
   w.n_exp = w.cand_count + align_up((size_t)B * kMaxExpansions * sizeof(int32_t), 256);
   w.total = w.n_exp + align_up((size_t)B * sizeof(int32_t), 256);
   return w;
@@ -86,6 +87,7 @@ struct ExpandArgs {
   const TreeFront *front_in;           // [B], this depth's frontier (depth >= 1)
   TreeFront *front_out;                // [B], the next one
   TreeCand *cand;                      // [B][kMaxExpansions][kCandSlots]
+  int32_t *cand_rank;                  // [B][kMaxExpansions][kCandSlots]: slot of each rank
   int32_t *cand_count;                 // [B][kMaxExpansions]
   int32_t *n_exp;                      // [B] expansions done
   int32_t *row_cnt, *seq_cnt;
@@ -371,6 +373,7 @@ __device__ void expand_sequence(const ExpandArgs &a, int b, int count, double *s
     const double vf = sval[f];
     rank += ((vf > value) | ((vf == value) & (f < lane))) ? 1 : 0;
   }
+  if (valid) a.cand_rank[cbase + rank] = slot;   // the depth's candidates best first
   const int n_sel = min(a.W, n_valid);
   TreeFront *fo = a.front_out + b;
   if (valid && rank < n_sel) {
@@ -457,15 +460,20 @@ struct FinalArgs {
   const int32_t *root_tokens;
   int B, n_nodes;
   const TreeCand *cand;
+  const int32_t *cand_rank;
   const int32_t *cand_count;
   const int32_t *n_exp;
   int32_t *parent, *tokens, *tree_size;
 };
 
 // The tree of each sequence: the n_nodes - 1 best candidates, numbered by depth, then by
-// value rank.  One workgroup per sequence: the candidates (id = depth * 64 + slot) are
-// sorted in LDS by a bitonic network into the order "larger value first, then lower id",
-// then one wavefront numbers the first n_nodes - 1.
+// value rank.  One workgroup per sequence.  The order is "larger value first, then lower
+// id" (id = depth * 64 + slot); each depth's candidates are already listed in that order
+// (expand_sequence ranks them for its beam), so a candidate's place in the whole order is
+// its rank in its own depth plus, for every other depth, the number of that depth's
+// candidates before it, found by binary search.  Only candidates ranked below
+// n_nodes - 1 in their own depth can be among the best n_nodes - 1.  (A full bitonic sort
+// of all candidates took 55 dependent LDS stages.)  One wavefront then numbers them.
 constexpr int kFinalThreads = 512;
 constexpr int kFinalKeys = kMaxExpansions * kCandSlots;
 
@@ -475,70 +483,68 @@ __device__ inline bool key_before(double v, int i, double v2, int i2) {
 
 __global__ __launch_bounds__(kFinalThreads) void tree_finalize_kernel(FinalArgs a) {
   __shared__ double kv[kFinalKeys];
-  __shared__ int ki[kFinalKeys];
+  __shared__ int ki[kCandSlots];
+  __shared__ int srt[kFinalKeys];
   __shared__ int pos_of[kFinalKeys];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   __shared__ int s_cc[kMaxExpansions];
-  // every load at once: the expansion count, the per-depth counts and all candidate slots
+  // every load at once: the expansion count, the per-depth counts, all candidate values
+  // and the rank-order lists
   const int n_exp_raw = a.n_exp[b];
   const TreeCand *cb = a.cand + (int64_t)b * kMaxExpansions * kCandSlots;
+  const int32_t *cr = a.cand_rank + (int64_t)b * kMaxExpansions * kCandSlots;
   const int32_t *cc = a.cand_count + (int64_t)b * kMaxExpansions;
   if (tid < kMaxExpansions) s_cc[tid] = cc[tid];
   double cval[kFinalKeys / kFinalThreads];
+  int crank[kFinalKeys / kFinalThreads];
 #pragma unroll
-  for (int r = 0; r < kFinalKeys / kFinalThreads; ++r) cval[r] = cb[tid + r * kFinalThreads].value;
+  for (int r = 0; r < kFinalKeys / kFinalThreads; ++r) {
+    cval[r] = cb[tid + r * kFinalThreads].value;
+    crank[r] = cr[tid + r * kFinalThreads];
+  }
   const int n_exp = max(0, min(n_exp_raw, kMaxExpansions));
   __syncthreads();
-  int n_keys = kCandSlots;
-  while (n_keys < n_exp * kCandSlots) n_keys <<= 1;
   int total = 0;
   for (int e = 0; e < n_exp; ++e) total += min(max(s_cc[e], 0), kCandSlots);
+  const int n_sel = min(a.n_nodes - 1, total);
 #pragma unroll
   for (int r = 0; r < kFinalKeys / kFinalThreads; ++r) {
     const int i = tid + r * kFinalThreads;
     const int e = i / kCandSlots, slot = i % kCandSlots;
     const bool valid = e < n_exp && slot < s_cc[e];
     kv[i] = valid ? cval[r] : -1.0;    // values are >= 0
-    ki[i] = valid ? i : INT_MAX;
+    srt[i] = (e << 6) | (crank[r] & (kCandSlots - 1));   // id of the rank-slot-th best
     pos_of[i] = 0;
   }
+  if (tid < kCandSlots) ki[tid] = INT_MAX;
   __syncthreads();
-  // bitonic network: each stage is n_keys / 2 compare-exchanges, pair p of a stage with
-  // distance j joins t (bit j clear) and t + j.  For j <= 64 both elements of every pair
-  // of wavefront w lie in its own 128-element block (pairs 64 w .. 64 w + 63), and LDS
-  // accesses of one wavefront take effect in order.  So the whole workgroup must have
-  // finished the previous stage only where one of the two stages crosses blocks: a stage
-  // with j >= 128, or the j = 64 stage that follows one.
-  for (int k = 2; k <= n_keys; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 128 || (j == 64 && k >= 256)) {
-        __syncthreads();
-      } else {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // candidate (depth e, own rank r): place = r + sum over the other depths of the number
+  // of their candidates before it
+#pragma unroll
+  for (int q = 0; q < kFinalKeys / kFinalThreads; ++q) {
+    const int i = tid + q * kFinalThreads;
+    const int e = i / kCandSlots, r = i % kCandSlots;
+    if (e >= n_exp || r >= min(s_cc[e], kCandSlots) || r >= n_sel) continue;
+    const int id = srt[i];
+    const double v = kv[id];
+    int place = r;
+    for (int e2 = 0; e2 < n_exp; ++e2) {
+      if (e2 == e) continue;
+      int lo = 0, hi = min(max(s_cc[e2], 0), kCandSlots);
+      while (lo < hi) {                  // first of depth e2 not before (v, id)
+        const int mid = (lo + hi) >> 1;
+        const int id2 = srt[e2 * kCandSlots + mid];
+        if (key_before(kv[id2], id2, v, id)) lo = mid + 1;
+        else hi = mid;
       }
-      for (int p = tid; p < n_keys / 2; p += kFinalThreads) {
-        const int t = ((p & ~(j - 1)) << 1) | (p & (j - 1));
-        const int u = t + j;
-        const double vt = kv[t], vu = kv[u];
-        const int it = ki[t], iu = ki[u];
-        const bool first_half = (t & k) == 0;     // this run sorts best-first
-        const bool swap = first_half ? key_before(vu, iu, vt, it) : key_before(vt, it, vu, iu);
-        if (swap) {
-          kv[t] = vu;
-          kv[u] = vt;
-          ki[t] = iu;
-          ki[u] = it;
-        }
-      }
+      place += lo;
     }
+    if (place < n_sel) ki[place] = id;
   }
   __syncthreads();
   // numbering (wavefront 0): by depth, then by rank (lane r holds the r-th best)
   const int lane = tid & 63;
-  const int n_sel = min(a.n_nodes - 1, total);
   int id = INT_MAX, pos = 0, n_tree = 1;
   bool mine = false;
   if (tid < 64) {
@@ -605,7 +611,8 @@ EV_API ev_status ev_draft_tree_expand(const float *draft_logits, int32_t B, int3
                1.0 / (double)temperature, (TreeChunk *)(base + w.chunk),
                (uint64_t *)(base + w.top), (TreeRow *)(base + w.rows),
                fronts + (size_t)(depth & 1) * B, fronts + (size_t)((depth + 1) & 1) * B,
-               (TreeCand *)(base + w.cand), (int32_t *)(base + w.cand_count),
+               (TreeCand *)(base + w.cand), (int32_t *)(base + w.cand_rank),
+               (int32_t *)(base + w.cand_count),
                (int32_t *)(base + w.n_exp), (int32_t *)(base + w.row_cnt),
                (int32_t *)(base + w.seq_cnt), frontier_tokens, frontier_slots, frontier_count,
                dev_status};
@@ -636,8 +643,8 @@ EV_API ev_status ev_draft_tree_finalize(const int32_t *root_tokens, int32_t B, i
   if (!ws || ws_bytes < w.total) return EV_ERR_WORKSPACE;
   char *base = (char *)ws;
   FinalArgs a{root_tokens, B, n_nodes, (const TreeCand *)(base + w.cand),
-              (const int32_t *)(base + w.cand_count), (const int32_t *)(base + w.n_exp),
-              parent, tokens, tree_size};
+              (const int32_t *)(base + w.cand_rank), (const int32_t *)(base + w.cand_count),
+              (const int32_t *)(base + w.n_exp), parent, tokens, tree_size};
   hipLaunchKernelGGL(tree_finalize_kernel, dim3(B), dim3(kFinalThreads), 0, stream, a);
   return launch_status();
 }
