@@ -711,7 +711,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // vector load that could only be waited for together with all of them.
   const int L = scalar_load(a.prefix_len, b);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // (uniform; said so for eight-wavefront workgroups, whose tile DMA addresses are scalar)
+  const int wave = NW == 8 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int qn = lane & 31;
   const int hh = lane >> 5;
   const int rows = a.T * a.G;
@@ -846,9 +847,49 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     return ((((int64_t)blk * a.kv.hkv + g) << a.kv.block_shift) |
             (slot & ((1 << a.kv.block_shift) - 1))) * D;
   };
-  auto issue = [&](int tile, int stg) {
+  // A full tile whose DMA instructions each stay within one page (pages of 4 or more
+  // tokens; a contiguous cache always): every instruction reads 4 consecutive slots, so
+  // its address is a wave-uniform base (scalar arithmetic; a paged cache's block id from
+  // a scalar load of the table, issued by page_ids ahead of the barrier that precedes the
+  // DMA) plus a lane-constant offset.  Other tiles go slot by slot.
+  const bool whole_pages = NW == 8 && (!PAGED || a.kv.block_shift >= 2);
+  const int lrow = (lane >> 4) * D;              // slot within the instruction's four
+  struct PageIds { int id[IPW]; };
+  auto page_ids = [&](int tile) {
+    PageIds p;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      p.id[i] = 0;
+      if constexpr (PAGED) {
+        const int kq = tile * kKT + 4 * (wave * IPW + i);
+        const int64_t e = (int64_t)b * a.kv.max_blocks + (min(kq, nkeys - 1) >> a.kv.block_shift);
+        p.id[i] = scalar_load(a.kv.table, e);
+      }
+    }
+    return p;
+  };
+  auto issue = [&](int tile, int stg, const PageIds &p) {
     const int key0 = tile * kKT;
     const bool full = key0 + kKT <= nkeys;
+    if (full && whole_pages) {
+      __bf16 *kd = lds + stg * 2 * MAT;
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int blk = wave * IPW + i;
+        const int kq = key0 + 4 * blk;           // first slot of this instruction
+        int64_t base;
+        if constexpr (PAGED) {
+          const int id = p.id[i] < 0 || p.id[i] >= a.kv.n_blocks ? 0 : p.id[i];   // reported
+          base = ((((int64_t)id * a.kv.hkv + g) << a.kv.block_shift) +
+                  (kq & ((1 << a.kv.block_shift) - 1))) * D;
+        } else {
+          base = seq_base + (int64_t)kq * D;
+        }
+        dma16(K + base + (uint32_t)(lrow + doffK[i]), kd + blk * 512);
+        dma16(V + base + (uint32_t)(lrow + doffV[i]), kd + MAT + blk * 512);
+      }
+      return;
+    }
     issue_rows(tile, stg, [&](int slot) {
       // past the sequence: finite data, masked out
       return row_off(!full && slot >= nkeys ? key0 : slot);
@@ -927,11 +968,12 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
     using REFILL = std::integral_constant<int, (STG + 3) % kStages>;
     const bool more = j + 1 < t_end;
     if (more) {
+      const PageIds ids = page_ids(j + 3);       // in flight while the tile lands
       landed(min(t_end - 1, j + 2) - (j + 1));
       if constexpr (!PAGED)
         if (j == t_begin) fix_tail(j + 1, NEXT::value);   // the second early tile
       wg_barrier();                              // tile j+1 visible; stage of j-1 free
-      if (j + 3 < t_end) issue(j + 3, REFILL::value);
+      if (j + 3 < t_end) issue(j + 3, REFILL::value, ids);
       scores_of(sn, NEXT{});
     }
     if (j * kKT + kKT > L) tile_mask(sc, anc_q, j * kKT + st0 * 32, L, hh);
@@ -947,10 +989,10 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // wave has them the third tile goes into the area they occupied; then the scores of the
   // first tile.
   if constexpr (PAGED) {
-    issue(t_begin, 0);
+    issue(t_begin, 0, page_ids(t_begin));
     n_early = 1;
     if (t_begin + 1 < t_end) {
-      issue(t_begin + 1, 1);
+      issue(t_begin + 1, 1, page_ids(t_begin + 1));
       n_early = 2;
     }
   }
@@ -963,7 +1005,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   wg_barrier();                                  // every wave holds its Q: stages 2, 3 free
   anc_q[0] = row0 + qn < rows ? s_anc[(row0 + qn) / a.G] : 0ull;
-  if (t_begin + 2 < t_end) issue(t_begin + 2, 2);
+  if (t_begin + 2 < t_end) issue(t_begin + 2, 2, page_ids(t_begin + 2));
   // (with an early second tile beyond t_end this waits for everything in flight)
   landed(min(t_end - 1, t_begin + 2) - t_begin);
   if constexpr (!PAGED) fix_tail(t_begin, 0);
