@@ -94,6 +94,19 @@ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations, not for its
 // global loads in flight (__syncthreads waits for those as well).
+// A lane's value combined with that of the lane 32 away (the other half of the wavefront),
+// through the cross-half swap of gfx950: a vector-unit operation, where a shuffle
+// (ds_bpermute) is an LDS round trip.  Lane l < 32 gets op(x[l], x[l+32]), lane l >= 32
+// op(x[l-32], x[l]), so both halves hold the same bits.
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -158,7 +158,7 @@ __device__ __forceinline__ void tile_rescale(const f32x16 (&s)[QT][NST], f32x16 
     for (int st = 0; st < NST; ++st)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][st][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    mx = halves_max(mx) * scale_log2;
     if (__any(mx > mref[t] + kRescaleSlack)) {
       const float mnew = fmaxf(mref[t], mx);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref[t] - mnew);
@@ -176,7 +176,7 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[QT][NST], bf16x8 (&pf
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const float nb = mref[t] == -INFINITY ? 0.f : -mref[t];
-    float sum = 0.f;
+    float sum = -0.f;                            // the additive identity: no leading add
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       f32x16 p;
@@ -225,7 +225,7 @@ __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int r = row0 + t * 32 + qn;
-    const float ltot = l[t] + __shfl_xor(l[t], 32);
+    const float ltot = halves_sum(l[t]);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse = ltot > 0.f ? (mref[t] + __log2f(ltot)) * kLn2 : -INFINITY;
     const bool ok = r < rows;
@@ -251,7 +251,7 @@ __device__ __forceinline__ void write_rows(const AttnArgs &a, const f32x16 (&o)[
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[t][dt][i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+      amax = halves_max(amax) * inv;
       const float scale = fmaxf(1.f, amax);
       const float k = inv / scale;
       if (!ok) continue;
@@ -609,7 +609,7 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
   constexpr int DT = D / 32, DCH = D / 8;
   const int lane = threadIdx.x & 63;
   const int rows = a.T * a.G;
-  const float ltot = l + __shfl_xor(l, 32);
+  const float ltot = halves_sum(l);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const float lse = ltot > 0.f ? (mref + __log2f(ltot)) * kLn2 : -INFINITY;
   const bool part = a.n_splits > 1;
@@ -620,7 +620,7 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[0][dt][i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+    amax = halves_max(amax) * inv;
     scale = fmaxf(1.f, amax);
     k = inv / scale;
   }
