@@ -111,16 +111,27 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[QT][NST], const bf16x8 (
 #pragma unroll
     for (int t = 0; t < QT; ++t) s[t][st] = f32x16{};
   // With two subtiles they alternate, so consecutive products accumulate into different
-  // registers and do not wait on each other; each K fragment is read one product ahead.
-  bf16x8 kf = kfrag(0, 0);
+  // registers and do not wait on each other.  Each K fragment is read four products ahead:
+  // the scheduling groups below keep that order (left to itself the scheduler put each
+  // read one product ahead and waited for it).
+  constexpr int AHEAD = 4;
+  bf16x8 kf[AHEAD];
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) kf[i] = kfrag(i % NST, i / NST);
 #pragma unroll
   for (int i = 0; i < NST * KS; ++i) {
     const int st = i % NST, ks = i / NST;
-    const bf16x8 cur = kf;
-    if (i + 1 < NST * KS) kf = kfrag((i + 1) % NST, (i + 1) / NST);
+    const bf16x8 cur = kf[i % AHEAD];
+    if (i + AHEAD < NST * KS) kf[i % AHEAD] = kfrag((i + AHEAD) % NST, (i + AHEAD) / NST);
 #pragma unroll
     for (int t = 0; t < QT; ++t)
       s[t][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[t][ks], s[t][st], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);     // LDS reads
+#pragma unroll
+  for (int i = 0; i < NST * KS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);      // matrix products
+    if (i + AHEAD < NST * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
 
