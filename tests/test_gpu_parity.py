@@ -162,6 +162,28 @@ def test_attention_full_long_context_sampled_heads():
     check_attention(inp, heads=[0, 9, 18, 27, 36, 45, 54, 63])
 
 
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64, 256])
+def test_attention_paged_page_sizes(bs):
+    """Pages of 1 and 2 tokens take the slot-by-slot tile fetch; pages of 4 or more the
+    per-instruction one (each four-slot piece of a tile lies in one page), including
+    pages longer than a 64-key tile.  GQA 64/8 with short splits: the 128-row key-split
+    workgroups."""
+    check_attention(generate(scaled(C4, B=2, L=(300, 1500), V=64, block_size=bs),
+                             with_logits=False))
+
+
+@pytest.mark.parametrize("bs", [4, 256])
+def test_attention_paged_page_sizes_long_splits(bs):
+    """As above with splits of more than 16 tiles: 256-row eight-wavefront workgroups,
+    32 of them per split (8 splits, read off the workspace size)."""
+    inp = generate(scaled(C4, B=2, L=(9000, 12000), V=64, block_size=bs), with_logits=False)
+    dev = to_device(inp)
+    kv = ev.KvCache(dev.k, dev.v, dev.block_table)
+    rows = 2 * C4.T * C4.Hq                     # B = 2
+    assert ev.ev_tree_attention_workspace(kv, 2, C4.T, C4.Hq, max_prefix(inp)) == rows * 8 * (2 * C4.d + 8)
+    check_attention(inp)
+
+
 def check_attention_dev(inp, kv, dev, seqs=None, heads=None):
     """Attention on an already-built device cache (same logical contents as inp) against
     the oracle on inp."""
