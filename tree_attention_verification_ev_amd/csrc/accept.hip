@@ -107,7 +107,7 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
 #pragma unroll
       for (int e = 0; e < 4; ++e) ep[e] = exp_split(shifted(lv[h + e], inv_tau, M));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tj[e] = tab[ep[e].k & 63];
+      for (int e = 0; e < 4; ++e) tj[e] = tab[exp_slot(ep[e].k)];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const double pe = exp_join(ep[e], tj[e]) * inv_S;
@@ -311,7 +311,7 @@ __device__ inline void publish_stat(const AcceptArgs &a, int64_t row, int chunk,
 // flight while the current one is reduced.
 template <bool REJ, int CPW, bool VEC>
 __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   __shared__ int s_last;
   args_in_sgprs(a.n_chunks, a.T, a.V, a.logits, a.parent, a.tokens, a.uniforms, a.inv_tau,
                 a.stats, a.row_cnt);
@@ -630,7 +630,7 @@ __device__ bool sampled_decide(const SampledArgs &a, int64_t row, const SampledR
 template <int CPW, bool VEC>
 __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
   constexpr int XB = 4;                  // exp table reads issued 4 at a time
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   __shared__ int s_last;
   fill_exp_table(tab);
   const int lane = threadIdx.x & 63;
@@ -749,7 +749,7 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
 // logits for the residual mass at its current shift; its last workgroup then decides.
 template <int CPW>
 __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   __shared__ int s_last;
   const int64_t row = blockIdx.y;
   const SampledRow st = a.state[row];    // written by an earlier launch

@@ -34,6 +34,8 @@
 namespace ev {
 
 constexpr int kTreeTop = 8;            // most children per node, widest beam
+// the float64 exp's table: 64 entries (small, latency-bound launches; see rowstream.h)
+constexpr int kTreeExpBits = 6;
 constexpr int kMaxExpansions = 16;     // deepest tree under construction
 constexpr int kCandSlots = 64;         // candidates per depth: kTreeTop frontier x kTreeTop
 
@@ -242,7 +244,7 @@ __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, M
     double S = 0.0, T = 0.0, xf[kChunkRegs], ef[kChunkRegs];
 #pragma unroll
     for (int r = 0; r < kChunkRegs; ++r) xf[r] = cs[r].M - M;
-    exp_nonpos_n(xf, ef, tab);
+    exp_nonpos_n<kChunkRegs, kTreeExpBits>(xf, ef, tab);
 #pragma unroll
     for (int r = 0; r < kChunkRegs; ++r) {
       if (cs[r].S > 0.0) {
@@ -253,7 +255,7 @@ __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, M
     }
     S = wave_sum(S);
     T = wave_sum(T);
-    const double ppl = S / exp_nonpos(T / S, tab);
+    const double ppl = S / exp_nonpos<kTreeExpBits>(T / S, tab);
     const double half_up = ppl + 0.5;
     const int k = half_up >= (double)a.k_max ? a.k_max : max(1, (int)floor(half_up));
     // the k chunks whose maxima rank first (k rounds over the lanes' chunk maxima); the
@@ -326,7 +328,7 @@ __device__ void merge_row(const ExpandArgs &a, int64_t row, const double *tab, M
   if (lane == 0) publish(&out->k, k);
   if (real && rank < k) {
     publish(&out->tok[rank], me.idx);
-    publish(&out->q[rank], exp_nonpos(shifted(me.val, a.inv_tau, sh.M), tab) / sh.S);
+    publish(&out->q[rank], exp_nonpos<kTreeExpBits>(shifted(me.val, a.inv_tau, sh.M), tab) / sh.S);
   }
   if (lane < kTreeTop && lane >= min(k, n_real)) {
     if (lane < k) report(a.dev_status, EV_DERR_TOKEN);   // only NaN logits: too few tokens
@@ -395,12 +397,12 @@ __device__ void expand_sequence(const ExpandArgs &a, int b, int count, double *s
 // Streaming launch: one 1024-logit chunk per wavefront per step.
 template <int CPW>
 __global__ __launch_bounds__(256) void tree_chunk_kernel(ExpandArgs a) {
-  __shared__ double tab[64];
+  __shared__ double tab[1 << kTreeExpBits];
   const int64_t row = blockIdx.y;
   const int b = (int)(row / a.W), w = (int)(row % a.W);
   const int count = a.depth == 0 ? 1 : a.front_in[b].count;   // written by the last depth
   if (w >= count) return;              // unused frontier slot
-  fill_exp_table(tab);
+  fill_exp_table<kTreeExpBits>(tab);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nc = a.n_chunks;
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(256) void tree_chunk_kernel(ExpandArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const double d = shifted(v[e], a.inv_tau, M);
-      const double ex = exp_nonpos(d, tab);
+      const double ex = exp_nonpos<kTreeExpBits>(d, tab);
       S += ex;
       T += d >= -745.0 ? ex * d : 0.0;  // e * d -> 0 as d -> -inf (padding, -inf logits)
     }
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256) void tree_chunk_kernel(ExpandArgs a) {
 // Merge launch: one workgroup per frontier row; the workgroup that completes a
 // sequence's frontier forms its candidates and the next beam.
 __global__ __launch_bounds__(kMergeThreads) void tree_merge_kernel(ExpandArgs a) {
-  __shared__ double tab[64];
+  __shared__ double tab[1 << kTreeExpBits];
   __shared__ int s_last;
   __shared__ MergeShared sh;
   __shared__ double s_rank[64];
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(kMergeThreads) void tree_merge_kernel(ExpandArgs a)
   const int b = (int)(row / a.W), w = (int)(row % a.W);
   const int count = a.depth == 0 ? 1 : a.front_in[b].count;
   if (w >= count) return;
-  fill_exp_table(tab);
+  fill_exp_table<kTreeExpBits>(tab);
   __syncthreads();
   merge_row(a, row, tab, sh);
   if (!last_arrival(&a.seq_cnt[counter_slot(b)], count, &s_last)) return;

@@ -32,54 +32,78 @@ struct RejStat {
 __host__ __device__ inline int n_chunks_of(int V) { return (V + kChunk - 1) / kChunk; }
 
 // exp(x) for x <= 0 in float64 by the table-driven method of P. T. P. Tang (ACM TOMS 15(2),
-// 1989): x = (64 m + j) ln2/64 + r with |r| <= ln2/128, exp(x) = 2^m 2^(j/64) exp(r), the
-// last factor by its Taylor polynomial to r^5 (truncation below 4e-17).  tab[j] = 2^(j/64).
-// The nearest integer to 64 x / ln2 comes from adding and removing 1.5 * 2^52, whose low
-// word then holds it as a two's-complement integer.  Arguments below -745 (results below
-// the smallest subnormal) are clamped there, so they return at most 5e-324.
-// The method in two halves, so that a caller can issue the table reads of several
-// arguments before it combines any of them (each read is an LDS round trip):
-// exp_nonpos(x) = exp_join(exp_split(x), tab[k & 63]).
+// 1989): x = (N m + j) ln2/N + r with |r| <= ln2/(2N), exp(x) = 2^m 2^(j/N) exp(r), the
+// last factor by its Taylor polynomial: to r^4 with N = 256 (kExpTabBits 8), to r^5 with
+// N = 64 (6); truncation below 4e-17 either way.  tab[j] = 2^(j/N).  The larger table saves
+// a float64 FMA per argument (the statistics streams: acceptance 3-5 % faster); filling it
+// costs every wavefront of a workgroup an exp2, which the small latency-bound draft-tree
+// launches feel more (2.5 % slower with it), so they keep N = 64.  The nearest integer to
+// N x / ln2 comes from adding and removing 1.5 * 2^52, whose low word then holds it as a
+// two's-complement integer.  Arguments below -745 (results below the smallest subnormal)
+// are clamped there, so they return at most 5e-324.  The method in two halves, so that a
+// caller can issue the table reads of several arguments before it combines any of them
+// (each read is an LDS round trip): exp_nonpos(x) = exp_join(exp_split(x), tab[exp_slot(k)]).
+constexpr int kExpTabBits = 8;                 // the acceptance kernels' table
+constexpr int kExpTab = 1 << kExpTabBits;
+template <int TB> struct ExpReduction;
+template <> struct ExpReduction<8> {
+  static constexpr double kInvLn2xN = 369.3299304675746;     // 256 / ln 2
+  static constexpr double kLn2dNHi = 0.0027076061740622863;  // ln2/256 rounded to double
+  static constexpr double kLn2dNLo = 9.058776616587108e-20;  // ln2/256 - kLn2dNHi
+};
+template <> struct ExpReduction<6> {
+  static constexpr double kInvLn2xN = 92.33248261689366;     // 64 / ln 2
+  static constexpr double kLn2dNHi = 0.010830424696249145;   // ln2/64 rounded to double
+  static constexpr double kLn2dNLo = 3.623510646634843e-19;  // ln2/64 - kLn2dNHi
+};
 struct ExpParts {
   double p;                                                   // exp(r) - 1
   int k;                                                      // 64 m + j
 };
+template <int TB = kExpTabBits>
 __device__ inline ExpParts exp_split(double x) {
-  constexpr double kInvLn2x64 = 92.33248261689366;            // 64 / ln 2
-  constexpr double kLn2d64Hi = 0.010830424696249145;          // ln2/64 rounded to double
-  constexpr double kLn2d64Lo = 3.623510646634843e-19;         // ln2/64 - kLn2d64Hi
+  using R = ExpReduction<TB>;
   constexpr double kShifter = 6755399441055744.0;             // 1.5 * 2^52
   x = fmax(x, -745.0);
-  const double t = fma(x, kInvLn2x64, kShifter);
+  const double t = fma(x, R::kInvLn2xN, kShifter);
   const double kf = t - kShifter;
   const int k = (int)(uint32_t)__double_as_longlong(t);
-  double r = fma(-kf, kLn2d64Hi, x);
-  r = fma(-kf, kLn2d64Lo, r);
-  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-  p = fma(r, p, 1.0 / 6.0);
+  double r = fma(-kf, R::kLn2dNHi, x);
+  r = fma(-kf, R::kLn2dNLo, r);
+  double p;
+  if constexpr (TB >= 8) {
+    p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+  } else {
+    p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+    p = fma(r, p, 1.0 / 6.0);
+  }
   p = fma(r, p, 0.5);
   p = fma(r, p, 1.0);
   return ExpParts{p * r, k};
 }
+template <int TB = kExpTabBits>
+__device__ inline int exp_slot(int k) { return k & ((1 << TB) - 1); }
+template <int TB = kExpTabBits>
 __device__ inline double exp_join(ExpParts e, double tj) {
-  return ldexp(fma(tj, e.p, tj), e.k >> 6);
+  return ldexp(fma(tj, e.p, tj), e.k >> TB);
 }
+template <int TB = kExpTabBits>
 __device__ inline double exp_nonpos(double x, const double *tab) {
-  const ExpParts e = exp_split(x);
-  return exp_join(e, tab[e.k & 63]);
+  const ExpParts e = exp_split<TB>(x);
+  return exp_join<TB>(e, tab[exp_slot<TB>(e.k)]);
 }
 // exp_nonpos of N arguments, their table reads issued together.
-template <int N>
+template <int N, int TB = kExpTabBits>
 __device__ __forceinline__ void exp_nonpos_n(const double (&x)[N], double (&y)[N],
                                              const double *tab) {
   ExpParts ep[N];
   double tj[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) ep[i] = exp_split(x[i]);
+  for (int i = 0; i < N; ++i) ep[i] = exp_split<TB>(x[i]);
 #pragma unroll
-  for (int i = 0; i < N; ++i) tj[i] = tab[ep[i].k & 63];
+  for (int i = 0; i < N; ++i) tj[i] = tab[exp_slot<TB>(ep[i].k)];
 #pragma unroll
-  for (int i = 0; i < N; ++i) y[i] = exp_join(ep[i], tj[i]);
+  for (int i = 0; i < N; ++i) y[i] = exp_join<TB>(ep[i], tj[i]);
 }
 // sum of exp_nonpos(x(e)), e = 0 .. N-1 in order, the table reads of every XB arguments
 // issued before any of them is used (with XB = 1, one read at a time, each waited for
@@ -95,7 +119,7 @@ __device__ __forceinline__ double exp_sum(F x, const double *tab) {
 #pragma unroll
     for (int e = 0; e < XB; ++e) ep[e] = exp_split(x(h + e));
 #pragma unroll
-    for (int e = 0; e < XB; ++e) tj[e] = tab[ep[e].k & 63];
+    for (int e = 0; e < XB; ++e) tj[e] = tab[exp_slot(ep[e].k)];
 #pragma unroll
     for (int e = 0; e < XB; ++e) sum += exp_join(ep[e], tj[e]);
   }
@@ -304,9 +328,13 @@ __device__ inline double wave_max(double x) {
   return lane_d(x, 63);
 }
 
-// 2^(j/64), j < 64, into LDS (one entry per thread of the first wavefront).
+// 2^(j/N), j < N = 2^TB, into LDS, one entry per thread (every workgroup that calls it
+// has at least 256 threads; a loop over blockDim made each launch fetch the dispatch
+// packet first).
+template <int TB = kExpTabBits>
 __device__ inline void fill_exp_table(double *tab) {
-  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+  constexpr int N = 1 << TB;
+  if (threadIdx.x < N) tab[threadIdx.x] = exp2((double)threadIdx.x / N);
 }
 
 // Data handed from one workgroup to another within a launch (chunk statistics, node
