@@ -35,9 +35,8 @@ __host__ __device__ inline int n_chunks_of(int V) { return (V + kChunk - 1) / kC
 // 1989): x = (N m + j) ln2/N + r with |r| <= ln2/(2N), exp(x) = 2^m 2^(j/N) exp(r), the
 // last factor by its Taylor polynomial: to r^4 with N = 256 (kExpTabBits 8), to r^5 with
 // N = 64 (6); truncation below 4e-17 either way.  tab[j] = 2^(j/N).  The larger table saves
-// a float64 FMA per argument (the statistics streams: acceptance 3-5 % faster); filling it
-// costs every wavefront of a workgroup an exp2, which the small latency-bound draft-tree
-// launches feel more (2.5 % slower with it), so they keep N = 64.  The nearest integer to
+// a float64 FMA per argument (the statistics streams: acceptance 3-5 % faster); the small
+// latency-bound draft-tree launches were 2.5 % slower with it, so they keep N = 64.  The nearest integer to
 // N x / ln2 comes from adding and removing 1.5 * 2^52, whose low word then holds it as a
 // two's-complement integer.  Arguments below -745 (results below the smallest subnormal)
 // are clamped there, so they return at most 5e-324.  The method in two halves, so that a
@@ -58,7 +57,7 @@ template <> struct ExpReduction<6> {
 };
 struct ExpParts {
   double p;                                                   // exp(r) - 1
-  int k;                                                      // 64 m + j
+  int k;                                                      // 2^TB m + j
 };
 template <int TB = kExpTabBits>
 __device__ inline ExpParts exp_split(double x) {
