@@ -635,46 +635,67 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
     scale = fmaxf(1.f, amax);
     k = inv / scale;
   }
-  // this lane's values: row qn, head dims dt*32 + 8j + 4hh + 0..3 = half hh of chunk 4dt + j
+  // The partial / final choice is made once, outside the loops, the eight row reads go
+  // out before the first store, and the output rows are stepped rather than divided out
+  // per row: one wavefront does all of this after the last tile, so its branches, LDS
+  // round trips and integer divisions were the call's tail (2.3 -> 1.8 us per wave, 26- and
+  // 128-row workgroups; 16.5 -> 15.9 us per call with 32 MHA heads x 26 rows).
+  auto store = [&](auto is_part) {
+    constexpr bool P = decltype(is_part)::value;
+    using H = typename std::conditional<P, f16x4, bf16x4>::type;
+    using E = typename std::conditional<P, _Float16, __bf16>::type;
+    // this lane's values: row qn, head dims dt*32 + 8j + 4hh + 0..3 = half hh of chunk 4dt + j
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16 &ov = o[0][dt];
-      uint32_t w0, w1;
-      if (part) {
-        const f16x4 h = f16x4{(_Float16)(ov[4 * j] * k), (_Float16)(ov[4 * j + 1] * k),
-                              (_Float16)(ov[4 * j + 2] * k), (_Float16)(ov[4 * j + 3] * k)};
-        w0 = __builtin_bit_cast(u32x2, h)[0];
-        w1 = __builtin_bit_cast(u32x2, h)[1];
-      } else {
-        const bf16x4 h = bf16x4{(__bf16)(ov[4 * j] * k), (__bf16)(ov[4 * j + 1] * k),
-                                (__bf16)(ov[4 * j + 2] * k), (__bf16)(ov[4 * j + 3] * k)};
-        w0 = __builtin_bit_cast(u32x2, h)[0];
-        w1 = __builtin_bit_cast(u32x2, h)[1];
+      for (int j = 0; j < 4; ++j) {
+        const f32x16 &ov = o[0][dt];
+        const H h = H{(E)(ov[4 * j] * k), (E)(ov[4 * j + 1] * k), (E)(ov[4 * j + 2] * k),
+                      (E)(ov[4 * j + 3] * k)};
+        const int pc = (4 * dt + j) ^ (qn & 15);
+        *(u32x2 *)(stage + qn * D + pc * 8 + 4 * hh) = __builtin_bit_cast(u32x2, h);
       }
-      const int pc = (4 * dt + j) ^ (qn & 15);
-      *(u32x2 *)(stage + qn * D + pc * 8 + 4 * hh) = u32x2{w0, w1};
-    }
-  // whole rows back out: lane takes row 4i + lane/16, chunk lane%16
+    // whole rows back out, all read before the first store: lane takes row 4i + lane/16,
+    // chunk lane%16
+    constexpr int NI = 32 * DCH / 64;
+    const int cc = lane & 15;
+    u32x4 v[NI];
 #pragma unroll
-  for (int i = 0; i < 32 * DCH / 64; ++i) {
-    const int rr = 4 * i + (lane >> 4), cc = lane & 15;
-    const int r = row0 + rr;
-    const u32x4 v = *(const u32x4 *)(stage + rr * D + ((cc ^ (rr & 15)) << 3));
-    if (r < rows) {
-      const int64_t orow = out_row(a, b, g, r);
-      if (part) {
-        u32x4 *dst = (u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8);
-        if constexpr (NT)
-          __builtin_nontemporal_store(v, dst);
-        else
-          *dst = v;
-      } else {
-        *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = v;
+    for (int i = 0; i < NI; ++i) {
+      const int rr = 4 * i + (lane >> 4);
+      v[i] = *(const u32x4 *)(stage + rr * D + ((cc ^ (rr & 15)) << 3));
+    }
+    // output row of query row r = node * G + m, stepped four rows at a time
+    int r = row0 + (lane >> 4);
+    int node = r / a.G, m = r % a.G;
+    const int dnode = 4 / a.G, dm = 4 % a.G;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (r < rows) {
+        const int64_t orow = ((int64_t)b * a.T + node) * a.Hq + g * a.G + m;
+        if constexpr (P) {
+          u32x4 *dst = (u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8);
+          if constexpr (NT)
+            __builtin_nontemporal_store(v[i], dst);
+          else
+            *dst = v[i];
+        } else {
+          *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = v[i];
+        }
+      }
+      r += 4;
+      node += dnode;
+      m += dm;
+      if (m >= a.G) {
+        m -= a.G;
+        ++node;
       }
     }
-  }
+  };
+  if (part)
+    store(std::true_type{});
+  else
+    store(std::false_type{});
   const int r = row0 + qn;
   if (hh == 0 && r < rows) {
     const int64_t orow = out_row(a, b, g, r);
