@@ -706,6 +706,132 @@ __device__ __forceinline__ void write_rows_staged(const AttnArgs &a, const f32x1
   }
 }
 
+// The end of a key-split group: wavefront kh holds the online-softmax state (reference
+// max m, partial sums l, accumulators o) of its half of every tile's keys, for all 32 rows
+// and all head dimensions.  Each finishes half of the head dimensions (dt = 2kh, 2kh + 1):
+// it hands the other half, with m, l and its max |o|, to its partner through `xch`, takes
+// the partner's values for its own dimensions, and writes the combined, normalised values
+// into the group's 32 staging rows (`stage`, chunk-swizzled like a K tile); after a
+// barrier each stores 16 of the 32 rows whole.  Both compute the row scalars in the same
+// order, so they agree bit for bit.  A split partial's divisor is max(1, bound) with the
+// bound a0 max|o_0| + a1 max|o_1| over the row sum, which is at least the row's max |O|,
+// so the fp16 row cannot overflow.  Every wavefront of the workgroup calls this (it holds
+// two barriers).  KH is a template argument so that the accumulators are only ever indexed
+// by constants (a run-time index put them in scratch memory).
+template <int D, bool NT, int KH>
+__device__ __forceinline__ void finish_pair(const AttnArgs &a, const f32x16 (&o)[1][D / 32],
+                                            float m, float l, int row0, int b, int g,
+                                            int split, int qn, int hh, float *xch,
+                                            uint16_t *stage) {
+  constexpr int kh = KH;
+  constexpr int DT = D / 32, DH = DT / 2, DCH = D / 8;
+  constexpr int XF = 3 + DH * 16;                // floats one wavefront hands over per lane
+  const int lane = threadIdx.x & 63;
+  const int rows = a.T * a.G;
+  const bool part = a.n_splits > 1;
+  float am = 0.f;
+  if (part) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(o[0][dt][i]));
+    am = halves_max(am);
+  }
+  float *mine = xch + kh * XF * 64;
+  const float *theirs = xch + (1 - kh) * XF * 64;
+  mine[lane] = m;
+  mine[64 + lane] = l;
+  mine[128 + lane] = am;
+#pragma unroll
+  for (int h = 0; h < DH; ++h)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mine[(3 + h * 16 + i) * 64 + lane] = o[0][(1 - kh) * DH + h][i];
+  __syncthreads();
+  const float m2 = theirs[lane], l2 = theirs[64 + lane], am2 = theirs[128 + lane];
+  const float m0 = kh == 0 ? m : m2, m1 = kh == 0 ? m2 : m;
+  const float l0 = kh == 0 ? l : l2, l1 = kh == 0 ? l2 : l;
+  const float am0 = kh == 0 ? am : am2, am1 = kh == 0 ? am2 : am;
+  const float mnew = fmaxf(m0, m1);
+  const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mnew);
+  const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mnew);
+  const float ltot = halves_sum(l0 * a0 + l1 * a1);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const float lse = ltot > 0.f ? (mnew + __log2f(ltot)) * kLn2 : -INFINITY;
+  float k = inv, scale = 1.f;
+  if (part) {
+    scale = fmaxf(1.f, (a0 * am0 + a1 * am1) * inv);
+    k = inv / scale;
+  }
+  const float km = k * (kh == 0 ? a0 : a1), kt = k * (kh == 0 ? a1 : a0);
+  auto store = [&](auto is_part) {
+    constexpr bool P = decltype(is_part)::value;
+    using H = typename std::conditional<P, f16x4, bf16x4>::type;
+    using E = typename std::conditional<P, _Float16, __bf16>::type;
+    // this lane's values: row qn, head dims dt*32 + 8j + 4hh + 0..3 = half hh of chunk 4dt + j
+#pragma unroll
+    for (int h = 0; h < DH; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int dt = kh * DH + h;
+        const f32x16 &ov = o[0][dt];
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = fmaf(ov[4 * j + e], km, theirs[(3 + h * 16 + 4 * j + e) * 64 + lane] * kt);
+        const H hv = H{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
+        const int pc = (4 * dt + j) ^ (qn & 15);
+        *(u32x2 *)(stage + qn * D + pc * 8 + 4 * hh) = __builtin_bit_cast(u32x2, hv);
+      }
+    __syncthreads();                             // both halves of every row staged
+    // rows 16kh .. 16kh + 15 back out whole: lane takes row 16kh + 4i + lane/16, chunk lane%16
+    constexpr int NI = 32 * DCH / 64 / 2;
+    const int cc = lane & 15;
+    u32x4 w[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int rr = 16 * kh + 4 * i + (lane >> 4);
+      w[i] = *(const u32x4 *)(stage + rr * D + ((cc ^ (rr & 15)) << 3));
+    }
+    int r = row0 + 16 * kh + (lane >> 4);
+    int node = r / a.G, mm = r % a.G;
+    const int dnode = 4 / a.G, dm = 4 % a.G;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (r < rows) {
+        const int64_t orow = ((int64_t)b * a.T + node) * a.Hq + g * a.G + mm;
+        if constexpr (P) {
+          u32x4 *dst = (u32x4 *)(a.part_o + part_row(a, orow, split) * D + cc * 8);
+          if constexpr (NT)
+            __builtin_nontemporal_store(w[i], dst);
+          else
+            *dst = w[i];
+        } else {
+          *(u32x4 *)((__bf16 *)a.out + orow * D + cc * 8) = w[i];
+        }
+      }
+      r += 4;
+      node += dnode;
+      mm += dm;
+      if (mm >= a.G) {
+        mm -= a.G;
+        ++node;
+      }
+    }
+  };
+  if (part)
+    store(std::true_type{});
+  else
+    store(std::false_type{});
+  const int r = row0 + qn;
+  if (kh == 0 && hh == 0 && r < rows) {
+    const int64_t orow = out_row(a, b, g, r);
+    if (part)
+      a.part_ls[part_row(a, orow, split)] = pack_ls(lse, scale);
+    else
+      a.lse[orow] = lse;
+  }
+}
+
 // Direct-to-LDS tree attention kernel, head_dim 128.  Without KSPLIT: NW wavefronts of 32
 // query rows each.  KSPLIT: NW / 2 groups of 32 rows, two wavefronts per group (one per
 // 32-key half of every tile, so each scores and accumulates half the keys), the halves
@@ -1055,42 +1181,27 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // flight.  Those two stages hold the waves' output rows (8 KB each).
   const int last = (t_end - 1 - t_begin) % kStages;
   if constexpr (KSPLIT) {
-    // the second wave of each group hands its half (reference max, partial sum,
-    // accumulators) to the first, element-major so the accesses are conflict-free: with
-    // one group through the second free stage, with four (66 KB) through stages 0-2 once
-    // every wave is past its last tile
+    // exchange areas: with one group the two stages after the last tile's (no wave reads
+    // them any more); with four (72 KB), stages 0-2 once every wave is past its last tile;
+    // the staging rows of the groups follow in stage 3
     float *xch;
+    uint16_t *gstage;
     if constexpr (NW == 2) {
       xch = (float *)(lds + ((last + 2) % kStages) * 2 * MAT);
+      gstage = (uint16_t *)(lds + ((last + 1) % kStages) * 2 * MAT);
     } else {
       __syncthreads();
-      xch = (float *)lds + rg * (2 + DT * 16) * 64;
+      xch = (float *)lds + rg * 2 * (3 + DT / 2 * 16) * 64;
+      gstage = (uint16_t *)(lds + 3 * 2 * MAT + rg * 32 * D);
     }
-    if (kh == 1) {
-      xch[lane] = mref[0];
-      xch[64 + lane] = l[0];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) xch[(2 + dt * 16 + i) * 64 + lane] = o[0][dt][i];
-    }
-    __syncthreads();
-    if (kh == 1) return;
-    const float m1 = xch[lane], l1 = xch[64 + lane];
-    const float mnew = fmaxf(mref[0], m1);
-    const float a0 = mref[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[0] - mnew);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mnew);
-    l[0] = l[0] * a0 + l1 * a1;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[0][dt][i] = o[0][dt][i] * a0 + xch[(2 + dt * 16 + i) * 64 + lane] * a1;
-    mref[0] = mnew;
+    if (__builtin_amdgcn_readfirstlane(kh) == 0)
+      finish_pair<D, RG * 32 >= 128, 0>(a, o, mref[0], l[0], row0, b, g, split, qn, hh, xch, gstage);
+    else
+      finish_pair<D, RG * 32 >= 128, 1>(a, o, mref[0], l[0], row0, b, g, split, qn, hh, xch, gstage);
+    return;
   }
-  uint16_t *stage = KSPLIT && NW == 8
-                        ? (uint16_t *)(lds + 3 * 2 * MAT + rg * 32 * D)   // past the exchange
-                        : (uint16_t *)(lds + ((last + 1 + (wave >> 2)) % kStages) * 2 * MAT +
-                                       (wave & 3) * 32 * D);
+  uint16_t *stage = (uint16_t *)(lds + ((last + 1 + (wave >> 2)) % kStages) * 2 * MAT +
+                                 (wave & 3) * 32 * D);
   // Partial rows go non-temporally from workgroups of 128 rows or more; a split plan of
   // smaller workgroups writes at most 256 x 64 partial rows (4 MB), which stay cached
   // (measured: 8 MB of partials, 8 splits of 4096 rows, 22.3 us per call non-temporal
