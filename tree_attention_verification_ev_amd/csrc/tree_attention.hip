@@ -1131,8 +1131,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
       if constexpr (!PAGED)
         if (j == t_begin) fix_tail(j + 1, NEXT::value);   // the second early tile
       wg_barrier();                              // tile j+1 visible; stage of j-1 free
-      if (j + 3 < t_end) issue(j + 3, REFILL::value, ids);
-      scores_of(sn, NEXT{});
+      // A contiguous cache issues the next tile's score products before the refill DMA
+      // (GQA 64/8 L=4096: 19.61 -> 19.35 us per call).  With a paged cache that order
+      // made the compiler wait for the refill before the V reads of every step.
+      if constexpr (PAGED) {
+        if (j + 3 < t_end) issue(j + 3, REFILL::value, ids);
+        scores_of(sn, NEXT{});
+      } else {
+        scores_of(sn, NEXT{});
+        if (j + 3 < t_end) issue(j + 3, REFILL::value, ids);
+      }
     }
     if (j * kKT + kKT > L) tile_mask(sc, anc_q, j * kKT + st0 * 32, L, hh);
     tile_rescale(sc, o, mref, l, a.scale_log2);
