@@ -187,24 +187,12 @@ ev_status ev_accept_greedy(const float *logits, const int32_t *tokens, const int
  *   no child is accepted the emitted token is drawn from the residual distribution by
  *   inverse CDF in ascending token id with t = uniforms[b][0] * Z.
  *   uniforms [B][T] double in [0, 1).  Outputs as for ev_accept_greedy.
- *   EV_ERR_ARG unless temperature is finite and > 0.
- *   The row sums are first taken with float32 exponentials together with a bound on their
- *   error.  A decision whose float64 outcome that bound cannot fix (a test with
- *   |u Z - p| or a draw with t within about 1e-6 of an edge) is recomputed from float64
- *   statistics of that row.  The results are those of the float64 definition above
- *   whenever its decisions are not rounding ties (margins well above 1e-13). */
+ *   EV_ERR_ARG unless temperature is finite and > 0. */
 ev_status ev_accept_rejection(const float *logits, const int32_t *tokens, const int32_t *parent,
                               int32_t B, int32_t T, int32_t V, float temperature,
                               const double *uniforms,
                               int32_t *accept_len, int32_t *path, int32_t *out_tokens,
                               void *ws, size_t ws_bytes, int32_t *dev_status, hipStream_t stream);
-
-/* (host) Scale of the margins within which ev_accept_rejection takes a decision from its
- * float32 statistics; the default is 1.  A larger scale sends more nodes through the
- * float64 recomputation.  A huge one (for example 1e300) sends every node the walk
- * visits, which tests use to check that path.  Values that are not > 0 leave the scale
- * unchanged.  Returns the previous scale.  Process-wide; it takes effect for later calls. */
-double ev_accept_set_bound_scale(double scale);
 
 /* Bytes of workspace ev_accept_sampled needs (same limits and zero-fill contract as the
  * acceptance workspace above). */

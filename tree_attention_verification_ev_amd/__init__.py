@@ -33,7 +33,7 @@ EXPORTED = (
     "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
     "ev_tree_attention_noalloc", "ev_tree_attention_noalloc_limit",
     "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection",
-    "ev_accept_set_bound_scale", "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact",
+    "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact",
     "ev_kv_compact_remap_workspace", "ev_kv_compact_remap",
     "ev_draft_tree_workspace", "ev_draft_tree_expand", "ev_draft_tree_finalize",
     "ev_status_string",
@@ -84,7 +84,6 @@ def lib() -> ctypes.CDLL:
             "ev_accept_greedy": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_rejection": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _P,
                                            _SZ, _P, _P]),
-            "ev_accept_set_bound_scale": (ctypes.c_double, [ctypes.c_double]),
             "ev_accept_sampled_workspace": (_SZ, [_I32, _I32, _I32]),
             "ev_accept_sampled": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _I32,
                                          _P, _P, _P, _P, _SZ, _P, _P]),
@@ -302,11 +301,6 @@ def ev_tree_attention_noalloc_limit() -> int:
 
 def ev_accept_workspace(B: int, T: int, V: int) -> int:
     return int(lib().ev_accept_workspace(B, T, V))
-
-
-def ev_accept_set_bound_scale(scale: float) -> float:
-    """Scale of the certification margins of ev_accept_rejection; returns the previous one."""
-    return float(lib().ev_accept_set_bound_scale(float(scale)))
 
 
 def _accept_outputs(B, T, dev, accept_len, path, out_tokens):

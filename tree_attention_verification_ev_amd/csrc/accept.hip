@@ -12,27 +12,23 @@
 // row, its children's draft tokens and their uniforms — not on how the walk got there.  So
 // everything happens in ONE launch over (row = node, 1024-logit chunk) wavefronts:
 //   * each wavefront streams its chunk of float32 logits once and stores the chunk's
-//     statistics — greedy: (max, lowest argmax); rejection: the chunk's largest logit,
-//     S_c = sum 2^((logit - max) log2(e)/tau) by the float32 exponential, and a bound on
-//     that sum's error (see "Rejection statistics in float32" below);
+//     statistics — greedy: (max, lowest argmax); rejection: float64 (M_c = max s,
+//     S_c = sum exp(s - M_c)), s = logit/tau;
 //   * the workgroup that completes a row's last chunk (a device-scope counter per row)
 //     reduces the row and settles that node's outcome: its argmax / accepted child,
 //     residual mass, rejected children and their probabilities;
 //   * the workgroup that completes a sequence's last row (a counter per sequence) follows
-//     accepted children from the root and emits the bonus token of the last node (greedy:
+//     accepted children from the root and draws the bonus token at the last node (greedy:
 //     its argmax; rejection: the residual inverse CDF, located through the chunk masses,
-//     then one 1024-logit chunk scanned in float64).  A rejection node whose decisions the
-//     float32 statistics could not settle is recomputed there, in float64, if the walk
-//     reaches it.
+//     then one 1024-logit chunk scanned in float64).
 // The counters live in the caller's workspace, which must be zero-filled before its first
 // use; every call leaves them at zero again.
 #include "ev_internal.h"
 #include "rowstream.h"
 
-#include <atomic>
 #include <limits.h>
-#include <math.h>
 #include <type_traits>
+#include <math.h>
 
 namespace ev {
 
@@ -42,8 +38,6 @@ struct AcceptArgs {
   const int32_t *parent;
   int B, T, V, n_chunks;
   double inv_tau;
-  float c32;                             // float(inv_tau * log2(e)): float32 exponent scale
-  double bound_scale;                    // multiplies the certification margins (1 normally)
   const double *uniforms;
   void *stats;                           // [B*T][n_chunks] chunk statistics
   int32_t *row_cnt;                      // [B*T] arrivals per row
@@ -59,56 +53,12 @@ __device__ inline uint64_t pack_node(int next, int bonus) {
   return (uint64_t)(uint32_t)next | ((uint64_t)(uint32_t)bonus << 32);
 }
 
-// ---------------------------------------------------------------------------------------
-// Rejection statistics in float32, with a certificate.
-//
-// The decisions are defined in float64 (see ev.h): p(y) = exp(s_y - M) / S.  Streaming
-// every logit through a float64 exp costs about as much vector time as reading the logits,
-// so the stream takes, per 1024-logit chunk with largest logit m_c,
-//   e_i = 2^(y_i),  y_i = (logit_i - m_c) * c32 in float32 (c32 = float(log2(e) / tau)),
-// by the float32 exponential, S_c = sum e_i (float32 sums of four, added in float64), and
-// E_c = sum e_i |y_i| (float32).  Against the exact exp((logit_i - m_c) / tau):
-//   * y_i carries three float32 roundings (the difference, c32, the product): its error is
-//     at most 3.02 * 2^-24 |y_i|, i.e. a relative error of at most 2.1 * 2^-24 |y_i| in e_i;
-//   * the exponential itself is within 1 ulp (2 * 2^-24 relative);
-//   * each sum of four adds at most 2 * 2^-24 of itself;
-//   * a term flushed or clamped below 2^-126 is off by at most that.
-// The bound takes twice the first (kErrY = 4.4 * 2^-24 per unit of |y|), three times the
-// second and third together (kErrS = 12 * 2^-24) and 2^-100 per term, so
-//   |S_c - exact| <= b_c = kErrY * E_c + kErrS * S_c + 1024 * 2^-100.
-// The row's S = sum S_c e^(M_c - M) then has an error of at most Err = sum b_c e^(M_c - M)
-// (plus 2^-40 S for the float64 work), i.e. a relative error r = Err / (S - Err).
-// A decision is taken from these sums only when it holds for every S within the bound:
-//   * child test u Z < p:  |u Z - p| > r (1 + r) (the rejected and tested tokens are
-//     distinct, so their probabilities add up to at most 1 + r);
-//   * bonus draw: the threshold, less the chunk masses before the crossing chunk, is off
-//     by at most Err / S = r; the drawn token's interval of the cumulative mass must
-//     contain it with that margin on both sides.
-// Both margins are scaled by AcceptArgs::bound_scale and padded by 1e-13 for the float64
-// rounding of the decision itself.  A node with a decision that fails its margin is marked
-// kUncertain; if the walk reaches it, the walk recomputes that row's chunk statistics in
-// float64 (exp by the table method, as ev.h defines them) and settles the node again.
-struct RejStatF {
-  float vmax;                            // largest logit of the chunk (-inf: no mass)
-  float E;                               // sum e_i |y_i|
-  double S;                              // sum e_i
-};
-static_assert(sizeof(RejStatF) == sizeof(RejStat), "one workspace layout for both");
-constexpr double kErrY = 4.4 / 16777216.0;                     // 2 x 2.2 * 2^-24 per |y|
-constexpr double kErrS = 12.0 / 16777216.0;                    // 3 x (2 + 2) * 2^-24
-constexpr double kErrTerm = 1024.0 * 7.888609052210118e-31;    // 1024 terms x 2^-100
-constexpr double kErrRow = 9.094947017729282e-13;              // 2^-40: float64 row sums
-constexpr double kErrDecision = 1e-13;
-constexpr int kUncertain = -3;           // node word: a decision needs the float64 path
-
-__device__ inline uint64_t pack_fe(float vmax, float E) {
-  return (uint64_t)__float_as_uint(vmax) | ((uint64_t)__float_as_uint(E) << 32);
-}
-
 // Inverse-CDF draw from the residual of a node, t = u0 * Z (one wavefront).  Rejected
 // tokens: lanes set in `rej` hold them in `tok` and their probabilities in `prej`.  The
 // chunk whose cumulative residual mass first exceeds t is found from the chunk statistics
 // (cs, strided as in row_stats_regs); that chunk is then scanned element by element.
+// Values of one lane at a wave-uniform index are read with readlane (a scalar-register
+// move), not a shuffle (an LDS round trip each); the settle and walk are chains of them.
 __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
                              const RejStat (&cs)[kChunkRegs], double M, double S,
                              uint64_t rej, int tok, double prej, double t, const double *tab) {
@@ -122,8 +72,8 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
   for (int r = 0; r < kChunkRegs; ++r) mass[r] = cs[r].S > 0.0 ? cs[r].S * em[r] * inv_S : 0.0;
   for (uint64_t rr = rej; rr; rr &= rr - 1) {
     const int src = __ffsll((unsigned long long)rr) - 1;
-    const int x = __shfl(tok, src);
-    const double px = __shfl(prej, src);
+    const int x = lane_i(tok, src);
+    const double px = lane_d(prej, src);
 #pragma unroll
     for (int r = 0; r < kChunkRegs; ++r)
       if (lane + 64 * r == x / kChunk) mass[r] -= px;
@@ -138,9 +88,9 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
       if (hit) {
         const int hl = __ffsll((unsigned long long)hit) - 1;
         cstar = hl + 64 * r;
-        cbefore = base + __shfl(incl - mass[r], hl);
+        cbefore = base + lane_d(incl - mass[r], hl);
       }
-      base += __shfl(incl, 63);
+      base += lane_d(incl, 63);
     }
   }
   if (cstar < 0) cstar = nc - 1;          // rounding left t beyond the total: last chunk
@@ -167,7 +117,7 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
       }
     }
     for (uint64_t rr = rej; rr; rr &= rr - 1) {
-      const int x = __shfl(tok, __ffsll((unsigned long long)rr) - 1);
+      const int x = lane_i(tok, __ffsll((unsigned long long)rr) - 1);
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (y0 + e == x) pv[e] = 0.0;
@@ -185,98 +135,14 @@ __device__ int residual_draw(const float *row, int V, int nc, double inv_tau,
       if (pv[e] > 0.0) last = y0 + e;
     }
     const uint64_t fh = __ballot(first >= 0);
-    if (fh) return __shfl(first, __ffsll((unsigned long long)fh) - 1);
+    if (fh) return lane_i(first, __ffsll((unsigned long long)fh) - 1);
     // no crossing (rounding at a chunk edge or beyond the total): largest positive id
     const uint64_t lh = __ballot(last >= 0);
-    if (lh) return __shfl(last, 63 - __clzll((long long)lh));
+    if (lh) return lane_i(last, 63 - __clzll((long long)lh));
     if (cstar == 0) return 0;
     --cstar;                             // empty chunk (all rejected / underflow): go down
     cbefore = -INFINITY;
   }
-}
-
-// The same draw from float32 chunk masses `mass` (normalised by the row sum, lane-strided
-// as in row_stats_regs, rejected tokens not yet removed), with the certificate: the token
-// is returned only if t lies inside its interval of the cumulative mass by more than
-// `delta` on both sides, else kUncertain.  The crossing chunk's logits are scanned in
-// float64 as in residual_draw, so only the mass before that chunk is uncertain.
-__device__ int residual_draw_certified(const float *row, int V, int nc, double inv_tau,
-                                       double (&mass)[kChunkRegs], double M, double inv_S,
-                                       uint64_t rej, int tok, double prej, double t,
-                                       double delta, const double *tab) {
-  const int lane = threadIdx.x & 63;
-  for (uint64_t rr = rej; rr; rr &= rr - 1) {
-    const int src = __ffsll((unsigned long long)rr) - 1;
-    const int x = __shfl(tok, src);
-    const double px = __shfl(prej, src);
-#pragma unroll
-    for (int r = 0; r < kChunkRegs; ++r)
-      if (lane + 64 * r == x / kChunk) mass[r] -= px;
-  }
-  int cstar = -1;
-  double cbefore = 0.0, base = 0.0;
-#pragma unroll
-  for (int r = 0; r < kChunkRegs; ++r) {
-    if (cstar < 0 && 64 * r < nc) {
-      const double incl = wave_inclusive_sum(mass[r]);
-      const uint64_t hit = __ballot(lane + 64 * r < nc && base + incl > t);
-      if (hit) {
-        const int hl = __ffsll((unsigned long long)hit) - 1;
-        cstar = hl + 64 * r;
-        cbefore = base + __shfl(incl - mass[r], hl);
-      }
-      base += __shfl(incl, 63);
-    }
-  }
-  if (cstar < 0) return kUncertain;      // t at or beyond the total: too close to call
-  const int y0 = cstar * kChunk + lane * 16;
-  double pv[16];
-  float lv[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) lv[e] = row[min(y0 + e, V - 1)];
-#pragma unroll
-  for (int h = 0; h < 16; h += 4) {
-    ExpParts ep[4];
-    double tj[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ep[e] = exp_split(shifted(lv[h + e], inv_tau, M));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tj[e] = tab[exp_slot(ep[e].k)];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double pe = exp_join(ep[e], tj[e]) * inv_S;
-      pv[h + e] = y0 + h + e < V ? pe : 0.0;
-    }
-  }
-  for (uint64_t rr = rej; rr; rr &= rr - 1) {
-    const int x = __shfl(tok, __ffsll((unsigned long long)rr) - 1);
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (y0 + e == x) pv[e] = 0.0;
-  }
-  double lsum = 0.0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) lsum += pv[e];
-  const double li = wave_inclusive_sum(lsum);
-  double C = cbefore + (li - lsum);
-  int first = -1;
-  double c_lo = 0.0, c_hi = 0.0;         // cumulative mass before / through `first`
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const double prev = C;
-    C += pv[e];
-    if (first < 0 && pv[e] > 0.0 && C > t) {
-      first = y0 + e;
-      c_lo = prev;
-      c_hi = C;
-    }
-  }
-  const uint64_t fh = __ballot(first >= 0);
-  if (!fh) return kUncertain;            // no crossing in the chunk: an edge case
-  const int src = __ffsll((unsigned long long)fh) - 1;
-  const int y = __shfl(first, src);
-  const double lo = __shfl(c_lo, src), hi = __shfl(c_hi, src);
-  return (t - lo > delta && hi - t > delta) ? y : kUncertain;
 }
 
 struct WsLayout {
@@ -294,48 +160,10 @@ inline WsLayout ws_layout(int B, int T, int V) {
   return w;
 }
 
-// The float64 decisions of node `row_id` (one wavefront; lane i holds token and uniform of
-// node i, `kids` the node's children) from its exact chunk statistics cs: the tests of its
-// children in ascending index and, when none is accepted, the bonus drawn from the
-// residual.  Returns the node word.
-__device__ uint64_t decide_exact(const AcceptArgs &a, int64_t row_id, uint64_t kids, int tok,
-                                 double ul, const RejStat (&cs)[kChunkRegs], const double *tab) {
-  const int lane = threadIdx.x & 63;
-  const float *row = a.logits + row_id * a.V;
-  const float lg = ((kids >> lane) & 1) ? row[tok] : 0.f;
-  double M, S;
-  row_stats_regs(cs, tab, M, S);
-  const double inv_S = 1.0 / S;
-  // every child's target probability at once, in its own lane (in the loop below, one
-  // exp per child, each waiting for its table read, made wide nodes the slowest rows)
-  const double pk = exp_nonpos(shifted(lg, a.inv_tau, M), tab) * inv_S;
-  double Z = 1.0, myp = 0.0;
-  uint64_t rej = 0;
-  int next = -1;
-  for (uint64_t kk = kids; kk; kk &= kk - 1) {
-    const int c = __ffsll((unsigned long long)kk) - 1;
-    const int x = __shfl(tok, c);
-    if (__ballot(((rej >> lane) & 1) && tok == x)) continue;   // already rejected here
-    const double p = __shfl(pk, c);
-    if (__shfl(ul, c) * Z < p) {
-      next = c;
-      break;
-    }
-    rej |= 1ull << c;
-    if (lane == c) myp = p;
-    Z -= p;
-  }
-  const int bonus = next >= 0 ? -1
-                              : residual_draw(row, a.V, a.n_chunks, a.inv_tau, cs, M, S, rej,
-                                              tok, myp, __shfl(ul, 0) * Z, tab);
-  return pack_node(next, bonus);
-}
-
 // Outcome of node n of sequence b (one wavefront; lane i holds parent, token and uniform
 // of node i): greedy — the row's lowest argmax y, the lowest-index child drafting y, and y
 // as the bonus; rejection — the tests of its children in ascending index, and, when none
-// is accepted, the bonus drawn from the residual, each taken from the float32 statistics
-// under their certificate (kUncertain where it fails).  The bonus is only used if the walk
+// is accepted, the bonus drawn from the residual.  The bonus is only used if the walk
 // ends here, but it depends on nothing else, so every row draws its own in parallel.
 template <bool REJ>
 __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok, double ul,
@@ -365,65 +193,30 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
       next = match ? __ffsll((unsigned long long)match) - 1 : -1;
       bonus = i;
     } else {
-      const RejStatF *st = (const RejStatF *)a.stats + row_id * nc;
+      const RejStat *st = (const RejStat *)a.stats + row_id * nc;
       const float *row = a.logits + row_id * a.V;
-      double Mc[kChunkRegs], Sc[kChunkRegs], Bc[kChunkRegs];
+      RejStat cs[kChunkRegs];
 #pragma unroll
       for (int r = 0; r < kChunkRegs; ++r) {
         const int c = lane + 64 * r;
-        Mc[r] = -INFINITY;
-        Sc[r] = 0.0;
-        Bc[r] = 0.0;
-        if (c < nc) {
-          const uint64_t fe = observe((const uint64_t *)&st[c]);
-          const float vm = __uint_as_float((uint32_t)fe);
-          const float E = __uint_as_float((uint32_t)(fe >> 32));
-          Sc[r] = observe(&st[c].S);
-          Mc[r] = vm == -INFINITY ? -INFINITY : (double)vm * a.inv_tau;
-          Bc[r] = kErrY * (double)E + kErrS * Sc[r] + kErrTerm;
-        }
+        cs[r] = c < nc ? RejStat{observe(&st[c].M), observe(&st[c].S)} : RejStat{-INFINITY, 0.0};
       }
       const float lg = ((kids >> lane) & 1) ? row[tok] : 0.f;
-      double M = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < kChunkRegs; ++r) M = fmax(M, Mc[r]);
-      M = wave_max(M);
-      double x[kChunkRegs], f[kChunkRegs];
-#pragma unroll
-      for (int r = 0; r < kChunkRegs; ++r) x[r] = Mc[r] - M;
-      exp_nonpos_n(x, f, tab);
-      // the chunk masses (unnormalised until S is known) and their error bounds
-      double mass[kChunkRegs];
-      double S = 0.0, err = 0.0;
-#pragma unroll
-      for (int r = 0; r < kChunkRegs; ++r) {
-        mass[r] = Sc[r] > 0.0 ? Sc[r] * f[r] : 0.0;
-        S += mass[r];
-        err += Bc[r] * f[r];
-      }
-      S = wave_sum(S);
-      err = wave_sum(err) + kErrRow * S;
+      double M, S;
+      row_stats_regs(cs, tab, M, S);
       const double inv_S = 1.0 / S;
-#pragma unroll
-      for (int r = 0; r < kChunkRegs; ++r) mass[r] *= inv_S;
-      // relative error bound of S and the margin every decision must clear
-      const double rel = S > 2.0 * err ? err / (S - err) : INFINITY;
-      const double delta = a.bound_scale * (rel * (1.0 + rel) + kErrDecision);
+      // every child's target probability at once, in its own lane (in the loop below, one
+      // exp per child, each waiting for its table read, made wide nodes the slowest rows)
       const double pk = exp_nonpos(shifted(lg, a.inv_tau, M), tab) * inv_S;
       double Z = 1.0, myp = 0.0;
       uint64_t rej = 0;
       next = -1;
       for (uint64_t kk = kids; kk; kk &= kk - 1) {
         const int c = __ffsll((unsigned long long)kk) - 1;
-        const int xt = __shfl(tok, c);
-        if (__ballot(((rej >> lane) & 1) && tok == xt)) continue;   // already rejected here
-        const double p = __shfl(pk, c);
-        const double d = __shfl(ul, c) * Z - p;
-        if (!(fabs(d) > delta)) {
-          next = kUncertain;
-          break;
-        }
-        if (d < 0.0) {
+        const int x = lane_i(tok, c);
+        if (__ballot(((rej >> lane) & 1) && tok == x)) continue;   // already rejected here
+        const double p = lane_d(pk, c);
+        if (lane_d(ul, c) * Z < p) {
           next = c;
           break;
         }
@@ -431,14 +224,9 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
         if (lane == c) myp = p;
         Z -= p;
       }
-      if (next == kUncertain) {
-        bonus = kUncertain;
-      } else if (next >= 0) {
-        bonus = -1;
-      } else {
-        bonus = residual_draw_certified(row, a.V, nc, a.inv_tau, mass, M, inv_S, rej, tok, myp,
-                                        __shfl(ul, 0) * Z, delta, tab);
-      }
+      bonus = next >= 0 ? -1
+                        : residual_draw(row, a.V, nc, a.inv_tau, cs, M, S, rej, tok, myp,
+                                        lane_d(ul, 0) * Z, tab);
     }
   }
   if (lane == 0) publish(&a.node_out[row_id], pack_node(next, bonus));
@@ -458,15 +246,15 @@ __device__ void finish_sequence(const Args &a, int b, int tok) {
   int my_path = lane == 0 ? 0 : -1;      // lane m holds path[m]
   int my_out = -1;                       // lane m holds out_tokens[m]
   for (;;) {
-    const int nxt = __shfl(next_l, node);
+    const int nxt = lane_i(next_l, node);
     if (nxt < 0) break;
-    const int drafted = __shfl(tok, nxt);
+    const int drafted = lane_i(tok, nxt);
     if (lane == k) my_out = drafted;
     ++k;
     if (lane == k) my_path = nxt;
     node = nxt;
   }
-  const int bonus = __shfl(bonus_l, node);
+  const int bonus = lane_i(bonus_l, node);
   if (lane == k) my_out = bonus;
   if (live) {
     a.path[(int64_t)b * T + lane] = my_path;
@@ -476,28 +264,13 @@ __device__ void finish_sequence(const Args &a, int b, int tok) {
 }
 
 // Statistics of one 1024-logit chunk (already in registers), the same in every lane:
-// greedy, the (max, lowest argmax) word; rejection, the float32 statistics with their
-// error term (RejStatF).  chunk_stats_exact gives the float64 ones (M_c = max s,
-// S_c = sum exp(s - M_c)) that the walk recomputes for an uncertain node.
+// greedy, the (max, lowest argmax) word; rejection, float64 (M_c = max s, S_c = sum exp(s - M_c)).
 template <bool REJ>
-using ChunkStat = typename std::conditional<REJ, RejStatF, uint64_t>::type;
+using ChunkStat = typename std::conditional<REJ, RejStat, uint64_t>::type;
 
-template <int XB>
-__device__ __forceinline__ RejStat chunk_stats_exact(const AcceptArgs &a, const float (&v)[16],
-                                                     const double *tab) {
-  float best = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) best = fmaxf(best, v[e]);
-  const double M = (double)wave_max_f(best) * a.inv_tau;
-  // Padding past V holds -inf: its term is clamped to at most 5e-324, which vanishes
-  // next to the chunk's own maximum term (1), so no per-element test is needed.
-  const double sum = exp_sum<16, XB>([&](int e) { return shifted(v[e], a.inv_tau, M); }, tab);
-  return RejStat{M, wave_sum(sum)};
-}
-
-template <bool REJ>
+template <bool REJ, int XB>
 __device__ __forceinline__ ChunkStat<REJ> chunk_stats(const AcceptArgs &a, int chunk,
-                                                      const float (&v)[16]) {
+                                                      const float (&v)[16], const double *tab) {
   const int lane = threadIdx.x & 63;
   if constexpr (!REJ) {
     // a lane visits its ids in increasing order, so a strict > keeps the lowest index; it
@@ -518,119 +291,21 @@ __device__ __forceinline__ ChunkStat<REJ> chunk_stats(const AcceptArgs &a, int c
     float best = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) best = fmaxf(best, v[e]);
-    const float vmax = wave_max_f(best);
-    if (vmax == -INFINITY) return RejStatF{vmax, 0.f, 0.0};      // a chunk without mass
-    // Padding past V holds -inf: y clamps to -256, whose exponential is 0.
-    double S = 0.0;
-    float E = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float y = fmaxf((v[4 * g + j] - vmax) * a.c32, -256.f);
-        p[j] = __builtin_amdgcn_exp2f(y);
-        E = fmaf(p[j], -y, E);
-      }
-      S += (double)((p[0] + p[1]) + (p[2] + p[3]));
-    }
-    return RejStatF{vmax, wave_sum_f(E), wave_sum(S)};
+    const double M = (double)wave_max_f(best) * a.inv_tau;
+    // Padding past V holds -inf: its term is clamped to at most 5e-324, which vanishes
+    // next to the chunk's own maximum term (1), so no per-element test is needed.
+    const double sum = exp_sum<16, XB>([&](int e) { return shifted(v[e], a.inv_tau, M); }, tab);
+    return RejStat{M, wave_sum(sum)};
   }
 }
 
 __device__ inline void publish_stat(const AcceptArgs &a, int64_t row, int chunk, uint64_t st) {
   publish((uint64_t *)a.stats + row * a.n_chunks + chunk, st);
 }
-__device__ inline void publish_stat(const AcceptArgs &a, int64_t row, int chunk, RejStatF st) {
-  RejStatF *dst = (RejStatF *)a.stats + row * a.n_chunks + chunk;
-  publish((uint64_t *)dst, pack_fe(st.vmax, st.E));
+__device__ inline void publish_stat(const AcceptArgs &a, int64_t row, int chunk, RejStat st) {
+  RejStat *dst = (RejStat *)a.stats + row * a.n_chunks + chunk;
+  publish(&dst->M, st.M);
   publish(&dst->S, st.S);
-}
-
-// Float64 chunk statistics of one row into s_cs (the whole workgroup; ends with a barrier).
-__device__ void exact_chunk_stats(const AcceptArgs &a, int64_t row_id, const double *tab,
-                                  RejStat *s_cs) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const float *row = a.logits + row_id * a.V;
-  const bool vec = (a.V & 3) == 0;
-  for (int c = wave; c < a.n_chunks; c += kChunksPerWG) {
-    float v[16];
-    int idx[16];
-    load_chunk(row, a.V, c * kChunk, vec, v, idx);
-    const RejStat st = chunk_stats_exact<4>(a, v, tab);
-    if (lane == 0) s_cs[c] = st;
-  }
-  __syncthreads();
-}
-
-// The rejection walk of sequence b (the whole workgroup; wavefront 0's lane i holds
-// parent, token and uniform of node i).  Wavefront 0 follows accepted children from the
-// root; at a node marked kUncertain every wavefront recomputes that row's chunk statistics
-// in float64, wavefront 0 settles the node from them (decide_exact) and goes on.
-__device__ void walk_rejection(const AcceptArgs &a, int b, int par, int tok, double ul,
-                               const double *tab, RejStat *s_cs, int *s_node) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int T = a.T;
-  const bool live = lane < T;
-  int next_l = -1, bonus_l = -1, node = 0, k = 0;
-  int my_path = lane == 0 ? 0 : -1;      // lane m holds path[m]
-  int my_out = -1;                       // lane m holds out_tokens[m]
-  bool bad = false;
-  if (wave == 0) {
-    const uint64_t w = live ? observe(&a.node_out[(int64_t)b * T + lane]) : pack_node(-1, -1);
-    next_l = (int)(uint32_t)w;
-    bonus_l = (int)(uint32_t)(w >> 32);
-    bad = __any(next_l == -2);           // invalid tree, already reported
-  }
-  for (;;) {
-    if (wave == 0) {
-      int pending = -1;
-      while (!bad) {
-        const int nxt = __shfl(next_l, node);
-        if (nxt == kUncertain || (nxt < 0 && __shfl(bonus_l, node) == kUncertain)) {
-          pending = node;
-          break;
-        }
-        if (nxt < 0) break;
-        const int drafted = __shfl(tok, nxt);
-        if (lane == k) my_out = drafted;
-        ++k;
-        if (lane == k) my_path = nxt;
-        node = nxt;
-      }
-      if (lane == 0) *s_node = pending;
-    }
-    __syncthreads();
-    const int pending = *s_node;
-    if (pending < 0) break;
-    const int64_t row_id = (int64_t)b * T + pending;
-    exact_chunk_stats(a, row_id, tab, s_cs);
-    if (wave == 0) {
-      RejStat cs[kChunkRegs];
-#pragma unroll
-      for (int r = 0; r < kChunkRegs; ++r) {
-        const int c = lane + 64 * r;
-        cs[r] = c < a.n_chunks ? s_cs[c] : RejStat{-INFINITY, 0.0};
-      }
-      const uint64_t kids = __ballot(live && par == pending);
-      const uint64_t w = decide_exact(a, row_id, kids, tok, ul, cs, tab);
-      if (lane == pending) {
-        next_l = (int)(uint32_t)w;
-        bonus_l = (int)(uint32_t)(w >> 32);
-      }
-    }
-    __syncthreads();                     // s_cs and s_node are reused
-  }
-  if (wave != 0 || bad) return;
-  const int bonus = __shfl(bonus_l, node);
-  if (lane == k) my_out = bonus;
-  if (live) {
-    a.path[(int64_t)b * T + lane] = my_path;
-    a.out_tokens[(int64_t)b * T + lane] = my_out;
-  }
-  if (lane == 0) a.accept_len[b] = k;
 }
 
 // grid (chunk groups, rows); a workgroup's four wavefronts stream CPW chunks each, the
@@ -639,10 +314,9 @@ __device__ void walk_rejection(const AcceptArgs &a, int b, int par, int tok, dou
 template <bool REJ, int CPW, bool VEC>
 __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ double tab[kExpTab];
-  __shared__ RejStat s_cs[REJ ? 64 * kChunkRegs : 1];   // the walk's float64 recomputation
-  __shared__ int s_last, s_node;
+  __shared__ int s_last;
   args_in_sgprs(a.n_chunks, a.T, a.V, a.logits, a.parent, a.tokens, a.uniforms, a.inv_tau,
-                a.c32, a.stats, a.row_cnt);
+                a.stats, a.row_cnt);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.y;
@@ -664,11 +338,15 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   // reduced, and publishes its statistics only at the end: a load or store under a branch,
   // or a store between the loads, made the compiler wait for the chunk still in flight.
   // A chunk past the row's end (last workgroup of a row) loads the row's last chunk and is
-  // not reduced.  The first chunk's loads go out first of all: the stream needs no table
-  // (the exp table serves the settle and walk steps, after the row's last arrival, whose
-  // barrier orders it).
+  // not reduced.  With one chunk per wavefront its loads go out before the exp table is
+  // filled (26 rows x 32000: 6.38 -> 5.98 us); with two or four they go out after the
+  // barrier (issued before it, 64 rows x 128256 took 16.15 -> 16.48 us, same-box pairs).
   ChunkStat<REJ> st[CPW];
-  load_chunk_raw<kNT, VEC>(lrow, a.V, min(c0, nc - 1) * kChunk, v[0]);
+  // exp table reads issued 8 (four chunks per wavefront: 4) at a time; 8 with four chunks
+  // took the kernel past the register count that keeps six wavefronts per SIMD
+  constexpr int kExpBatch = CPW == 4 ? 4 : 8;
+  if constexpr (CPW == 1) load_chunk_raw<kNT, VEC>(lrow, a.V, min(c0, nc - 1) * kChunk, v[0]);
+
   if (REJ) fill_exp_table(tab);
   // The tree of this sequence, for the settle and walk steps below (loaded up front so
   // that its latency hides behind the logit stream).
@@ -679,6 +357,8 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     tok = a.tokens[(int64_t)b * a.T + lane];
     if (REJ) ul = a.uniforms[(int64_t)b * a.T + lane];
   }
+  lds_barrier();                          // the exp table
+  if constexpr (CPW != 1) load_chunk_raw<kNT, VEC>(lrow, a.V, min(c0, nc - 1) * kChunk, v[0]);
 #pragma unroll
   for (int m = 0; m < CPW; ++m) {
     const int c = c0 + kChunksPerWG * m;
@@ -686,7 +366,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
       load_chunk_raw<kNT, VEC>(lrow, a.V, min(c + kChunksPerWG, nc - 1) * kChunk, v[(m + 1) & 1]);
     if (c < nc) {
       mask_chunk(a.V, c * kChunk, v[m & 1], idx_unused);
-      st[m] = chunk_stats<REJ>(a, c, v[m & 1]);
+      st[m] = chunk_stats<REJ, kExpBatch>(a, c, v[m & 1], tab);
     }
   }
   if (lane == 0) {
@@ -701,10 +381,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
 
   // ---- last row of this sequence: walk ----
-  if constexpr (REJ)
-    walk_rejection(a, b, par, tok, ul, tab, s_cs, &s_node);
-  else if (wave == 0)
-    finish_sequence(a, b, tok);
+  if (wave == 0) finish_sequence(a, b, tok);
 }
 
 static ev_status check_common(const float *logits, const int32_t *tokens, const int32_t *parent,
@@ -718,9 +395,6 @@ static ev_status check_common(const float *logits, const int32_t *tokens, const 
   return EV_OK;
 }
 
-// Multiplier of the rejection path's certification margins (ev_accept_set_bound_scale).
-static std::atomic<double> g_bound_scale{1.0};
-
 static ev_status launch_accept(bool rej, const float *logits, const int32_t *tokens,
                                const int32_t *parent, int32_t B, int32_t T, int32_t V,
                                double inv_tau, const double *uniforms, int32_t *accept_len,
@@ -728,9 +402,7 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
                                int32_t *dev_status, hipStream_t stream) {
   const WsLayout w = ws_layout(B, T, V);
   char *base = (char *)ws;
-  const float c32 = (float)(inv_tau * 1.4426950408889634);   // log2(e) / tau
-  AcceptArgs a{logits, tokens, parent, B, T, V, n_chunks_of(V), inv_tau, c32, g_bound_scale.load(),
-               uniforms,
+  AcceptArgs a{logits, tokens, parent, B, T, V, n_chunks_of(V), inv_tau, uniforms,
                base + w.stats, (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
                (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status};
   // Chunks per wavefront: as many as keep at least 1024 workgroups in the grid (four per
@@ -1194,11 +866,6 @@ EV_API ev_status ev_accept_rejection(const float *logits, const int32_t *tokens,
   if (!uniforms) return EV_ERR_NULL;
   return ev::launch_accept(true, logits, tokens, parent, B, T, V, 1.0 / (double)temperature,
                            uniforms, accept_len, path, out_tokens, ws, dev_status, stream);
-}
-
-EV_API double ev_accept_set_bound_scale(double scale) {
-  if (!(scale > 0.0)) return ev::g_bound_scale.load();
-  return ev::g_bound_scale.exchange(scale);
 }
 
 EV_API size_t ev_accept_sampled_workspace(int32_t B, int32_t T, int32_t V) {
