@@ -156,6 +156,22 @@ ev_status ev_tree_attention_noalloc(const void *q, const ev_kv_desc *kv, const i
 /* (host) Bytes of the fixed scratch array ev_tree_attention_noalloc uses. */
 size_t ev_tree_attention_noalloc_limit(void);
 
+/* ev_tree_mask_attention — ev_tree_mask_build followed by ev_tree_attention, in one call
+ * ([TR] sec. 2: the mask M is derived from the tree and applied in the same forward).
+ *   parent [B][T] int32 as for ev_tree_mask_build; anc_mask [B][T] uint64 (output, required)
+ *   and depth [B][T] int32 (output, may be NULL) receive what ev_tree_mask_build writes;
+ *   every other argument, the workspace (ev_tree_attention_workspace) and the outputs are
+ *   those of ev_tree_attention.  For bf16 caches with head_dim 128 the attention launch
+ *   itself builds the masks from parent[] (the workgroups whose keys reach the tree slots
+ *   build them, one per sequence stores them), so mask and attention cost one launch;
+ *   otherwise the mask kernel runs first.  A parent[] that is not a tree sets
+ *   EV_DERR_PARENT; that sequence's outputs are then unspecified. */
+ev_status ev_tree_mask_attention(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
+                                 const int32_t *parent, uint64_t *anc_mask, int32_t *depth,
+                                 int32_t B, int32_t T, int32_t Hq, int64_t max_prefix_len,
+                                 float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes,
+                                 int32_t *dev_status, hipStream_t stream);
+
 /* Bytes of workspace the acceptance calls need (B * T <= 65535, V <= 262144).
  * The acceptance workspace holds arrival counters: zero-fill it (for example with
  * hipMemset) before its first use.  Every call that launches leaves the counters at zero

@@ -31,7 +31,7 @@ STATUS_NAMES = {
 }
 EXPORTED = (
     "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
-    "ev_tree_attention_noalloc", "ev_tree_attention_noalloc_limit",
+    "ev_tree_attention_noalloc", "ev_tree_attention_noalloc_limit", "ev_tree_mask_attention",
     "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection",
     "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact",
     "ev_kv_compact_remap_workspace", "ev_kv_compact_remap",
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "ev_tree_attention_noalloc": (_I32, [_P, kv, _P, _P, _I32, _I32, _I32, _I64, _F32, _P,
                                                  _P, _P, _P]),
             "ev_tree_attention_noalloc_limit": (_SZ, []),
+            "ev_tree_mask_attention": (_I32, [_P, kv, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _F32,
+                                              _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_workspace": (_SZ, [_I32, _I32, _I32]),
             "ev_accept_greedy": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_rejection": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _P,
@@ -267,6 +269,38 @@ def ev_tree_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor, an
                                    _ptr(status), _stream(dev))
     _finish(code, "ev_tree_attention", status, check)
     return out, lse
+
+
+def ev_tree_mask_attention(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor,
+                           parent: torch.Tensor, sm_scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           anc_mask: Optional[torch.Tensor] = None, depth: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None, dev_status: Optional[torch.Tensor] = None,
+                           check: bool = False, max_prefix_len: Optional[int] = None):
+    """ev_tree_mask_build and ev_tree_attention in one call; returns (out, lse, anc_mask, depth).
+    depth is only written when given (or returned as None)."""
+    _dev(q, "q", torch.bfloat16 if kv.dtype == torch.uint8 else kv.dtype)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    B, T, Hq, d = q.shape
+    dev = q.device
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    mpl = max(0, kv.capacity - T) if max_prefix_len is None else int(max_prefix_len)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    anc_mask = torch.empty((B, T), dtype=torch.int64, device=dev) if anc_mask is None else anc_mask
+    need = ev_tree_attention_workspace(kv, B, T, Hq, mpl)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = _status_word(dev, dev_status)
+    code = lib().ev_tree_mask_attention(_ptr(q), kv.ref(), _ptr(prefix_len), _ptr(parent),
+                                        _ptr(anc_mask), _ptr(depth), B, T, Hq, mpl, float(sm_scale),
+                                        _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(status),
+                                        _stream(dev))
+    _finish(code, "ev_tree_mask_attention", status, check)
+    return out, lse, anc_mask, depth
 
 
 def ev_tree_attention_noalloc(q: torch.Tensor, kv: KvCache, prefix_len: torch.Tensor,

@@ -76,6 +76,9 @@ struct AttnArgs {
   int32_t *dev_status;
   const float *k_scale;    // INT4 caches: one scale per (slot, KV head) row
   const float *v_scale;
+  const int32_t *parent;   // set: the DMA kernel builds the masks itself from the parents
+  uint64_t *anc_out;       //   and writes them (and depth_out, if set) once per sequence
+  int32_t *depth_out;
 };
 
 // Row of split `split`'s partial for output row `orow` ((sequence, node, head) order): the
@@ -838,7 +841,45 @@ __device__ __forceinline__ void finish_pair(const AttnArgs &a, const f32x16 (&o)
 // combined through LDS at the end; with NW = 2 it serves heads of at most 32 rows, with
 // NW = 8 it halves the rows per workgroup of short split plans (more row blocks, fewer
 // splits, fewer partial rows).
-template <int NW, bool PAGED, bool KSPLIT>
+// Ancestor masks of sequence b from its parents in LDS (one wavefront, lane i = node i),
+// by pointer doubling over the parent links as ev_tree_mask_build does ([TR] sec. 2, mask
+// equation M): after round r a lane holds its ancestors within distance 2^r, so six rounds
+// cover 64 nodes.  The masks go to LDS; `writer` also stores them (and the depths) to
+// anc_out / depth_out, or reports a parent array that is not a tree (whose outputs are
+// then unspecified, like every output of a sequence with a device error).
+__device__ void build_masks(const AttnArgs &a, int b, const int32_t *s_par, uint64_t *s_anc,
+                            bool writer) {
+  const int i = threadIdx.x & 63;
+  const bool live = i < a.T;
+  int p = live ? s_par[i] : -1;
+  const bool ok = !live || (i == 0 ? p == -1 : (p >= 0 && p < i));
+  const bool tree_ok = !__any(!ok);
+  if (!ok) p = -1;
+  uint64_t set = live ? (1ull << i) : 0ull;
+  int up = p;
+  for (int r = 0; r < 6; ++r) {
+    const int src = up < 0 ? i : up;
+    const uint64_t s_up = __shfl(set, src);
+    const int up_up = __shfl(up, src);
+    if (up >= 0) {
+      set |= s_up;
+      up = up_up;
+    }
+  }
+  if (live) s_anc[i] = set;
+  if (writer) {
+    if (!tree_ok) {
+      if (i == 0) report(a.dev_status, EV_DERR_PARENT);
+    } else if (live) {
+      a.anc_out[(int64_t)b * a.T + i] = set;
+      if (a.depth_out) a.depth_out[(int64_t)b * a.T + i] = __popcll(set) - 1;
+    }
+  }
+}
+
+// MASKS: the masks are built from a.parent (ev_tree_mask_attention) instead of read from
+// a.anc; a separate instantiation, so that ev_tree_attention's kernels are unchanged.
+template <int NW, bool PAGED, bool KSPLIT, bool MASKS>
 __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int D = 128;
   constexpr int QT = 1;
@@ -852,7 +893,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   constexpr int RG = KSPLIT ? NW / 2 : NW;       // groups of 32 query rows per workgroup
   constexpr int NT = NW * 64;
   // kStages K|V tile pairs, then the sequence's ancestor masks (64 x 8 bytes)
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT + kMaxNodes * 4];
+  // (then the parents, when the kernel builds the masks: 64 x 4 bytes)
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[kStages * 2 * MAT + kMaxNodes * (MASKS ? 6 : 4)];
   __shared__ int stbl[PAGED ? kTableCache : 1];
 
   args_in_sgprs(gridDim.x, a.n_work, a.row_blocks, a.n_splits, a.kv.hkv, a.kv.cap, a.T, a.G, a.Hq,
@@ -890,7 +932,17 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
   // The sequence's ancestor masks, also global -> LDS by DMA (wave 0, 4-byte pieces),
   // into the same LDS array as the tiles.
   uint64_t *s_anc = (uint64_t *)(lds + kStages * 2 * MAT);
+  // With a.parent set, the sequence's parents come instead (one 4-byte piece per node,
+  // after the masks' area) and the masks are built from them in the prologue.
+  int32_t *s_par = (int32_t *)(s_anc + kMaxNodes);
   auto issue_anc = [&]() {
+    if constexpr (MASKS) {
+      if (lane < a.T)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(a.parent + (int64_t)b * a.T + lane),
+            (__attribute__((address_space(3))) void *)s_par, 4, 0, 0);
+      return;
+    }
     const uint32_t *src = (const uint32_t *)(a.anc + (int64_t)b * a.T);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1168,6 +1220,12 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_dma_kernel(AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qf[0][ks] = *(const bf16x8 *)(qlds + qn * D + ((((2 * ks) | hh) ^ (qn & 15)) << 3));
+  // Masks from the parents (their DMA has landed with this wave's Q rows): only workgroups
+  // whose keys reach the tree slots use them, so only those build them; the one holding
+  // the sequence's last tile for KV head 0 and row block 0 also writes them out.
+  if constexpr (MASKS)
+    if (wave == 0 && t_end * kKT > L)
+      build_masks(a, b, s_par, s_anc, g == 0 && rb == 0 && t_end == ntiles);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   wg_barrier();                                  // every wave holds its Q: stages 2, 3 free
   anc_q[0] = row0 + qn < rows ? s_anc[(row0 + qn) / a.G] : 0ull;
@@ -1599,21 +1657,29 @@ static size_t workspace_bytes(const Plan &p, int B, int T, int Hq, int D) {
   return align_up(rows * D * sizeof(_Float16), 256) + align_up(rows * sizeof(uint64_t), 256);
 }
 
+template <bool PAGED, bool MASKS>
+static void launch_dma(const Plan &p, const AttnArgs &a, dim3 grid, hipStream_t stream) {
+  if (p.nw == 8 && p.ksplit)
+    hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED, true, MASKS>), grid, dim3(512), 0, stream, a);
+  else if (p.nw == 8)
+    hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED, false, MASKS>), grid, dim3(512), 0, stream, a);
+  else if (p.nw == 4)
+    hipLaunchKernelGGL((tree_attn_dma_kernel<4, PAGED, false, MASKS>), grid, dim3(256), 0, stream, a);
+  else if (p.ksplit)
+    hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED, true, MASKS>), grid, dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED, false, MASKS>), grid, dim3(128), 0, stream, a);
+}
+
 template <int D, bool PAGED, bool Q4>
 static void launch_main(const Plan &p, const AttnArgs &a, hipStream_t stream) {
   dim3 grid(p.grid);
   if constexpr (!Q4 && D == 128) {
     // bf16 with d = 128: the direct-to-LDS kernel (the plan gives it at least 2 waves)
-    if (p.nw == 8 && p.ksplit)
-      hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED, true>), grid, dim3(512), 0, stream, a);
-    else if (p.nw == 8)
-      hipLaunchKernelGGL((tree_attn_dma_kernel<8, PAGED, false>), grid, dim3(512), 0, stream, a);
-    else if (p.nw == 4)
-      hipLaunchKernelGGL((tree_attn_dma_kernel<4, PAGED, false>), grid, dim3(256), 0, stream, a);
-    else if (p.ksplit)
-      hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED, true>), grid, dim3(128), 0, stream, a);
+    if (a.parent)
+      launch_dma<PAGED, true>(p, a, grid, stream);
     else
-      hipLaunchKernelGGL((tree_attn_dma_kernel<2, PAGED, false>), grid, dim3(128), 0, stream, a);
+      launch_dma<PAGED, false>(p, a, grid, stream);
   } else if (p.nw == 8) {
     hipLaunchKernelGGL((tree_attn_bf16_kernel<D, 1, 8, PAGED, Q4>), grid, dim3(512), 0, stream, a);
   } else if (p.nw == 4) {
@@ -1678,11 +1744,16 @@ namespace ev {
 
 // ev_tree_attention's work with the workspace given; scratch_call: the workspace is the
 // fixed scratch array, so a plan that needs more than ws_bytes is EV_ERR_SCRATCH.
+// With `parent` set (ev_tree_mask_attention) the masks are built from it and written to
+// anc_out (and depth_out): inside the direct-to-LDS kernel, else by the mask kernel
+// launched first.
 static ev_status attention_call(const void *q, const ev_kv_desc *kv, const int32_t *prefix_len,
                                 const uint64_t *anc_mask, int32_t B, int32_t T, int32_t Hq,
                                 int64_t max_prefix_len, float sm_scale, void *out, float *lse,
                                 void *ws, size_t ws_bytes, int32_t *dev_status,
-                                hipStream_t stream, bool scratch_call) {
+                                hipStream_t stream, bool scratch_call,
+                                const int32_t *parent = nullptr, uint64_t *anc_out = nullptr,
+                                int32_t *depth_out = nullptr) {
   ev::KvAddr addr;
   ev_status st = ev::make_kv_addr(kv, &addr);
   if (st != EV_OK) return st;
@@ -1690,7 +1761,8 @@ static ev_status attention_call(const void *q, const ev_kv_desc *kv, const int32
     return EV_ERR_SHAPE;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return EV_ERR_ARG;
   if (B == 0) return EV_OK;
-  if (!q || !prefix_len || !anc_mask || !out || !lse) return EV_ERR_NULL;
+  if (!q || !prefix_len || !out || !lse) return EV_ERR_NULL;
+  if (parent ? !anc_out : !anc_mask) return EV_ERR_NULL;
   // rows of q, out and the cache are read and written in 16-byte pieces
   if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)kv->k | (uintptr_t)kv->v) & 15) return EV_ERR_ARG;
   if ((int64_t)B * kv->n_kv_heads > (1 << 24)) return EV_ERR_SHAPE;
@@ -1721,6 +1793,17 @@ static ev_status attention_call(const void *q, const ev_kv_desc *kv, const int32
   a.out = out;
   a.lse = lse;
   a.dev_status = dev_status;
+  if (parent) {
+    if (p.dma) {
+      a.parent = parent;
+      a.anc_out = anc_out;
+      a.depth_out = depth_out;
+    } else {
+      st = ev_tree_mask_build(parent, B, T, anc_out, depth_out, dev_status, stream);
+      if (st != EV_OK) return st;
+      a.anc = anc_out;
+    }
+  }
   if (need) {
     size_t rows = ev::part_rows(p, B, T, Hq);
     char *base = (char *)ws;
@@ -1794,4 +1877,15 @@ EV_API ev_status ev_tree_attention_noalloc(const void *q, const ev_kv_desc *kv,
 }
 
 EV_API size_t ev_tree_attention_noalloc_limit(void) { return ev::kScratchBytes; }
+
+EV_API ev_status ev_tree_mask_attention(const void *q, const ev_kv_desc *kv,
+                                        const int32_t *prefix_len, const int32_t *parent,
+                                        uint64_t *anc_mask, int32_t *depth, int32_t B, int32_t T,
+                                        int32_t Hq, int64_t max_prefix_len, float sm_scale,
+                                        void *out, float *lse, void *ws, size_t ws_bytes,
+                                        int32_t *dev_status, hipStream_t stream) {
+  if (!parent) return EV_ERR_NULL;
+  return ev::attention_call(q, kv, prefix_len, nullptr, B, T, Hq, max_prefix_len, sm_scale, out,
+                            lse, ws, ws_bytes, dev_status, stream, false, parent, anc_mask, depth);
+}
 
