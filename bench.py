@@ -63,9 +63,9 @@ def algorithmic_work(inp):
             "logit_bytes": 4 * cfg.B * cfg.T * cfg.V}
 
 
-# Calls timed one by one; the step runs STEP_PARTS (mask and attention as one call).
-ALL_PARTS = ("mask", "attention", "mask_attention", "accept", "compact")
-STEP_PARTS = ("mask_attention", "accept", "compact")
+# Calls timed one by one; the step runs STEP_PARTS (the four steps in two calls).
+ALL_PARTS = ("mask", "attention", "mask_attention", "accept", "compact", "accept_compact")
+STEP_PARTS = ("mask_attention", "accept_compact")
 
 
 class BufferSet:
@@ -111,11 +111,22 @@ class BufferSet:
     def compact(self):
         ev.ev_kv_compact(self.kv, self.d.prefix_len, self.path, self.acc, self.new_len, self.status)
 
+    def accept_compact(self):
+        if self.mode == "rejection":
+            ev.ev_accept_rejection_compact(self.d.logits, self.d.tokens, self.d.parent, self.d.tau,
+                                           self.d.uniforms, self.kv, self.d.prefix_len, self.acc,
+                                           self.path, self.tok, self.new_len, self.ws_acc,
+                                           self.status)
+        else:
+            ev.ev_accept_greedy_compact(self.d.logits, self.d.tokens, self.d.parent, self.kv,
+                                        self.d.prefix_len, self.acc, self.path, self.tok,
+                                        self.new_len, self.ws_acc, self.status)
+
     def step(self):
-        # mask build and attention in one call (one launch for bf16 head_dim 128)
+        # mask build with attention, and acceptance with compaction: two calls (three
+        # launches with the split merge) for the four steps of the pass
         self.mask_attention()
-        self.accept()
-        self.compact()
+        self.accept_compact()
 
 
 def capture(fn):

@@ -210,6 +210,28 @@ ev_status ev_accept_rejection(const float *logits, const int32_t *tokens, const 
                               int32_t *accept_len, int32_t *path, int32_t *out_tokens,
                               void *ws, size_t ws_bytes, int32_t *dev_status, hipStream_t stream);
 
+/* ev_accept_greedy_compact, ev_accept_rejection_compact — ev_accept_greedy /
+ * ev_accept_rejection followed by ev_kv_compact of each accepted path ([TR] sec. 2: keep
+ * the accepted branch's KV) in the same launch: the workgroup that walks a sequence's tree
+ * then moves its accepted rows.  Arguments and outputs are those of the acceptance call,
+ * plus kv, prefix_len and new_len as for ev_kv_compact (the path and accept_len written
+ * here are what it compacts).  When one accepted node's rows (all layers, KV heads, K and
+ * V) exceed 4 KB, the ev_kv_compact kernel is launched after the acceptance instead.
+ * Device errors as for both calls. */
+ev_status ev_accept_greedy_compact(const float *logits, const int32_t *tokens,
+                                   const int32_t *parent, int32_t B, int32_t T, int32_t V,
+                                   int32_t *accept_len, int32_t *path, int32_t *out_tokens,
+                                   const ev_kv_desc *kv, const int32_t *prefix_len,
+                                   int32_t *new_len, void *ws, size_t ws_bytes,
+                                   int32_t *dev_status, hipStream_t stream);
+ev_status ev_accept_rejection_compact(const float *logits, const int32_t *tokens,
+                                      const int32_t *parent, int32_t B, int32_t T, int32_t V,
+                                      float temperature, const double *uniforms,
+                                      int32_t *accept_len, int32_t *path, int32_t *out_tokens,
+                                      const ev_kv_desc *kv, const int32_t *prefix_len,
+                                      int32_t *new_len, void *ws, size_t ws_bytes,
+                                      int32_t *dev_status, hipStream_t stream);
+
 /* Bytes of workspace ev_accept_sampled needs (same limits and zero-fill contract as the
  * acceptance workspace above). */
 size_t ev_accept_sampled_workspace(int32_t B, int32_t T, int32_t V);

@@ -33,6 +33,7 @@ EXPORTED = (
     "ev_tree_mask_build", "ev_tree_attention_workspace", "ev_tree_attention",
     "ev_tree_attention_noalloc", "ev_tree_attention_noalloc_limit", "ev_tree_mask_attention",
     "ev_accept_workspace", "ev_accept_greedy", "ev_accept_rejection",
+    "ev_accept_greedy_compact", "ev_accept_rejection_compact",
     "ev_accept_sampled_workspace", "ev_accept_sampled", "ev_kv_compact",
     "ev_kv_compact_remap_workspace", "ev_kv_compact_remap",
     "ev_draft_tree_workspace", "ev_draft_tree_expand", "ev_draft_tree_finalize",
@@ -86,6 +87,10 @@ def lib() -> ctypes.CDLL:
             "ev_accept_greedy": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_rejection": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _P,
                                            _SZ, _P, _P]),
+            "ev_accept_greedy_compact": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, kv, _P,
+                                                _P, _P, _SZ, _P, _P]),
+            "ev_accept_rejection_compact": (_I32, [_P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P,
+                                                   _P, kv, _P, _P, _P, _SZ, _P, _P]),
             "ev_accept_sampled_workspace": (_SZ, [_I32, _I32, _I32]),
             "ev_accept_sampled": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _I32,
                                          _P, _P, _P, _P, _SZ, _P, _P]),
@@ -384,6 +389,58 @@ def ev_accept_rejection(logits: torch.Tensor, tokens: torch.Tensor, parent: torc
                                      _ptr(status), _stream(dev))
     _finish(code, "ev_accept_rejection", status, check)
     return accept_len, path, out_tokens
+
+
+def ev_accept_greedy_compact(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                             kv: KvCache, prefix_len: torch.Tensor, accept_len=None, path=None,
+                             out_tokens=None, new_len=None, ws=None, dev_status=None,
+                             check: bool = False):
+    """Greedy acceptance and compaction of each accepted path in one call; returns
+    (accept_len, path, out_tokens, new_len)."""
+    return _accept_compact(False, logits, tokens, parent, None, None, kv, prefix_len, accept_len,
+                           path, out_tokens, new_len, ws, dev_status, check)
+
+
+def ev_accept_rejection_compact(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                                temperature: float, uniforms: torch.Tensor, kv: KvCache,
+                                prefix_len: torch.Tensor, accept_len=None, path=None,
+                                out_tokens=None, new_len=None, ws=None, dev_status=None,
+                                check: bool = False):
+    """Rejection acceptance and compaction of each accepted path in one call; returns
+    (accept_len, path, out_tokens, new_len)."""
+    return _accept_compact(True, logits, tokens, parent, temperature, uniforms, kv, prefix_len,
+                           accept_len, path, out_tokens, new_len, ws, dev_status, check)
+
+
+def _accept_compact(rej, logits, tokens, parent, temperature, uniforms, kv, prefix_len, accept_len,
+                    path, out_tokens, new_len, ws, dev_status, check):
+    _dev(logits, "logits", torch.float32)
+    _dev(tokens, "tokens", torch.int32)
+    _dev(parent, "parent", torch.int32)
+    _dev(prefix_len, "prefix_len", torch.int32)
+    B, T, V = logits.shape
+    dev = logits.device
+    accept_len, path, out_tokens = _accept_outputs(B, T, dev, accept_len, path, out_tokens)
+    new_len = torch.empty(B, dtype=torch.int32, device=dev) if new_len is None else new_len
+    if ws is None:
+        ws = torch.zeros(max(1, ev_accept_workspace(B, T, V)), dtype=torch.uint8, device=dev)
+    status = _status_word(dev, dev_status)
+    ws_bytes = ws.numel() * ws.element_size()
+    if rej:
+        _dev(uniforms, "uniforms", torch.float64)
+        name = "ev_accept_rejection_compact"
+        code = lib().ev_accept_rejection_compact(
+            _ptr(logits), _ptr(tokens), _ptr(parent), B, T, V, float(temperature), _ptr(uniforms),
+            _ptr(accept_len), _ptr(path), _ptr(out_tokens), kv.ref(), _ptr(prefix_len),
+            _ptr(new_len), _ptr(ws), ws_bytes, _ptr(status), _stream(dev))
+    else:
+        name = "ev_accept_greedy_compact"
+        code = lib().ev_accept_greedy_compact(
+            _ptr(logits), _ptr(tokens), _ptr(parent), B, T, V, _ptr(accept_len), _ptr(path),
+            _ptr(out_tokens), kv.ref(), _ptr(prefix_len), _ptr(new_len), _ptr(ws), ws_bytes,
+            _ptr(status), _stream(dev))
+    _finish(code, name, status, check)
+    return accept_len, path, out_tokens, new_len
 
 
 def ev_accept_sampled_workspace(B: int, T: int, V: int) -> int:

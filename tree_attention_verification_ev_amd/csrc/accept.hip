@@ -32,6 +32,21 @@
 
 namespace ev {
 
+// Compaction of the accepted path in the acceptance launch (the *_compact entry points):
+// the cache (ev_kv_desc as KvAddr plus the raw pointers), its row size and layers.
+struct CompactSeq {
+  char *k;
+  char *v;
+  float *k_scale;                        // INT4 caches: one scale per row, moved with it
+  float *v_scale;
+  KvAddr kv;
+  int row_bytes;                         // bytes of one (slot, KV head) row
+  int64_t layer_rows;                    // rows from one layer to the next
+  int n_layers;
+  const int32_t *prefix_len;
+  int32_t *new_len;
+};
+
 struct AcceptArgs {
   const float *logits;
   const int32_t *tokens;
@@ -47,6 +62,7 @@ struct AcceptArgs {
   int32_t *path;
   int32_t *out_tokens;
   int32_t *dev_status;
+  CompactSeq cmp;                        // used by the compacting kernels only
 };
 
 __device__ inline uint64_t pack_node(int next, int bonus) {
@@ -234,14 +250,20 @@ __device__ void settle_node(const AcceptArgs &a, int b, int n, int par, int tok,
 
 // Follow accepted children from the root of sequence b and emit the bonus token of the
 // last node (one wavefront; lane i holds the token of node i).
+// With s_path set, the path and k also go to LDS for the compaction that follows (k = -1
+// for an invalid tree).
 template <class Args>
-__device__ void finish_sequence(const Args &a, int b, int tok) {
+__device__ void finish_sequence(const Args &a, int b, int tok, int *s_path = nullptr,
+                                int *s_k = nullptr) {
   const int lane = threadIdx.x & 63;
   const int T = a.T;
   const bool live = lane < T;
   const uint64_t w = live ? observe(&a.node_out[(int64_t)b * T + lane]) : pack_node(-1, -1);
   const int next_l = (int)(uint32_t)w, bonus_l = (int)(uint32_t)(w >> 32);
-  if (__any(next_l == -2)) return;       // invalid tree, already reported
+  if (__any(next_l == -2)) {             // invalid tree, already reported
+    if (s_k && lane == 0) *s_k = -1;
+    return;
+  }
   int node = 0, k = 0;
   int my_path = lane == 0 ? 0 : -1;      // lane m holds path[m]
   int my_out = -1;                       // lane m holds out_tokens[m]
@@ -261,6 +283,93 @@ __device__ void finish_sequence(const Args &a, int b, int tok) {
     a.out_tokens[(int64_t)b * T + lane] = my_out;
   }
   if (lane == 0) a.accept_len[b] = k;
+  if (s_path) {
+    if (live) s_path[lane] = my_path;
+    if (lane == 0) *s_k = k;
+  }
+}
+
+// Row index (within layer 0) of logical slot `slot` of sequence b, KV head g; a paged
+// cache's block ids come from s_blk, which holds those of blocks blk0, blk0 + 1, ...
+__device__ inline int64_t slot_row(const CompactSeq &c, const int *s_blk, int blk0, int b, int g,
+                                   int slot) {
+  if (!c.kv.paged) return (int64_t)(b * c.kv.hkv + g) * c.kv.cap + slot;
+  const int blk = s_blk[(slot >> c.kv.block_shift) - blk0];
+  return (((int64_t)blk * c.kv.hkv + g) << c.kv.block_shift) | (slot & ((1 << c.kv.block_shift) - 1));
+}
+
+// Accepted-path KV compaction of sequence b ([TR] sec. 2: keep the accepted branch's KV)
+// by the whole workgroup, as ev_kv_compact does it: slot L + path[m] moves to slot L + m,
+// m = 1 .. k, in every layer, KV head, K and V.  The moves go in rounds of up to 4 x 256
+// 16-byte pieces, ordered by m; a round reads all its pieces into registers before it
+// writes any, since a destination L + m can be the source of an earlier move of the same
+// round (path[m'] = m, m' < m).  It is never the source of a later round: path[m'] >= m'
+// for every move, so later sources lie above every destination written before them.
+__device__ void compact_sequence(const CompactSeq &c, int b, int T, int L, int k,
+                                 const int *s_path, int *s_blk, int32_t *dev_status) {
+  if (k < 0) return;                     // invalid tree, already reported
+  const int tid = threadIdx.x;
+  bool bad = L < 0 || !c.kv.fits(L + T);
+  // a paged cache: the block ids of the tree's slots, checked and kept in LDS (every
+  // source and destination slot lies in [L, L + T))
+  const int blk0 = c.kv.paged && L >= 0 ? L >> c.kv.block_shift : 0;
+  if (!bad && c.kv.paged) {
+    const int X = blk0 + tid;
+    int bad_blk = 0;
+    if (X <= (L + T - 1) >> c.kv.block_shift) {
+      const int blk = c.kv.table[(int64_t)b * c.kv.max_blocks + X];
+      bad_blk = blk < 0 || blk >= c.kv.n_blocks;
+      s_blk[tid] = blk;
+    }
+    bad = __syncthreads_or(bad_blk);
+  }
+  if (bad) {
+    if (tid == 0) report(dev_status, EV_DERR_BOUNDS);
+    return;
+  }
+  if (tid == 0) c.new_len[b] = L + k + 1;
+  const int cpr = c.row_bytes / 16;      // 16-byte pieces per row: 2 .. 32
+  const int cshift = __ffs(cpr) - 1;
+  const int hk2 = c.kv.hkv * 2;
+  const int per_move = c.n_layers * hk2;
+  const int n_pieces = k * per_move * cpr;
+  constexpr int R = 4;
+  for (int base = 0; base < n_pieces; base += R * 256) {
+    u32x4 val[R];
+    float sc[R];
+    int64_t dst[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int idx = base + tid + 256 * i;
+      dst[i] = -1;
+      if (idx < n_pieces) {
+        const int row = idx >> cshift, ch = idx & (cpr - 1);
+        const int m = 1 + row / per_move, r2 = row % per_move;
+        const int l = r2 / hk2, g = (r2 % hk2) >> 1, which = r2 & 1;
+        const int64_t lrow = (int64_t)l * c.layer_rows;
+        const int64_t src = lrow + slot_row(c, s_blk, blk0, b, g, L + s_path[m]);
+        const int64_t dr = lrow + slot_row(c, s_blk, blk0, b, g, L + m);
+        const char *basep = which ? c.v : c.k;
+        val[i] = *(const u32x4 *)(basep + src * c.row_bytes + ch * 16);
+        const float *scales = which ? c.v_scale : c.k_scale;
+        sc[i] = scales && ch == 0 ? scales[src] : 0.f;
+        dst[i] = dr * cpr + ch + ((int64_t)which << 60);   // destination piece, K or V
+      }
+    }
+    __syncthreads();                     // every piece of the round read
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (dst[i] < 0) continue;
+      const int which = (int)(dst[i] >> 60);
+      const int64_t piece = dst[i] & (((int64_t)1 << 60) - 1);
+      const int64_t dr = piece >> cshift;
+      const int ch = (int)(piece & (cpr - 1));
+      char *basep = which ? c.v : c.k;
+      *(u32x4 *)(basep + dr * c.row_bytes + ch * 16) = val[i];
+      float *scales = which ? c.v_scale : c.k_scale;
+      if (scales && ch == 0) scales[dr] = sc[i];
+    }
+  }
 }
 
 // Statistics of one 1024-logit chunk (already in registers), the same in every lane:
@@ -311,10 +420,14 @@ __device__ inline void publish_stat(const AcceptArgs &a, int64_t row, int chunk,
 // grid (chunk groups, rows); a workgroup's four wavefronts stream CPW chunks each, the
 // wavefronts of a workgroup interleaved chunk by chunk, with the next chunk's loads in
 // flight while the current one is reduced.
-template <bool REJ, int CPW, bool VEC>
+// COMPACT: the workgroup that walks a sequence then compacts its accepted path's KV.
+template <bool REJ, int CPW, bool VEC, bool COMPACT>
 __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ double tab[kExpTab];
   __shared__ int s_last;
+  __shared__ int s_path[COMPACT ? kMaxNodes : 1];
+  __shared__ int s_blk[COMPACT ? kMaxNodes + 1 : 1];
+  __shared__ int s_k;
   args_in_sgprs(a.n_chunks, a.T, a.V, a.logits, a.parent, a.tokens, a.uniforms, a.inv_tau,
                 a.stats, a.row_cnt);
   const int lane = threadIdx.x & 63;
@@ -380,8 +493,15 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   if (wave == 0) settle_node<REJ>(a, b, n, par, tok, ul, tab);
   if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
 
-  // ---- last row of this sequence: walk ----
-  if (wave == 0) finish_sequence(a, b, tok);
+  // ---- last row of this sequence: walk (and compaction) ----
+  if constexpr (COMPACT) {
+    const int L = scalar_load(a.cmp.prefix_len, b);
+    if (wave == 0) finish_sequence(a, b, tok, s_path, &s_k);
+    __syncthreads();
+    compact_sequence(a.cmp, b, a.T, L, s_k, s_path, s_blk, a.dev_status);
+  } else if (wave == 0) {
+    finish_sequence(a, b, tok);
+  }
 }
 
 static ev_status check_common(const float *logits, const int32_t *tokens, const int32_t *parent,
@@ -399,12 +519,14 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
                                const int32_t *parent, int32_t B, int32_t T, int32_t V,
                                double inv_tau, const double *uniforms, int32_t *accept_len,
                                int32_t *path, int32_t *out_tokens, void *ws,
-                               int32_t *dev_status, hipStream_t stream) {
+                               int32_t *dev_status, hipStream_t stream,
+                               const CompactSeq *cmp = nullptr) {
   const WsLayout w = ws_layout(B, T, V);
   char *base = (char *)ws;
   AcceptArgs a{logits, tokens, parent, B, T, V, n_chunks_of(V), inv_tau, uniforms,
                base + w.stats, (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
-               (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status};
+               (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status, {}};
+  if (cmp) a.cmp = *cmp;
   // Chunks per wavefront: as many as keep at least 1024 workgroups in the grid (four per
   // CU), so that the streams run with the next chunk's loads in flight behind the reduction
   // while every workgroup stays resident at once.
@@ -416,8 +538,13 @@ static ev_status launch_accept(bool rej, const float *logits, const int32_t *tok
   const bool vec = (V & 3) == 0;          // rows start 16-byte aligned
 #define EV_LAUNCH_ACCEPT(R, C)                                                                \
   do {                                                                                        \
-    if (vec) hipLaunchKernelGGL((accept_kernel<R, C, true>), grid, dim3(256), 0, stream, a);  \
-    else hipLaunchKernelGGL((accept_kernel<R, C, false>), grid, dim3(256), 0, stream, a);     \
+    if (cmp) {                                                                                \
+      if (vec) hipLaunchKernelGGL((accept_kernel<R, C, true, true>), grid, dim3(256), 0, stream, a); \
+      else hipLaunchKernelGGL((accept_kernel<R, C, false, true>), grid, dim3(256), 0, stream, a); \
+    } else {                                                                                  \
+      if (vec) hipLaunchKernelGGL((accept_kernel<R, C, true, false>), grid, dim3(256), 0, stream, a); \
+      else hipLaunchKernelGGL((accept_kernel<R, C, false, false>), grid, dim3(256), 0, stream, a); \
+    }                                                                                         \
   } while (0)
   if (rej) {
     if (cpw == 4) EV_LAUNCH_ACCEPT(true, 4);
@@ -866,6 +993,87 @@ EV_API ev_status ev_accept_rejection(const float *logits, const int32_t *tokens,
   if (!uniforms) return EV_ERR_NULL;
   return ev::launch_accept(true, logits, tokens, parent, B, T, V, 1.0 / (double)temperature,
                            uniforms, accept_len, path, out_tokens, ws, dev_status, stream);
+}
+
+namespace ev {
+
+// The walking workgroup compacts the cache itself when one accepted node's rows (every
+// layer, KV head, K and V) are at most this many 16-byte pieces, so that a typical path of
+// a few nodes fits one round of its 1024 pieces; larger moves go to the compaction
+// kernel's grid of workgroups (32 MHA heads of 256-byte rows, 1024 pieces a node, took the
+// fused Llama-2-7B-shaped step from 30.1 to 34.1 us).
+constexpr int kFusedCompactPieces = 256;
+
+// Acceptance followed by compaction of each accepted path: one launch when the cache has
+// few layers, else the acceptance launch and then ev_kv_compact.
+static ev_status accept_and_compact(bool rej, const float *logits, const int32_t *tokens,
+                                    const int32_t *parent, int32_t B, int32_t T, int32_t V,
+                                    double inv_tau, const double *uniforms, int32_t *accept_len,
+                                    int32_t *path, int32_t *out_tokens, const ev_kv_desc *kv,
+                                    const int32_t *prefix_len, int32_t *new_len, void *ws,
+                                    int32_t *dev_status, hipStream_t stream) {
+  KvAddr addr;
+  ev_status st = make_kv_addr(kv, &addr);
+  if (st != EV_OK) return st;
+  if ((int64_t)kv->n_layers * kv->n_kv_heads * 2 > 65535) return EV_ERR_SHAPE;
+  if (kv->n_layers > 1 && (kv->layer_stride <= 0 || kv->layer_stride % kv->head_dim))
+    return EV_ERR_SHAPE;
+  if (!prefix_len || !new_len) return EV_ERR_NULL;
+  const int row_bytes = kv->dtype == EV_F32 ? 4 * kv->head_dim
+                      : kv->dtype == EV_BF16 ? 2 * kv->head_dim : kv->head_dim / 2;
+  const int64_t pieces_per_move = (int64_t)kv->n_layers * kv->n_kv_heads * 2 * (row_bytes / 16);
+  if (pieces_per_move > kFusedCompactPieces) {
+    st = launch_accept(rej, logits, tokens, parent, B, T, V, inv_tau, uniforms, accept_len, path,
+                       out_tokens, ws, dev_status, stream);
+    if (st != EV_OK) return st;
+    return ev_kv_compact(kv, prefix_len, path, accept_len, B, T, new_len, dev_status, stream);
+  }
+  CompactSeq c{};
+  c.k = (char *)kv->k;
+  c.v = (char *)kv->v;
+  c.k_scale = kv->dtype == EV_INT4 ? const_cast<float *>(kv->k_scale) : nullptr;
+  c.v_scale = kv->dtype == EV_INT4 ? const_cast<float *>(kv->v_scale) : nullptr;
+  c.kv = addr;
+  c.row_bytes = row_bytes;
+  c.layer_rows = kv->n_layers > 1 ? kv->layer_stride / kv->head_dim : 0;
+  c.n_layers = kv->n_layers;
+  c.prefix_len = prefix_len;
+  c.new_len = new_len;
+  return launch_accept(rej, logits, tokens, parent, B, T, V, inv_tau, uniforms, accept_len, path,
+                       out_tokens, ws, dev_status, stream, &c);
+}
+
+}  // namespace ev
+
+EV_API ev_status ev_accept_greedy_compact(const float *logits, const int32_t *tokens,
+                                          const int32_t *parent, int32_t B, int32_t T, int32_t V,
+                                          int32_t *accept_len, int32_t *path, int32_t *out_tokens,
+                                          const ev_kv_desc *kv, const int32_t *prefix_len,
+                                          int32_t *new_len, void *ws, size_t ws_bytes,
+                                          int32_t *dev_status, hipStream_t stream) {
+  ev_status st = ev::check_common(logits, tokens, parent, B, T, V, accept_len, path, out_tokens,
+                                  ws, ws_bytes);
+  if (st != EV_OK || B == 0) return st;
+  return ev::accept_and_compact(false, logits, tokens, parent, B, T, V, 0.0, nullptr, accept_len,
+                                path, out_tokens, kv, prefix_len, new_len, ws, dev_status, stream);
+}
+
+EV_API ev_status ev_accept_rejection_compact(const float *logits, const int32_t *tokens,
+                                             const int32_t *parent, int32_t B, int32_t T,
+                                             int32_t V, float temperature,
+                                             const double *uniforms, int32_t *accept_len,
+                                             int32_t *path, int32_t *out_tokens,
+                                             const ev_kv_desc *kv, const int32_t *prefix_len,
+                                             int32_t *new_len, void *ws, size_t ws_bytes,
+                                             int32_t *dev_status, hipStream_t stream) {
+  if (!(temperature > 0.f) || !isfinite(temperature)) return EV_ERR_ARG;
+  ev_status st = ev::check_common(logits, tokens, parent, B, T, V, accept_len, path, out_tokens,
+                                  ws, ws_bytes);
+  if (st != EV_OK || B == 0) return st;
+  if (!uniforms) return EV_ERR_NULL;
+  return ev::accept_and_compact(true, logits, tokens, parent, B, T, V, 1.0 / (double)temperature,
+                                uniforms, accept_len, path, out_tokens, kv, prefix_len, new_len,
+                                ws, dev_status, stream);
 }
 
 EV_API size_t ev_accept_sampled_workspace(int32_t B, int32_t T, int32_t V) {
