@@ -44,6 +44,9 @@ CASES = [
     ("C3_V5000_odd", scaled(C3, V=5001, L=8)),
     ("C4_B4", scaled(C4, B=4, V=3000, L=8)),
     ("C5_B2", scaled(C5, B=2, V=2048, L=8)),
+    # 2048 rows of 3 chunks: the rounds after the first run over lists of undecided rows,
+    # one chunk group (here the whole row) per work item
+    ("C4_B32_V3000_list_rounds", scaled(C4, B=32, V=3000, L=8)),
 ]
 
 
@@ -58,7 +61,11 @@ def test_sampled_bit_exact(name, cfg):
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("cfg", [C3, scaled(C4, B=4), C4], ids=["C3_full", "C4_B4_fullV", "C4_full"])
+# C3: every round over all rows (one chunk per wavefront); C4 with 3 sequences (two chunks
+# per wavefront), 4 and 16 (four): later rounds over lists of the undecided rows, more
+# work items than workgroups at 16
+@pytest.mark.parametrize("cfg", [C3, scaled(C4, B=3), scaled(C4, B=4), C4],
+                         ids=["C3_full", "C4_B3_fullV", "C4_B4_fullV", "C4_full"])
 def test_sampled_full_vocabulary(cfg):
     inp = generate(cfg, with_kv=False)
     draft, tokens = sampled_drafts(inp, DRAFT_TAU)

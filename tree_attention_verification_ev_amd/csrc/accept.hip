@@ -27,6 +27,7 @@
 #include "rowstream.h"
 
 #include <limits.h>
+#include <algorithm>
 #include <type_traits>
 #include <math.h>
 
@@ -579,6 +580,15 @@ struct SampledRow {
   int32_t tried;                         // children tested so far
 };
 
+// A row still undecided after a round, with its state: the next round's work list.
+struct SampledEntry {
+  SampledRow st;
+  int64_t row;
+  int64_t pad;
+};
+static_assert(sizeof(SampledEntry) == 64, "one list entry per 64 bytes");
+constexpr int kMaxLaunches = kMaxNodes + 1;   // the statistics launch and up to T rounds
+
 struct SampledArgs {
   const float *logits;
   const float *draft;
@@ -598,10 +608,14 @@ struct SampledArgs {
   int32_t *path;
   int32_t *out_tokens;
   int32_t *dev_status;
+  SampledEntry *list[2];                 // rows still undecided after round r: list[r & 1]
+  int32_t *list_cnt;                     // [kMaxLaunches] their number, per round
+  int round;                             // 0: the statistics launch
+  int reset_lists;                       // the statistics launch clears the list counters
 };
 
 struct SampledWs {
-  size_t row_cnt, seq_cnt, pstat, qstat, wpart, state, node_out, total;
+  size_t row_cnt, seq_cnt, pstat, qstat, wpart, state, node_out, list_cnt, list, total;
 };
 
 inline SampledWs sampled_ws_layout(int B, int T, int V) {
@@ -614,7 +628,9 @@ inline SampledWs sampled_ws_layout(int B, int T, int V) {
   w.wpart = w.qstat + align_up(per_chunk * sizeof(RejStat), 256);
   w.state = w.wpart + align_up(per_chunk * sizeof(double), 256);
   w.node_out = w.state + align_up(rows * sizeof(SampledRow), 256);
-  w.total = w.node_out + align_up(rows * sizeof(uint64_t), 256);
+  w.list_cnt = w.node_out + align_up(rows * sizeof(uint64_t), 256);
+  w.list = w.list_cnt + align_up(kMaxLaunches * sizeof(int32_t), 256);
+  w.total = w.list + 2 * rows * sizeof(SampledEntry);
   return w;
 }
 
@@ -717,7 +733,9 @@ __device__ inline NodeView node_view(const SampledArgs &a, int64_t row, int b, i
 // Decision of node n (row `row`) once the residual at shift st.s is known through its
 // chunk masses: the next untested child is accepted or rejected, or, with no child left,
 // the bonus token is drawn.  One wavefront.  Returns whether the node is settled (its
-// node_out published); a rejection instead advances the row state.
+// node_out published); a rejection instead advances the row state, in state[] or (LIST)
+// in the entry that lists the row for the next round.
+template <bool LIST>
 __device__ bool sampled_decide(const SampledArgs &a, int64_t row, const SampledRow &st,
                                const NodeView &v, const double (&mass)[kChunkRegs],
                                const double *tab) {
@@ -737,7 +755,13 @@ __device__ bool sampled_decide(const SampledArgs &a, int64_t row, const SampledR
         nst.s = st.s + Z;
         nst.tried = st.tried + 1;
         nst.active = 1;
-        a.state[row] = nst;                // read by the next launch
+        if constexpr (!LIST) {
+          a.state[row] = nst;              // read by the next round
+        } else {                           // listed for the next round
+          const int i = __hip_atomic_fetch_add(&a.list_cnt[a.round], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          a.list[a.round & 1][i] = SampledEntry{nst, row, 0};
+        }
       }
       return false;
     }
@@ -746,9 +770,11 @@ __device__ bool sampled_decide(const SampledArgs &a, int64_t row, const SampledR
     bonus = sampled_draw(a, row, st, mass, v.u0 * Z, tab);
   }
   if (lane == 0) {
-    SampledRow nst = st;
-    nst.active = 0;
-    a.state[row] = nst;
+    if constexpr (!LIST) {
+      SampledRow nst = st;
+      nst.active = 0;
+      a.state[row] = nst;
+    }
     publish(&a.node_out[row], pack_node(next, bonus));
   }
   return true;
@@ -821,7 +847,11 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
       }
     }
   }
-  if (!last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last)) return;
+  const bool row_done = last_arrival(&a.row_cnt[counter_slot(row)], gridDim.x, &s_last);
+  // the rounds' list counters start at zero (no round runs before this launch ends)
+  if (a.reset_lists && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kMaxLaunches)
+    publish(&a.list_cnt[threadIdx.x], 0);
+  if (!row_done) return;
   if (wave == 0) {
     const bool live = lane < a.T;
     const int par = v.par, tok = v.tok;
@@ -859,7 +889,7 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
       exp_nonpos_n(xm, em, tab);
 #pragma unroll
       for (int r = 0; r < kChunkRegs; ++r) mass[r] = cp[r].S > 0.0 ? cp[r].S * em[r] * inv_sp : 0.0;
-      const bool done = sampled_decide(a, row, st, v, mass, tab);
+      const bool done = sampled_decide<false>(a, row, st, v, mass, tab);
       if (lane == 0) s_last = done ? 1 : 0;
     } else if (lane == 0) {
       a.state[row] = SampledRow{};       // inactive
@@ -874,9 +904,11 @@ __global__ __launch_bounds__(256) void sampled_stats_kernel(SampledArgs a) {
   if (wave == 0) finish_sequence(a, b, v.tok);
 }
 
-// One round: every row still being decided takes one pass over its target and draft
-// logits for the residual mass at its current shift; its last workgroup then decides.
-template <int CPW>
+// A round over every row (the first round, or every round when one chunk per wavefront
+// covers the rows): every row still being decided takes one pass over its target and
+// draft logits for the residual mass at its current shift; its last workgroup then
+// decides.  Rows settled earlier return at once.
+template <int CPW, bool LIST>
 __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
   __shared__ double tab[kExpTab];
   __shared__ int s_last;
@@ -917,7 +949,7 @@ __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
       const int c = lane + 64 * r;
       mass[r] = c < nc ? observe(&a.wpart[row * nc + c]) : 0.0;
     }
-    const bool done = sampled_decide(a, row, st, v, mass, tab);
+    const bool done = sampled_decide<LIST>(a, row, st, v, mass, tab);
     if (lane == 0) s_last = done ? 1 : 0;
   }
   __syncthreads();
@@ -925,6 +957,69 @@ __global__ __launch_bounds__(256) void sampled_round_kernel(SampledArgs a) {
   if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) return;
   if (wave == 0) finish_sequence(a, b, v.tok);
 }
+
+// Later rounds: work item (i, j) is chunk group j of the i-th row listed by the round
+// before (one chunk per wavefront), and a fixed grid strides over the items.  A round with
+// few rows spreads each of them over many workgroups, and an empty round costs one load.
+// The list's count and a workgroup's first entry are loaded together.
+__global__ __launch_bounds__(256) void sampled_list_round_kernel(SampledArgs a) {
+  __shared__ double tab[kExpTab];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const SampledEntry *list = a.list[(a.round - 1) & 1];
+  const int nc = a.n_chunks;
+  const int gpr = (nc + kChunksPerWG - 1) / kChunksPerWG;
+  const int64_t rows = (int64_t)a.B * a.T;
+  const int64_t i0 = min((int64_t)blockIdx.x / gpr, rows - 1);
+  SampledEntry e = list[i0];             // speculative: valid if i0 < the count
+  const int64_t n_items = (int64_t)observe(&a.list_cnt[a.round - 1]) * gpr;
+  if ((int64_t)blockIdx.x >= n_items) return;
+  fill_exp_table(tab);
+  const bool vec_ok = (a.V & 3) == 0;
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int64_t i = it / gpr;
+    if (i != i0) e = list[i];
+    const int c = (int)(it % gpr) * kChunksPerWG + wave;
+    const int64_t row = e.row;
+    const SampledRow st = e.st;
+    const int b = (int)(row / a.T), n = (int)(row % a.T);
+    NodeView v{};
+    if (wave == 0) v = node_view(a, row, b, n, st.tried);
+    __syncthreads();                     // the exp table; the previous item's LDS flag read
+    if (c < nc) {
+      const float *lp = a.logits + row * a.V;
+      const float *lq = a.draft + row * a.V;
+      const double inv_sp = 1.0 / st.Sp, inv_sq = 1.0 / st.Sq;
+      int idx_unused[16];
+      float vp[16], vq[16];
+      load_pair(lp, lq, a.V, c * kChunk, vec_ok, vp, vq, idx_unused);
+      double w = 0.0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w += residual_weight(vp[k], vq[k], a, st, inv_sp, inv_sq, tab);
+      w = wave_sum(w);
+      if (lane == 0) publish(&a.wpart[row * nc + c], w);
+    }
+    if (!last_arrival(&a.row_cnt[counter_slot(row)], gpr, &s_last)) continue;
+    if (wave == 0) {
+      double mass[kChunkRegs];
+#pragma unroll
+      for (int r = 0; r < kChunkRegs; ++r) {
+        const int cc = lane + 64 * r;
+        mass[r] = cc < nc ? observe(&a.wpart[row * nc + cc]) : 0.0;
+      }
+      const bool done = sampled_decide<true>(a, row, st, v, mass, tab);
+      if (lane == 0) s_last = done ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) continue;
+    if (!last_arrival(&a.seq_cnt[counter_slot(b)], a.T, &s_last)) continue;
+    if (wave == 0) finish_sequence(a, b, v.tok);
+  }
+}
+
+// Workgroups of a later round's launch (at most).
+constexpr int kRoundGrid = 1024;
 
 static ev_status launch_sampled(const float *logits, const float *draft, const int32_t *tokens,
                                 const int32_t *parent, int32_t B, int32_t T, int32_t V,
@@ -938,13 +1033,26 @@ static ev_status launch_sampled(const float *logits, const float *draft, const i
                 inv_tau_q, uniforms, (RejStat *)(base + w.pstat), (RejStat *)(base + w.qstat),
                 (double *)(base + w.wpart), (SampledRow *)(base + w.state),
                 (int32_t *)(base + w.row_cnt), (int32_t *)(base + w.seq_cnt),
-                (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status};
+                (uint64_t *)(base + w.node_out), accept_len, path, out_tokens, dev_status,
+                {(SampledEntry *)(base + w.list), (SampledEntry *)(base + w.list) + (int64_t)B * T},
+                (int32_t *)(base + w.list_cnt), 0, 0};
   const int64_t rows = (int64_t)B * T;
   int cpw = 4;
   while (cpw > 1 && rows * ((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw)) < 2048)
     cpw /= 2;
   dim3 grid((a.n_chunks + kChunksPerWG * cpw - 1) / (kChunksPerWG * cpw), (unsigned)rows);
-#define EV_LAUNCH_SAMPLED(K, C) hipLaunchKernelGGL((K<C>), grid, dim3(256), 0, stream, a)
+  // Rounds.  With one chunk per wavefront the grid over every row already spreads a few
+  // undecided rows as widely as a list would, so every round takes it.  With more, a
+  // wavefront would reduce its chunks one after another however few rows are left, so
+  // after the first round (where most rows are still undecided) the rounds run over a
+  // list of the undecided rows, one chunk per wavefront.
+  const bool lists = cpw > 1 && max_children > 1;
+  a.reset_lists = lists;
+#define EV_LAUNCH_SAMPLED(C)                                                                  \
+  do {                                                                                        \
+    if (lists) hipLaunchKernelGGL((sampled_round_kernel<C, true>), grid, dim3(256), 0, stream, a); \
+    else hipLaunchKernelGGL((sampled_round_kernel<C, false>), grid, dim3(256), 0, stream, a); \
+  } while (0)
 #define EV_LAUNCH_STATS(C)                                                                    \
   do {                                                                                        \
     if ((V & 3) == 0) hipLaunchKernelGGL((sampled_stats_kernel<C, true>), grid, dim3(256), 0, stream, a); \
@@ -954,10 +1062,15 @@ static ev_status launch_sampled(const float *logits, const float *draft, const i
   else if (cpw == 2) EV_LAUNCH_STATS(2);
   else EV_LAUNCH_STATS(1);
 #undef EV_LAUNCH_STATS
-  for (int r = 0; r < max_children; ++r) {
-    if (cpw == 4) EV_LAUNCH_SAMPLED(sampled_round_kernel, 4);
-    else if (cpw == 2) EV_LAUNCH_SAMPLED(sampled_round_kernel, 2);
-    else EV_LAUNCH_SAMPLED(sampled_round_kernel, 1);
+  const int64_t items = rows * ((a.n_chunks + kChunksPerWG - 1) / kChunksPerWG);
+  const dim3 lgrid((unsigned)std::min<int64_t>(items, kRoundGrid));
+  for (int r = 1; r <= max_children; ++r) {
+    a.round = r;
+    if (r > 1 && lists)
+      hipLaunchKernelGGL(sampled_list_round_kernel, lgrid, dim3(256), 0, stream, a);
+    else if (cpw == 4) EV_LAUNCH_SAMPLED(4);
+    else if (cpw == 2) EV_LAUNCH_SAMPLED(2);
+    else EV_LAUNCH_SAMPLED(1);
   }
 #undef EV_LAUNCH_SAMPLED
   return launch_status();
