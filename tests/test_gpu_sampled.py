@@ -154,3 +154,22 @@ def test_sampled_root_only_trees():
     assert (got[0] == 0).all()
     for a, b in zip(got, ref[:3]):
         assert np.array_equal(a, b)
+
+
+def test_sampled_list_rounds_reuse_workspace():
+    """Calls that share one workspace, each on other trees and logits, with rounds over
+    lists of undecided rows (2048 rows, four chunks per wavefront in the first round): the
+    lists' counters start from zero in every call (the statistics launch clears them) and
+    stale entries of an earlier call are never read."""
+    cfg = scaled(C4, B=32, V=3000, L=8)
+    ws = torch.zeros(ev.ev_accept_sampled_workspace(cfg.B, cfg.T, cfg.V), dtype=torch.uint8,
+                     device="cuda")
+    for seed in (11, 12, 13):
+        inp = generate(cfg, with_kv=False, seed=seed)
+        draft, tokens = sampled_drafts(inp, DRAFT_TAU)
+        got = run_sampled(inp, draft, tokens, ws=ws)
+        ref = oracle_sampled(inp, draft, tokens)
+        assert min(min(m) for m in ref[3]) > 1e-12
+        for a, b in zip(got, ref[:3]):
+            assert np.array_equal(a, b), seed
+        assert int(ws[:2 * 65536 * 4].count_nonzero()) == 0
