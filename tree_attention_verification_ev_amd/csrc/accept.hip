@@ -299,6 +299,21 @@ __device__ inline int64_t slot_row(const CompactSeq &c, const int *s_blk, int bl
   return (((int64_t)blk * c.kv.hkv + g) << c.kv.block_shift) | (slot & ((1 << c.kv.block_shift) - 1));
 }
 
+// Whether the slots of sequence b's tree, [L, L + T), fall outside the cache; for a paged
+// cache thread t also loads the id of the tree's t-th block into s_blk (every source and
+// destination slot of the compaction lies in that range).  Run by the wavefronts that do
+// not walk, while the walk runs.
+__device__ inline bool tree_slots_bad(const CompactSeq &c, int b, int T, int L, int t,
+                                      int *s_blk) {
+  if (L < 0 || !c.kv.fits(L + T)) return t == 0;
+  if (!c.kv.paged) return false;
+  const int blk0 = L >> c.kv.block_shift;
+  if (blk0 + t > (L + T - 1) >> c.kv.block_shift) return false;
+  const int blk = c.kv.table[(int64_t)b * c.kv.max_blocks + blk0 + t];
+  s_blk[t] = blk;
+  return blk < 0 || blk >= c.kv.n_blocks;
+}
+
 // Accepted-path KV compaction of sequence b ([TR] sec. 2: keep the accepted branch's KV)
 // by the whole workgroup, as ev_kv_compact does it: slot L + path[m] moves to slot L + m,
 // m = 1 .. k, in every layer, KV head, K and V.  The moves go in rounds of up to 4 x 256
@@ -306,24 +321,12 @@ __device__ inline int64_t slot_row(const CompactSeq &c, const int *s_blk, int bl
 // writes any, since a destination L + m can be the source of an earlier move of the same
 // round (path[m'] = m, m' < m).  It is never the source of a later round: path[m'] >= m'
 // for every move, so later sources lie above every destination written before them.
-__device__ void compact_sequence(const CompactSeq &c, int b, int T, int L, int k,
-                                 const int *s_path, int *s_blk, int32_t *dev_status) {
+// `bad`: the tree's slots [L, L + T) are not all in the cache (tree_slots_bad).
+__device__ void compact_sequence(const CompactSeq &c, int b, int T, int L, int k, bool bad,
+                                 const int *s_path, const int *s_blk, int32_t *dev_status) {
   if (k < 0) return;                     // invalid tree, already reported
   const int tid = threadIdx.x;
-  bool bad = L < 0 || !c.kv.fits(L + T);
-  // a paged cache: the block ids of the tree's slots, checked and kept in LDS (every
-  // source and destination slot lies in [L, L + T))
-  const int blk0 = c.kv.paged && L >= 0 ? L >> c.kv.block_shift : 0;
-  if (!bad && c.kv.paged) {
-    const int X = blk0 + tid;
-    int bad_blk = 0;
-    if (X <= (L + T - 1) >> c.kv.block_shift) {
-      const int blk = c.kv.table[(int64_t)b * c.kv.max_blocks + X];
-      bad_blk = blk < 0 || blk >= c.kv.n_blocks;
-      s_blk[tid] = blk;
-    }
-    bad = __syncthreads_or(bad_blk);
-  }
+  const int blk0 = c.kv.paged ? L >> c.kv.block_shift : 0;
   if (bad) {
     if (tid == 0) report(dev_status, EV_DERR_BOUNDS);
     return;
@@ -429,8 +432,10 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __shared__ int s_path[COMPACT ? kMaxNodes : 1];
   __shared__ int s_blk[COMPACT ? kMaxNodes + 1 : 1];
   __shared__ int s_k;
+  __shared__ int s_bad;
   args_in_sgprs(a.n_chunks, a.T, a.V, a.logits, a.parent, a.tokens, a.uniforms, a.inv_tau,
                 a.stats, a.row_cnt);
+  if (COMPACT && threadIdx.x == 0) s_bad = 0;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.y;
@@ -497,9 +502,13 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   // ---- last row of this sequence: walk (and compaction) ----
   if constexpr (COMPACT) {
     const int L = scalar_load(a.cmp.prefix_len, b);
-    if (wave == 0) finish_sequence(a, b, tok, s_path, &s_k);
+    if (wave == 0) {
+      finish_sequence(a, b, tok, s_path, &s_k);
+    } else if (tree_slots_bad(a.cmp, b, a.T, L, (int)threadIdx.x - 64, s_blk)) {
+      s_bad = 1;
+    }
     __syncthreads();
-    compact_sequence(a.cmp, b, a.T, L, s_k, s_path, s_blk, a.dev_status);
+    compact_sequence(a.cmp, b, a.T, L, s_k, s_bad != 0, s_path, s_blk, a.dev_status);
   } else if (wave == 0) {
     finish_sequence(a, b, tok);
   }
