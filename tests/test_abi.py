@@ -86,6 +86,13 @@ def test_workspace_queries(lib):
     assert lib.ev_accept_workspace(1, 64, 128256) == counters + stats + 64 * 8
     assert lib.ev_accept_workspace(1, 64, 128256) % 256 == 0
     assert lib.ev_accept_workspace(0, 64, 10) == 0
+    # sampled drafts: counters, (max, sum) of both rows and the residual mass per chunk,
+    # the row states (48 bytes), the node words, the per-round list counters (65, padded to
+    # 256 bytes) and two lists of undecided rows (64 bytes per row each)
+    rows, chunks = 64, 126
+    assert lib.ev_accept_sampled_workspace(1, 64, 128256) == (
+        counters + 2 * rows * chunks * 16 + rows * chunks * 8 + rows * 48 + rows * 8 + 512
+        + 2 * rows * 64)
 
 
 def test_host_errors_return_before_launch(lib):
